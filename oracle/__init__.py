@@ -1,0 +1,20 @@
+"""Float64 CPU oracle for the gated-delta-rule token mixer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library and imports nothing from it.
+
+Every function is the plain definition written out, token by token, in
+float64, following "On the Design of Qwen3.8-Next Architecture" as summarised
+on the slinene ai-papers-daily page (Module A, Gated DeltaNet: the four-line
+delta form of the recurrence and the output parameterisation) and on the
+paper.rainbus.top digest (method step (1)).
+"""
+
+from .gdn_ref import (  # noqa: F401
+    gated_delta_recurrence,
+    gated_delta_decode_step,
+    gated_rmsnorm,
+    rel_err,
+)
