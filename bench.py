@@ -1,0 +1,221 @@
+"""Throughput of the GDN token-mixer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the hot path over the long-prefill workload
+(B=1, H=32, T=32768, d_k=d_v=128, bf16 q/k/v, fp32 alpha/beta/state): the
+chunked prefill kernel (gdn_prefill_fwd) followed by the gated RMSNorm
+epilogue (gdn_gated_rmsnorm) on its output.  ``value`` is prefill tokens/s of
+the whole step.  The same run measures the decode step on the decode workload
+(256 sequences x 32 heads, d = 128, fp32 states, 1000 consecutive steps) as
+state GB/s, and times the float64 CPU oracle on a bounded sample of the
+prefill workload.  Rank 0 prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s at T=32K + decode state GB/s, as % of MI355X roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_bytes(B, T, H, dk, dv, in_bytes=2, with_final_state=True, with_initial_state=False):
+    """Algorithmic HBM bytes of one prefill call: q, k, v read once, alpha and
+    beta read once, y (fp32) written once, states read/written once."""
+    per_token_head = (2 * dk + dv) * in_bytes + 8 + 4 * dv
+    state = 4 * dk * dv * B * H
+    return B * T * H * per_token_head + state * (int(with_final_state) + int(with_initial_state))
+
+
+def prefill_flops(B, T, H, dk, dv, C=64):
+    """Dense MFMA tile work per token-head of the chunked form (a chunk of C
+    tokens: K K^T, Q K^T, the (C x C)(C x d_v) products T R and P E, and the
+    three state products K S, Q S and K^T E; the diagonal-block inverse is
+    left out)."""
+    return B * T * H * (2 * 2 * C * dk + 2 * 2 * C * dv + 3 * 2 * dk * dv)
+
+
+def norm_bytes(rows, dv, in_bytes=2):
+    return rows * dv * (4 + 2 * in_bytes)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is per "
+              "(sequence, head) and needs no collectives; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_rule_amd as gdn
+    from workloads import CONFIGS, config_prefill_inputs, decode_initial_state, decode_step_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gdn.load_library()
+
+    # ---------------- prefill + epilogue (the timed step) ----------------
+    c = CONFIGS[2]
+    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
+    log(f"generating prefill inputs B={B} T={T} H={H} d={dk}")
+    d = config_prefill_inputs(2)
+
+    def to_dev(x, bf16):
+        t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    q, k, v, z = (to_dev(d[n], True) for n in ("q", "k", "v", "z"))
+    alpha, beta = to_dev(d["alpha"], False), to_dev(d["beta"], False)
+    del d
+    y = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = []
+
+    def step(record):
+        if record:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+        gdn.gdn_prefill_fwd(q, k, v, alpha, beta, None, S, y, stream=stream)
+        if record:
+            e1.record(stream)
+        gdn.gdn_gated_rmsnorm(y, z, None, 1e-6, out, stream=stream)
+        if record:
+            e2.record(stream)
+            ev.append((e0, e1, e2))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    prefill_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    norm_ms = float(np.mean([b.elapsed_time(c_) for _, b, c_ in ev]))
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    pf_bytes = prefill_bytes(B, T, H, dk, dv)
+    pf_gbps = pf_bytes / (prefill_ms * 1e-3) / 1e9
+    pf_tflops = prefill_flops(B, T, H, dk, dv) / (prefill_ms * 1e-3) / 1e12
+    nb = norm_bytes(B * T * H, dv)
+    log(f"step {ms_step:.3f} ms; prefill kernel {prefill_ms:.3f} ms ({pf_gbps:.0f} GB/s); "
+        f"epilogue {norm_ms:.3f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN prefill, long sequence, + gated RMSNorm epilogue",
+                   "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": 64,
+                   "qkv_dtype": "bf16", "state_dtype": "fp32", "y_dtype": "fp32",
+                   "epilogue_out_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "prefill_kernel", "achieved": pf_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pf_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": pf_bytes,
+                     "avg_launch_ms": prefill_ms,
+                     "mfma_tflops": pf_tflops, "mfma_frac_of_bf16_peak": pf_tflops / BF16_MFMA_PEAK_TFLOPS},
+        "epilogue": {"kernel": "gated_rmsnorm_kernel", "avg_launch_ms": norm_ms,
+                     "achieved": nb / (norm_ms * 1e-3) / 1e9, "unit": "GB/s",
+                     "frac": nb / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+    }
+    del q, k, v, z, alpha, beta, y, out
+    torch.cuda.empty_cache()
+
+    # ---------------- decode: state GB/s over consecutive steps ----------------
+    if not args.no_decode:
+        c3 = CONFIGS[3]
+        N, H3, d3 = c3["N"], c3["H"], c3["dk"]
+        log(f"decode: N={N} H={H3} d={d3}, {args.decode_steps} steps")
+        state = to_dev(decode_initial_state(), False)
+        n_inputs = 8   # distinct seeded step inputs, cycled
+        steps_in = []
+        for s in range(n_inputs):
+            di = decode_step_inputs(s)
+            steps_in.append(tuple(to_dev(di[n], True) for n in ("q", "k", "v"))
+                            + (to_dev(di["alpha"], False), to_dev(di["beta"], False)))
+        yd = torch.empty((N, H3, d3), dtype=torch.float32, device=dev)
+        for s in range(5):
+            gdn.gdn_decode_step(*steps_in[s % n_inputs], state, yd, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.decode_steps):
+            gdn.gdn_decode_step(*steps_in[s % n_inputs], state, yd, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / args.decode_steps
+        state_bytes = 2 * N * H3 * d3 * d3 * 4
+        all_bytes = state_bytes + N * H3 * (3 * d3 * 2 + 8 + 4 * d3)
+        gbps = state_bytes / (step_ms * 1e-3) / 1e9
+        log(f"decode step {step_ms * 1e3:.1f} us, state {gbps:.0f} GB/s")
+        result["decode"] = {"workload": "decode, 256 sequences x 32 heads, d=128, fp32 state",
+                            "steps": args.decode_steps, "us_per_step": step_ms * 1e3,
+                            "state_GBps": gbps, "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
+                            "all_bytes_GBps": all_bytes / (step_ms * 1e-3) / 1e9,
+                            "tokens_per_s": N / (step_ms * 1e-3)}
+        del state, steps_in, yd
+        torch.cuda.empty_cache()
+
+    # ---------------- float64 CPU oracle on a bounded sample ----------------
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import gated_delta_recurrence
+        Ts = 1024
+        log(f"cpu oracle: B=1 H={H} T={Ts} (single thread)")
+        ds = config_prefill_inputs(2, T=Ts)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            gated_delta_recurrence(ds["q"], ds["k"], ds["v"], ds["alpha"], ds["beta"])
+            dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": Ts / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"float64 numpy oracle, first {Ts} tokens of the long-prefill "
+                                            f"workload shape (B=1, H={H}, d=128), {dt:.1f} s, "
+                                            f"{platform.processor() or platform.machine()}"}
+        log(f"cpu oracle {Ts / dt:.1f} tokens/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet token-mixer library.
+ *
+ * The operations are those of the Gated DeltaNet mixer in "On the Design of
+ * Qwen3.8-Next Architecture" (slinene ai-papers-daily page, Module A; the
+ * paper.rainbus.top digest, method step (1)).  Per (batch b, head h) the state
+ * S is a d_k x d_v matrix and, token by token,
+ *
+ *     S_dec = alpha_t S_{t-1}
+ *     e_t   = v_t - S_dec^T k_t
+ *     S_t   = S_dec + beta_t k_t e_t^T
+ *     y_t   = scale * S_t^T q_t
+ *
+ * and the output epilogue is  o = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w)
+ * (sigmoid output gate, zero-centred RMSNorm weight; slinene page, Module A).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers, contiguous, in the layouts given
+ *    below (row-major, last index fastest), 16-byte aligned.  The caller
+ *    allocates and frees all memory; the library never allocates, frees or
+ *    keeps pointers after a call returns, and holds no mutable global state,
+ *    so calls are reentrant and thread-safe.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t passed as void*, NULL =
+ *    the null stream); no call synchronises the stream.  Results are ready
+ *    once the stream has reached the call.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is launched and no output is touched.  A launch failure
+ *    reported by the runtime returns GDN_ERR_LAUNCH.  Faults inside a kernel
+ *    surface at the caller's next synchronisation, as for any HIP kernel.
+ *  - No C++ exception crosses this interface.
+ *  - Supported head sizes: d_k, d_v in {16, 32, 64, 128}.
+ *  - q and k are expected L2-normalised per token (the mixer normalises them
+ *    before the recurrence); alpha and beta are expected in [0, 1].  Neither
+ *    is checked or clamped.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    GDN_ERR_SHAPE = 2,       /* a size is negative / zero where it must not be */
+    GDN_ERR_DTYPE = 3,       /* unknown dtype code                             */
+    GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+    GDN_ERR_UNSUPPORTED = 5, /* head size outside {16, 32, 64, 128}, or a size
+                                whose element count overflows the indexing     */
+    GDN_ERR_LAUNCH = 6       /* the HIP runtime rejected the kernel launch     */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,             /* IEEE float32                                   */
+    GDN_BF16 = 1             /* bfloat16                                       */
+} gdn_dtype;
+
+/*
+ * Chunked prefill over T tokens (slinene page, Module A: the recurrence above,
+ * evaluated 64 tokens at a time in its chunkwise form).
+ *
+ *   q, k          [B, T, H, d_k]  qkv_dtype
+ *   v             [B, T, H, d_v]  qkv_dtype
+ *   alpha, beta   [B, T, H]       float32, decay and write strength per token
+ *   initial_state [B, H, d_k, d_v] float32, or NULL for a zero state
+ *   final_state   [B, H, d_k, d_v] float32 out, or NULL to skip; may be the
+ *                 same pointer as initial_state (updated in place)
+ *   y             [B, T, H, d_v]  float32 out (may be NULL only when T == 0)
+ *   scale         multiplies y (1.0: the pages apply no query scaling)
+ *
+ * With qkv_dtype == GDN_BF16 the dense chunk products run on fp16/bf16 MFMA
+ * with float32 accumulation and a float32 state; with GDN_F32 they run on
+ * float32 MFMA.  T may be any value >= 0 (T == 0 copies the initial state).
+ */
+gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           const float* initial_state, float* final_state, float* y,
+                           int B, int T, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, float scale, void* hip_stream);
+
+/*
+ * One decode step for N live sequences (slinene page, Module A, one step of the
+ * recurrence; the step is bound by moving the state, not by arithmetic, as
+ * the rainbus digest notes for decoding).
+ *
+ *   q, k          [N, H, d_k]  qkv_dtype
+ *   v             [N, H, d_v]  qkv_dtype
+ *   alpha, beta   [N, H]       float32
+ *   state         [N, H, d_k, d_v] float32, read and updated in place
+ *   y             [N, H, d_v]  float32 out
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           float* state, float* y,
+                           int N, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, float scale, void* hip_stream);
+
+/*
+ * Gated zero-centred RMSNorm epilogue (slinene page, Module A: sigmoid gate
+ * times RMSNorm of the mixer output, RMSNorm weight stored as an offset w
+ * from one), per row of d_v values:
+ *
+ *     out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w)
+ *
+ *   y       [rows, d_v]  float32 (e.g. the prefill output viewed as B*T*H rows)
+ *   z       [rows, d_v]  io_dtype
+ *   weight  [d_v]        float32 offsets w, or NULL for w = 0
+ *   out     [rows, d_v]  io_dtype
+ *   eps     > 0 recommended (1e-6); rows >= 0.
+ */
+gdn_status gdn_gated_rmsnorm(const float* y, const void* z, const float* weight,
+                             float eps, void* out, long rows, int d_v,
+                             gdn_dtype io_dtype, void* hip_stream);
+
+/* Static, never-NULL description of a status code. */
+const char* gdn_status_string(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,176 @@
+"""Python binding of libgdn, the gfx950 Gated DeltaNet token-mixer library.
+
+The functions below carry the names of the C entry points declared in
+include/gdn.h and only marshal arguments: they check dtypes, shapes and
+contiguity of torch tensors, allocate missing outputs with torch (device
+memory is PyTorch's job here), and pass raw device pointers plus the current
+HIP stream to the library.  Every step of the computation runs in the HIP
+kernels.  There is no fallback: if libgdn.so is missing, loading fails with an
+ImportError that says how to build it.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
+    "gdn_prefill_fwd", "gdn_decode_step", "gdn_gated_rmsnorm", "gdn_status_string",
+]
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgdn.so"
+_lib = None
+
+
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+class GdnError(RuntimeError):
+    """A non-zero gdn_status returned by the library."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_string(status)} (status {status})")
+
+
+def load_library():
+    """Load libgdn.so from this package directory (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m linear_attention_recurrence_rule_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, f, lg = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_long
+    lib.gdn_prefill_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i, i, i, i, i, i, f, vp]
+    lib.gdn_prefill_fwd.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, f, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [fp, vp, fp, f, vp, lg, i, i, vp]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status):
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _require_gpu(t, name):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, y=None,
+                    scale=1.0, return_final_state=True, stream=None):
+    """Chunked prefill.  q, k [B, T, H, d_k]; v [B, T, H, d_v] (bf16 or fp32, one
+    dtype); alpha, beta [B, T, H] fp32; initial_state [B, H, d_k, d_v] fp32 or
+    None.  Returns (y [B, T, H, d_v] fp32, final_state or None).  ``final_state``
+    may be ``initial_state`` for an in-place update."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _check(y, "y", (B, T, H, dv), torch.float32, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    st = lib.gdn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+                             _ptr(final_state), _ptr(y), B, T, H, dk, dv, _dtype_code(q), float(scale),
+                             _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_prefill_fwd")
+    return y, final_state
+
+
+def gdn_decode_step(q, k, v, alpha, beta, state, y=None, scale=1.0, stream=None):
+    """One decode step.  q, k [N, H, d_k]; v [N, H, d_v]; alpha, beta [N, H] fp32;
+    state [N, H, d_k, d_v] fp32, updated in place.  Returns y [N, H, d_v] fp32."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (N, H, dk), q.dtype, dev)
+    _check(v, "v", (N, H, dv), q.dtype, dev)
+    _check(alpha, "alpha", (N, H), torch.float32, dev)
+    _check(beta, "beta", (N, H), torch.float32, dev)
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _check(y, "y", (N, H, dv), torch.float32, dev)
+    st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
+                             N, H, dk, dv, _dtype_code(q), float(scale), _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_decode_step")
+    return y
+
+
+def gdn_gated_rmsnorm(y, z, weight=None, eps=1e-6, out=None, stream=None):
+    """sigmoid(z) * RMSNorm(y) * (1 + weight) over the last axis.  y fp32, z bf16
+    or fp32 of the same shape; weight [d_v] fp32 or None.  Returns out (z's dtype)."""
+    lib = load_library()
+    _require_gpu(y, "y")
+    dv = y.shape[-1]
+    dev = y.device
+    _check(y, "y", y.shape, torch.float32, dev)
+    _check(z, "z", y.shape, z.dtype, dev)
+    _check(weight, "weight", (dv,), torch.float32, dev)
+    if out is None:
+        out = torch.empty(y.shape, dtype=z.dtype, device=dev)
+    _check(out, "out", y.shape, z.dtype, dev)
+    rows = y.numel() // dv if dv else 0
+    st = lib.gdn_gated_rmsnorm(_ptr(y), _ptr(z), _ptr(weight), float(eps), _ptr(out), rows, dv,
+                               _dtype_code(z), _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_gated_rmsnorm")
+    return out

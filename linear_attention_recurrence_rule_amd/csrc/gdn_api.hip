@@ -1,0 +1,101 @@
+// C ABI of libgdn: argument validation and dispatch.  Every check runs on the
+// host before anything is launched; nothing here allocates, synchronises or
+// keeps state between calls.
+#include <stdint.h>
+
+#include <climits>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+bool head_size_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+
+// Element counts must stay well inside 64-bit indexing and the grid limit.
+bool fits(long long a, long long b, long long c, long long d) {
+    const long long lim = 1LL << 46;
+    long long n = a;
+    for (long long f : {b, c, d}) {
+        if (f != 0 && n > lim / f) return false;
+        n *= f;
+    }
+    return true;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, float* final_state, float* y,
+                           int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
+                           void* hip_stream) {
+    if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
+    if (B <= 0 || H <= 0 || T < 0) return GDN_ERR_SHAPE;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, 128) || static_cast<long long>(B) * H * (d_v / 16) > INT_MAX / 8)
+        return GDN_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !y)) return GDN_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(initial_state), static_cast<const void*>(final_state),
+                          static_cast<const void*>(y)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!final_state && T == 0) return GDN_OK;
+    gdn::PrefillArgs a{q, k, v, alpha, beta, initial_state, final_state, y,
+                       B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale,
+                       static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_prefill(a));
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, float* state, float* y, int N, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, float scale, void* hip_stream) {
+    if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
+    if (N < 0 || H <= 0) return GDN_ERR_SHAPE;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!fits(N, H, d_k, d_v) || static_cast<long long>(N) * H > INT_MAX) return GDN_ERR_UNSUPPORTED;
+    if (N == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !y) return GDN_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(state), static_cast<const void*>(y)})
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::DecodeArgs a{q, k, v, alpha, beta, state, y, N, H, d_k, d_v, qkv_dtype == GDN_BF16, scale,
+                      static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_decode(a));
+}
+
+gdn_status gdn_gated_rmsnorm(const float* y, const void* z, const float* weight, float eps, void* out,
+                             long rows, int d_v, gdn_dtype io_dtype, void* hip_stream) {
+    if (!dtype_ok(io_dtype)) return GDN_ERR_DTYPE;
+    if (rows < 0) return GDN_ERR_SHAPE;
+    if (!head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!fits(rows, d_v, 1, 1) || rows / (256 / (d_v / 4)) >= INT_MAX) return GDN_ERR_UNSUPPORTED;
+    if (rows == 0) return GDN_OK;
+    if (!y || !z || !out) return GDN_ERR_NULL;
+    for (const void* p : {static_cast<const void*>(y), z, static_cast<const void*>(weight),
+                          static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::NormArgs a{y, z, weight, eps, out, rows, d_v, io_dtype == GDN_BF16,
+                    static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_gated_rmsnorm(a));
+}
+
+const char* gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid size argument";
+        case GDN_ERR_DTYPE: return "unknown dtype code";
+        case GDN_ERR_ALIGN: return "pointer is not 16-byte aligned";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head size or problem size";
+        case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/gdn.h declares, and rejects bad arguments with the documented status
+codes before anything is launched (every call below fails validation, so no
+HIP call is made)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_recurrence_rule_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH = range(7)
+FAKE = 0x10000          # an aligned, never-dereferenced address
+MISALIGNED = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|const char\*)\s+(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["gdn_decode_step", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
+                                    "gdn_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    for name in declared_functions():
+        assert name in exported
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    assert gdn.gdn_status_string(OK) == "ok"
+    for s in range(1, 7):
+        assert gdn.gdn_status_string(s) and gdn.gdn_status_string(s) != "unknown status"
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def _prefill(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y=FAKE,
+             B=1, T=8, H=2, dk=64, dv=64, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_prefill_fwd(q, k, v, a, b, s0, sT, y, B, T, H, dk, dv, dtype, 1.0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), ERR_DTYPE),
+    (dict(dtype=-1), ERR_DTYPE),
+    (dict(B=0), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(T=-1), ERR_SHAPE),
+    (dict(dk=48), ERR_UNSUPPORTED),
+    (dict(dv=256), ERR_UNSUPPORTED),
+    (dict(dk=8), ERR_UNSUPPORTED),
+    (dict(B=1 << 20, T=1 << 20, H=1 << 10), ERR_UNSUPPORTED),
+    (dict(q=None), ERR_NULL),
+    (dict(y=None), ERR_NULL),
+    (dict(a=None), ERR_NULL),
+    (dict(v=MISALIGNED), ERR_ALIGN),
+    (dict(s0=MISALIGNED), ERR_ALIGN),
+    (dict(sT=MISALIGNED), ERR_ALIGN),
+])
+def test_prefill_rejects(kwargs, status):
+    assert _prefill(**kwargs) == status
+
+
+def test_prefill_empty_without_state_is_a_no_op():
+    assert _prefill(q=None, k=None, v=None, a=None, b=None, y=None, sT=None, T=0) == OK
+
+
+def _decode(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, y=FAKE, N=4, H=2, dk=128, dv=128, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_decode_step(q, k, v, a, b, s, y, N, H, dk, dv, dtype, 1.0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=5), ERR_DTYPE),
+    (dict(N=-1), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(dk=100), ERR_UNSUPPORTED),
+    (dict(s=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(y=MISALIGNED), ERR_ALIGN),
+    (dict(s=MISALIGNED), ERR_ALIGN),
+])
+def test_decode_rejects(kwargs, status):
+    assert _decode(**kwargs) == status
+
+
+def test_decode_zero_sequences_is_a_no_op():
+    assert _decode(q=None, s=None, N=0) == OK
+
+
+def _norm(y=FAKE, z=FAKE, w=None, out=FAKE, rows=16, dv=128, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_gated_rmsnorm(y, z, w, ctypes.c_float(1e-6), out, rows, dv, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(rows=-2), ERR_SHAPE),
+    (dict(dv=96), ERR_UNSUPPORTED),
+    (dict(z=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(w=MISALIGNED), ERR_ALIGN),
+    (dict(y=MISALIGNED), ERR_ALIGN),
+])
+def test_norm_rejects(kwargs, status):
+    assert _norm(**kwargs) == status
+
+
+def test_norm_zero_rows_is_a_no_op():
+    assert _norm(y=None, z=None, out=None, rows=0) == OK
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 16)
+    a = torch.zeros(1, 4, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_prefill_fwd(q, q, q, a, a)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_decode_step(q[0], q[0], q[0], a[0], a[0], torch.zeros(4, 2, 16, 16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_gated_rmsnorm(q, q)

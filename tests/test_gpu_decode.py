@@ -1,0 +1,63 @@
+"""gdn_decode_step on the GPU against the float64 oracle's decode step."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gated_delta_decode_step, gated_delta_recurrence
+from tests.gpu_util import TOL, check, dev, host, say
+from workloads import decode_initial_state, decode_step_inputs, prefill_inputs
+import linear_attention_recurrence_rule_amd as gdn
+
+pytestmark = pytest.mark.gpu
+
+# The step is float32 arithmetic on exact inputs (bf16 values are exact in
+# float32): a d_k-term dot product per output, so errors stay near 1e-6; the
+# bound used is the float32 one for both input dtypes.
+DEC_TOL = 1e-4
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps_small(dk, dv, dtype):
+    say(f"decode small dk={dk} dv={dv} {dtype}")
+    N, H, steps = 3, 5, 4
+    rng = np.random.default_rng(dk * 1000 + dv)
+    S = (0.3 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    state = dev(S)
+    for step in range(steps):
+        d = prefill_inputs(N, 1, H, dk, dv, dtype, -1.0, 0.5, seed=7 + step)
+        q, k, v = (d[x][:, 0] for x in ("q", "k", "v"))
+        a, b = d["alpha"][:, 0], d["beta"][:, 0]
+        y = gdn.gdn_decode_step(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(a), dev(b), state,
+                                scale=0.75)
+        y_ref, S = gated_delta_decode_step(q, k, v, a, b, S, scale=0.75)
+        check(f"step {step} y", host(y), y_ref, DEC_TOL)
+        check(f"step {step} state", host(state), S, DEC_TOL)
+
+
+def test_decode_equals_recurrence_over_steps():
+    """T decode steps from S0 give the oracle's T-token recurrence."""
+    say("decode vs recurrence")
+    d = prefill_inputs(2, 12, 3, 64, 64, "bf16", -1.0, 0.5, seed=3, state_std=0.1)
+    y_ref, S_ref = gated_delta_recurrence(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"])
+    state = dev(d["initial_state"])
+    for t in range(12):
+        y = gdn.gdn_decode_step(*(dev(d[x][:, t], "bf16") for x in ("q", "k", "v")),
+                                dev(d["alpha"][:, t]), dev(d["beta"][:, t]), state)
+        check(f"t={t} y", host(y), y_ref[:, t], DEC_TOL)
+    check("final state", host(state), S_ref, DEC_TOL)
+
+
+def test_decode_config3_full_shape():
+    """256 sequences x 32 heads, d = 128, bf16: every state for 4 steps."""
+    say("decode config 3 full shape")
+    S = decode_initial_state()
+    state = dev(S)
+    for step in range(4):
+        d = decode_step_inputs(step)
+        y = gdn.gdn_decode_step(dev(d["q"], "bf16"), dev(d["k"], "bf16"), dev(d["v"], "bf16"),
+                                dev(d["alpha"]), dev(d["beta"]), state)
+        y_ref, S = gated_delta_decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S)
+        check(f"step {step} y", host(y), y_ref, DEC_TOL)
+        check(f"step {step} state", host(state), S, DEC_TOL)

@@ -21,7 +21,8 @@ values handed to the GPU (bf16 values are exactly representable in float32).
 
 Seeds: a sequence of at most SEGMENT tokens draws from
 numpy.random.default_rng(seed); longer ones draw segment s (SEGMENT tokens
-each) from default_rng([seed, s]).  Draw order inside a segment: q, k, v,
+each) from default_rng([seed, s]).  An optional prefill initial state draws
+from default_rng([seed, STATE_STREAM]).  Draw order inside a segment: q, k, v,
 beta-logit, alpha-logit, z.  Decode step j draws from default_rng([seed, j]);
 the decode initial state draws from default_rng(seed).
 """
@@ -29,6 +30,7 @@ the decode initial state draws from default_rng(seed).
 import numpy as np
 
 SEGMENT = 4096
+STATE_STREAM = 2**31 - 1     # second seed word of the initial-state stream
 
 CONFIGS = {
     0: dict(name="tiny_oracle_check", kind="prefill", B=1, H=1, T=64, dk=16, dv=16,
@@ -97,7 +99,7 @@ def prefill_inputs(B, T, H, dk, dv, dtype="bf16", A=-1.0, b=0.5, seed=0, with_z=
     ``t_begin`` (a multiple of SEGMENT) lets callers draw tokens
     [t_begin, t_begin + T) of a long sequence without drawing the rest.
     ``state_std`` > 0 adds an N(0, state_std^2) float32 initial state drawn
-    from default_rng([seed, -1]).
+    from default_rng([seed, STATE_STREAM]).
     """
     if T + t_begin <= SEGMENT and t_begin == 0:
         out = _draw_segment(np.random.default_rng(seed), B, T, H, dk, dv, A, b, dtype, with_z)
@@ -114,7 +116,7 @@ def prefill_inputs(B, T, H, dk, dv, dtype="bf16", A=-1.0, b=0.5, seed=0, with_z=
             t += n
         out = {key: np.concatenate([p[key] for p in parts], axis=1) for key in parts[0]}
     if state_std > 0:
-        rng = np.random.default_rng([seed, -1])
+        rng = np.random.default_rng([seed, STATE_STREAM])
         out["initial_state"] = (state_std * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
     return out
 
