@@ -50,7 +50,8 @@ typedef enum {
     GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
     GDN_ERR_UNSUPPORTED = 5, /* head size outside {16, 32, 64, 128}, or a size
                                 whose element count overflows the indexing     */
-    GDN_ERR_LAUNCH = 6       /* the HIP runtime rejected the kernel launch     */
+    GDN_ERR_LAUNCH = 6,      /* the HIP runtime rejected the kernel launch     */
+    GDN_ERR_WORKSPACE = 7    /* workspace NULL or smaller than required        */
 } gdn_status;
 
 typedef enum {
@@ -70,16 +71,29 @@ typedef enum {
  *                 same pointer as initial_state (updated in place)
  *   y             [B, T, H, d_v]  float32 out (may be NULL only when T == 0)
  *   scale         multiplies y (1.0: the pages apply no query scaling)
+ *   workspace     device scratch of at least gdn_prefill_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); owned by the caller, its
+ *                 contents are overwritten and are meaningless afterwards.  A
+ *                 workspace must not be shared by calls that can overlap.
  *
- * With qkv_dtype == GDN_BF16 the dense chunk products run on fp16/bf16 MFMA
- * with float32 accumulation and a float32 state; with GDN_F32 they run on
- * float32 MFMA.  T may be any value >= 0 (T == 0 copies the initial state).
+ * With qkv_dtype == GDN_BF16 the dense chunk products run on fp16 MFMA with
+ * float32 accumulation and a float32 state (bf16 inputs convert exactly to
+ * fp16 when |x| <= 65504); with GDN_F32 they run on float32 MFMA.  T may be
+ * any value >= 0 (T == 0 copies the initial state).  B * H must not exceed
+ * 65535.
  */
 gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta,
                            const float* initial_state, float* final_state, float* y,
                            int B, int T, int H, int d_k, int d_v,
-                           gdn_dtype qkv_dtype, float scale, void* hip_stream);
+                           gdn_dtype qkv_dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Workspace bytes gdn_prefill_fwd needs for these sizes (0 for GDN_F32 and
+ * for T == 0), or 0 with an invalid argument (the call reports the error).
+ */
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype);
 
 /*
  * One decode step for N live sequences (slinene page, Module A, one step of the

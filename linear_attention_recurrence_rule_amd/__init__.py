@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
-    "gdn_prefill_fwd", "gdn_decode_step", "gdn_gated_rmsnorm", "gdn_status_string",
+    "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
+    "gdn_status_string",
 ]
 
 GDN_F32 = 0
@@ -50,8 +51,11 @@ def load_library():
                           "`python -m linear_attention_recurrence_rule_amd.build`")
     lib = ctypes.CDLL(path)
     vp, fp, i, f, lg = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_long
-    lib.gdn_prefill_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i, i, i, i, i, i, f, vp]
+    sz = ctypes.c_size_t
+    lib.gdn_prefill_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.gdn_prefill_fwd.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, f, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [fp, vp, fp, f, vp, lg, i, i, vp]
@@ -101,12 +105,20 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def gdn_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype):
+    """Scratch bytes gdn_prefill_fwd needs (dtype: torch.bfloat16 or torch.float32)."""
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(load_library().gdn_prefill_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
 def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, y=None,
-                    scale=1.0, return_final_state=True, stream=None):
+                    scale=1.0, return_final_state=True, workspace=None, stream=None):
     """Chunked prefill.  q, k [B, T, H, d_k]; v [B, T, H, d_v] (bf16 or fp32, one
     dtype); alpha, beta [B, T, H] fp32; initial_state [B, H, d_k, d_v] fp32 or
     None.  Returns (y [B, T, H, d_v] fp32, final_state or None).  ``final_state``
-    may be ``initial_state`` for an in-place update."""
+    may be ``initial_state`` for an in-place update.  ``workspace`` is a uint8
+    device tensor of at least gdn_prefill_workspace_bytes(...) bytes; one is
+    allocated when it is None."""
     lib = load_library()
     _require_gpu(q, "q")
     B, T, H, dk = q.shape
@@ -124,9 +136,14 @@ def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, 
     if final_state is None and return_final_state:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    code = _dtype_code(q)
+    need = int(lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
-                             _ptr(final_state), _ptr(y), B, T, H, dk, dv, _dtype_code(q), float(scale),
-                             _stream(stream, dev))
+                             _ptr(final_state), _ptr(y), B, T, H, dk, dv, code, float(scale),
+                             _ptr(workspace), ws_bytes, _stream(stream, dev))
     if st:
         raise GdnError(st, "gdn_prefill_fwd")
     return y, final_state

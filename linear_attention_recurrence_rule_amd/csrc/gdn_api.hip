@@ -31,23 +31,43 @@ gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LA
 
 extern "C" {
 
-gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* initial_state, float* final_state, float* y,
-                           int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
-                           void* hip_stream) {
+namespace {
+
+gdn_status prefill_check(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
     if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
     if (B <= 0 || H <= 0 || T < 0) return GDN_ERR_SHAPE;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
-    if (!fits(B, T, H, 128) || static_cast<long long>(B) * H * (d_v / 16) > INT_MAX / 8)
-        return GDN_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, 128) || static_cast<long long>(B) * H > 65535) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+size_t workspace_needed(int B, int T, int H, gdn_dtype qkv_dtype) {
+    return (qkv_dtype == GDN_BF16 && T > 0) ? gdn::prefill_bf16_workspace_bytes(B, T, H) : 0;
+}
+
+}  // namespace
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
+    if (prefill_check(B, T, H, d_k, d_v, qkv_dtype) != GDN_OK) return 0;
+    return workspace_needed(B, T, H, qkv_dtype);
+}
+
+gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, float* final_state, float* y,
+                           int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = prefill_check(B, T, H, d_k, d_v, qkv_dtype);
+    if (st != GDN_OK) return st;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !y)) return GDN_ERR_NULL;
     for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
                           static_cast<const void*>(initial_state), static_cast<const void*>(final_state),
-                          static_cast<const void*>(y)})
+                          static_cast<const void*>(y), static_cast<const void*>(workspace)})
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = workspace_needed(B, T, H, qkv_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
     if (!final_state && T == 0) return GDN_OK;
     gdn::PrefillArgs a{q, k, v, alpha, beta, initial_state, final_state, y,
-                       B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale,
+                       B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale, workspace,
                        static_cast<hipStream_t>(hip_stream)};
     return from_hip(gdn::launch_prefill(a));
 }
@@ -94,6 +114,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERR_ALIGN: return "pointer is not 16-byte aligned";
         case GDN_ERR_UNSUPPORTED: return "unsupported head size or problem size";
         case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     }
     return "unknown status";
 }

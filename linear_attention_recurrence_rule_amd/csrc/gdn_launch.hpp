@@ -18,6 +18,7 @@ struct PrefillArgs {
     int B, T, H, dk, dv;
     bool bf16;
     float scale;
+    void* workspace;             // bf16 path: per-chunk T' blocks (prefill_bf16_workspace_bytes)
     hipStream_t stream;
 };
 
@@ -48,6 +49,8 @@ struct NormArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_prefill_bf16(const PrefillArgs& a);
+size_t prefill_bf16_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
 

@@ -454,12 +454,12 @@ static hipError_t launch_prefill_dk(const PrefillArgs& a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-    const bool bf = a.bf16;
+    if (a.bf16) return launch_prefill_bf16(a);
     switch (a.dk) {
-        case 16: return bf ? launch_prefill_dk<16, true>(a) : launch_prefill_dk<16, false>(a);
-        case 32: return bf ? launch_prefill_dk<32, true>(a) : launch_prefill_dk<32, false>(a);
-        case 64: return bf ? launch_prefill_dk<64, true>(a) : launch_prefill_dk<64, false>(a);
-        case 128: return bf ? launch_prefill_dk<128, true>(a) : launch_prefill_dk<128, false>(a);
+        case 16: return launch_prefill_dk<16, false>(a);
+        case 32: return launch_prefill_dk<32, false>(a);
+        case 64: return launch_prefill_dk<64, false>(a);
+        case 128: return launch_prefill_dk<128, false>(a);
         default: return hipErrorInvalidValue;
     }
 }

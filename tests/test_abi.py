@@ -15,19 +15,19 @@ import linear_attention_recurrence_rule_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(8)
 FAKE = 0x10000          # an aligned, never-dereferenced address
 MISALIGNED = 0x10004
 
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:gdn_status|const char\*)\s+(gdn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|const char\*|size_t)\s+(gdn_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gdn_decode_step", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
-                                    "gdn_status_string"]
+                                    "gdn_prefill_workspace_bytes", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,15 +42,15 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert gdn.gdn_status_string(OK) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert gdn.gdn_status_string(s) and gdn.gdn_status_string(s) != "unknown status"
     assert gdn.gdn_status_string(99) == "unknown status"
 
 
 def _prefill(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y=FAKE,
-             B=1, T=8, H=2, dk=64, dv=64, dtype=1):
+             B=1, T=8, H=2, dk=64, dv=64, dtype=1, ws=FAKE, ws_bytes=1 << 30):
     lib = gdn.load_library()
-    return lib.gdn_prefill_fwd(q, k, v, a, b, s0, sT, y, B, T, H, dk, dv, dtype, 1.0, None)
+    return lib.gdn_prefill_fwd(q, k, v, a, b, s0, sT, y, B, T, H, dk, dv, dtype, 1.0, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -69,13 +69,27 @@ def _prefill(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y=FAKE,
     (dict(v=MISALIGNED), ERR_ALIGN),
     (dict(s0=MISALIGNED), ERR_ALIGN),
     (dict(sT=MISALIGNED), ERR_ALIGN),
+    (dict(ws=MISALIGNED), ERR_ALIGN),
+    (dict(B=300, H=300), ERR_UNSUPPORTED),
+    (dict(ws=None), ERR_WORKSPACE),
+    (dict(ws_bytes=5119), ERR_WORKSPACE),
 ])
 def test_prefill_rejects(kwargs, status):
     assert _prefill(**kwargs) == status
 
 
+def test_workspace_bytes():
+    lib = gdn.load_library()
+    # bf16: one block set of 10 fp16 16x16 blocks per (sequence, head, 64-token chunk)
+    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 2 * 10 * 256 * 2
+    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 2 * 3 * 2 * 5120
+    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 0) == 0
+    assert lib.gdn_prefill_workspace_bytes(2, 0, 3, 128, 128, 1) == 0
+    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 48, 128, 1) == 0
+
+
 def test_prefill_empty_without_state_is_a_no_op():
-    assert _prefill(q=None, k=None, v=None, a=None, b=None, y=None, sT=None, T=0) == OK
+    assert _prefill(q=None, k=None, v=None, a=None, b=None, y=None, sT=None, T=0, ws=None) == OK
 
 
 def _decode(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, y=FAKE, N=4, H=2, dk=128, dv=128, dtype=1):
