@@ -19,12 +19,16 @@
 //               operand it produces (S, R, E) is fed to the next MFMA straight
 //               from the accumulator registers (split-K operand layout below),
 //               so the chain has no LDS round trip.
-//   waves 1, 2  output waves (token blocks {0,3} and {1,2}): Q S and P (built
-//               transposed so it too feeds the MFMA from registers), then, once
-//               the state wave has published E for the chunk, Y += P E -> y.
-//   waves 3..7  loader waves: chunk c+1's q, k, v (bf16 -> fp16), k^T, T' and
-//               the gates go to the other LDS buffer; one-word loads two to
-//               three chunks ahead pull the lines into L2 so that these loads hit.
+//   waves 1, 2  output waves (token blocks {0,3} and {1,2}): their q rows come
+//               straight from global memory into registers a chunk ahead; Q S
+//               and P (built transposed so it feeds the MFMA from registers),
+//               then, once the state wave has published E, Y += P E -> y.
+//   waves 3..7  loader waves (k and k^T on waves 3..6; v, T', alpha and the
+//               gates on wave 7): chunk c+1 goes to the other LDS buffer from
+//               registers loaded during the previous chunk.
+// Loads run one chunk ahead in two register sets; they are unconditional
+// (clamped addresses, out-of-range data zeroed afterwards) so that the
+// compiler's wait counts stay exact across the chunk loop.
 // Split-K operand layout: for a 16x16x32 MFMA, slot s of lane (m + 16 g) holds
 // K-index 16*(s/4) + 4 g + s%4 of its row/column.  Two 16x16 accumulator tiles
 // (lane (n + 16 g) holds rows 4 g .. 4 g + 3 of column n) stacked along K are
@@ -63,10 +67,24 @@ __device__ __forceinline__ half8 cat(half4 lo, half4 hi) {
 // halfs per row whose 16-byte chunks are XOR-swizzled by the row index.
 template <int LD>
 __device__ __forceinline__ int swz(int row, int col) {
-    constexpr int kChunks = LD / 8;
-    constexpr int kMask = (kChunks < 8 ? kChunks : 8) - 1;
-    const int ch = col >> 3;
-    return row * LD + (((ch ^ row) & kMask) | (ch & ~kMask)) * 8 + (col & 7);
+    constexpr int kMask = LD / 8 - 1;   // LD / 8 chunks per row, a power of two
+    return row * LD + (((col >> 3) ^ row) & kMask) * 8 + (col & 7);
+}
+
+// Token-major tiles (rows = d_k index or value column, C tokens per row) are
+// written one 2-byte element at a time by the loaders, 16 rows 8 apart per
+// instruction, and read as 8-byte runs of 4 tokens from 16 consecutive rows by
+// the MFMA operand loads.  XORing the 4-token unit index with
+// (row & 15) ^ ((row >> 3) & 15) puts both access patterns on distinct banks.
+__device__ __forceinline__ int swz_t(int row, int tok) {
+    const int h = (row & 15) ^ ((row >> 3) & 15);
+    return row * C + ((((tok >> 2) ^ h) & 15) << 2) + (tok & 3);
+}
+__device__ __forceinline__ half4 ld4_t(const _Float16* base, int row, int tok) {
+    return *reinterpret_cast<const half4*>(base + swz_t(row, tok));
+}
+__device__ __forceinline__ half8 ld_split_t(const _Float16* base, int row, int k0, int g) {
+    return cat(ld4_t(base, row, k0 + 4 * g), ld4_t(base, row, k0 + 16 + 4 * g));
 }
 template <int LD>
 __device__ __forceinline__ half4 ld4(const _Float16* base, int row, int col) {
@@ -253,20 +271,23 @@ template <int DK>
 struct MainCfg {
     static constexpr int SV = 16;                  // value columns per workgroup
     static constexpr int NT = 512;                 // 8 waves
-    static constexpr int W_STATE = 0, W_OUT0 = 1, W_LOAD0 = 3, NLW = 5;
-    static constexpr int LT = NLW * 64;            // loader threads
-    static constexpr int QC = DK / 8;              // 16-byte chunks per q/k row
-    static constexpr int N_V = 64 * (SV / 8);      // v items
-    static constexpr int N_T = NTB * TBLK / 8;     // T' items
-    static_assert(N_V <= LT && N_T <= LT, "one v item and one T' item per loader thread");
+    static constexpr int W_STATE = 0, W_OUT0 = 1;  // state wave, two output waves
+    static constexpr int W_QK0 = 3, NQKW = 4;      // k loader waves 3..6
+    static constexpr int W_MISC = 7;               // v, T', alpha and gates loader
+    static constexpr int LQK = NQKW * 64;          // k loader threads
+    static constexpr int QC = DK / 8;              // 16-byte pieces per q/k row
+    static constexpr int NQ = (64 * QC + LQK - 1) / LQK;   // k pieces per thread
+    static constexpr int NVI = 64 * (SV / 8) / 64;         // v pieces per misc lane
+    static constexpr int NTI = NTB * TBLK / 8 / 64;        // T' pieces per misc lane
+    static constexpr int NA = NQ > NVI + NTI ? NQ : NVI + NTI;
     static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1; // 32-wide K steps over d_k
     static constexpr int NST = DK / 16;            // 16-row state tiles
+    static_assert(NTB * TBLK / 8 == NTI * 64, "T' pieces fill the misc wave");
 };
 
 template <int DK>
 struct MainSmem {
     using Cfg = MainCfg<DK>;
-    _Float16 Q[2][C * DK];
     _Float16 K[2][C * DK];
     _Float16 KT[2][DK * C];
     _Float16 Tp[2][C * C];
@@ -276,83 +297,6 @@ struct MainSmem {
     float g[2][C], gam[2][C], dec[2][C];
     int flagE;
 };
-
-template <int DK>
-struct Prefetch {
-    static constexpr int NQ = (64 * MainCfg<DK>::QC + MainCfg<DK>::LT - 1) / MainCfg<DK>::LT;
-    uint4 q[NQ], k[NQ];
-    uint4 v, t;
-    float alpha;
-};
-
-// Loader items: q and k as (16-byte chunk cq, token t) with t = item % 64, so
-// the 64 lanes of a wave take 64 consecutive tokens of one chunk column (the
-// k^T scatter then spreads over the banks); v as (chunk cv, token); T' as 320
-// 16-byte pieces of its 10 lower blocks.
-template <int DK>
-__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, bool gate_wave, int lane,
-                                            const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                            const float* alpha, const _Float16* ws, long tok0, int T, int H,
-                                            int DV, int col0, int h, long wsbase) {
-    using Cfg = MainCfg<DK>;
-    const int t0 = chunk * C;
-    const long rowbase = (tok0 + t0) * H + h;
-#pragma unroll
-    for (int i = 0; i < Prefetch<DK>::NQ; ++i) {
-        const int idx = lt + i * Cfg::LT;
-        const int cq = idx / 64, t = idx % 64;
-        pf.q[i] = pf.k[i] = make_uint4(0, 0, 0, 0);
-        if (idx < 64 * Cfg::QC && t0 + t < T) {
-            const long off = (rowbase + static_cast<long>(t) * H) * DK + cq * 8;
-            pf.q[i] = *reinterpret_cast<const uint4*>(q + off);
-            pf.k[i] = *reinterpret_cast<const uint4*>(k + off);
-        }
-    }
-    pf.v = make_uint4(0, 0, 0, 0);
-    if (lt < Cfg::N_V) {
-        const int cv = lt / 64, t = lt % 64;
-        if (t0 + t < T)
-            pf.v = *reinterpret_cast<const uint4*>(v + (rowbase + static_cast<long>(t) * H) * DV + col0 + cv * 8);
-    }
-    pf.t = make_uint4(0, 0, 0, 0);
-    if (lt < Cfg::N_T)
-        pf.t = *reinterpret_cast<const uint4*>(ws + wsbase + static_cast<long>(chunk) * NTB * TBLK + lt * 8);
-    pf.alpha = 1.f;
-    if (gate_wave && t0 + lane < T) pf.alpha = alpha[rowbase + static_cast<long>(lane) * H];
-}
-
-// One 4-byte load per 128-byte line of a chunk's q rows, k rows, v slice rows
-// and T' blocks (about one or two per loader thread): brings them into L2
-// ahead of the real loads.  Returns the loaded words XORed together.
-template <int DK>
-__device__ __forceinline__ uint32_t loader_touch(int chunk, int lt, const uint16_t* q, const uint16_t* k,
-                                                 const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
-                                                 int DV, int col0, int h, long wsbase) {
-    using Cfg = MainCfg<DK>;
-    constexpr int LPR = DK * 2 >= 128 ? DK * 2 / 128 : 1;   // lines per q/k row
-    constexpr int NQK = 2 * 64 * LPR, NV = 64, NTL = NTB * TBLK * 2 / 128;
-    const int t0 = chunk * C;
-    uint32_t x = 0;
-#pragma unroll
-    for (int rep = 0; rep < (NQK + NV + NTL + Cfg::LT - 1) / Cfg::LT; ++rep) {
-        const int idx = lt + rep * Cfg::LT;
-        const uint32_t* p = nullptr;
-        if (idx < NQK) {
-            const int which = idx / (64 * LPR), rem = idx % (64 * LPR), t = rem / LPR, part = rem % LPR;
-            if (t0 + t < T)
-                p = reinterpret_cast<const uint32_t*>((which ? k : q) + ((tok0 + t0 + t) * H + h) * DK + part * 64);
-        } else if (idx < NQK + NV) {
-            const int t = idx - NQK;
-            if (t0 + t < T)
-                p = reinterpret_cast<const uint32_t*>(v + ((tok0 + t0 + t) * H + h) * static_cast<long>(DV) + col0);
-        } else if (idx < NQK + NV + NTL) {
-            p = reinterpret_cast<const uint32_t*>(ws + wsbase + static_cast<long>(chunk) * NTB * TBLK +
-                                                  (idx - NQK - NV) * 64);
-        }
-        if (p) x ^= *p;
-    }
-    return x;
-}
 
 __device__ __forceinline__ half8 bf16x8_to_h8(const uint4& r) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -366,46 +310,119 @@ __device__ __forceinline__ half8 bf16x8_to_h8(const uint4& r) {
 }
 
 template <int DK>
-__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int buf, int lt,
-                                             bool gate_wave, int lane) {
+struct Prefetch {
+    uint4 a[MainCfg<DK>::NA];
+    float alpha;
+    int chunk;
+};
+
+// Loader pieces are 16 bytes.  k waves: (token t, piece cq) with consecutive
+// pieces of one row on consecutive lanes, so a wave's load covers whole rows.
+// Misc wave: a[0 .. NVI) hold v (token, piece of the slice), a[NVI ..) hold
+// T' (10 lower blocks, in order).  Loads are unconditional: tokens past the
+// end read the last token's row (always in bounds) and are zeroed later by
+// loader_convert, so no load sits behind a branch.
+template <int DK>
+__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, bool misc, int lt, int lane,
+                                            const uint16_t* k, const uint16_t* v, const float* alpha,
+                                            const _Float16* ws, long tok0, int T, int H, int DV, int col0,
+                                            int h, long wsbase) {
     using Cfg = MainCfg<DK>;
+    const int t0 = chunk * C;
+    pf.chunk = chunk;
+    auto row = [&](int t) { return (tok0 + min(t0 + t, T - 1)) * H + h; };
+    if (!misc) {
 #pragma unroll
-    for (int i = 0; i < Prefetch<DK>::NQ; ++i) {
-        const int idx = lt + i * Cfg::LT;
-        if (idx < 64 * Cfg::QC) {
-            const int cq = idx / 64, t = idx % 64;
-            *reinterpret_cast<half8*>(&sm.Q[buf][swz<DK>(t, cq * 8)]) = bf16x8_to_h8(pf.q[i]);
-            const half8 kh = bf16x8_to_h8(pf.k[i]);
-            *reinterpret_cast<half8*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = kh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.KT[buf][swz<C>(cq * 8 + e, t)] = kh[e];
+        for (int i = 0; i < Cfg::NQ; ++i) {
+            const int idx = min(lt + i * Cfg::LQK, 64 * Cfg::QC - 1);
+            const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
+            pf.a[i] = *reinterpret_cast<const uint4*>(k + row(t) * DK + cq * 8);
         }
-    }
-    if (lt < Cfg::N_V) {
-        const int cv = lt / 64, t = lt % 64;
-        const half8 vh = bf16x8_to_h8(pf.v);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.VT[buf][swz<C>(cv * 8 + e, t)] = vh[e];
+        for (int i = 0; i < Cfg::NVI; ++i) {
+            const int idx = lane + i * 64;
+            const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
+            pf.a[i] = *reinterpret_cast<const uint4*>(v + row(t) * DV + col0 + cv * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::NTI; ++i)
+            pf.a[Cfg::NVI + i] = *reinterpret_cast<const uint4*>(ws + wsbase + static_cast<long>(chunk) * NTB * TBLK +
+                                                                 (lane + i * 64) * 8);
+        pf.alpha = alpha[row(lane)];
     }
-    if (lt < Cfg::N_T) {
-        const int blk = lt / 32, r = (lt % 32) / 2, hh = lt % 2;
+}
+
+// bf16 pieces (k, v) -> fp16 pieces in place, zero for tokens past the end;
+// alpha becomes 1 there.  T' pieces are fp16 already.
+template <int DK>
+__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf, bool misc, int lt, int lane, int T) {
+    using Cfg = MainCfg<DK>;
+    const int t0 = pf.chunk * C;
+    if (!misc) {
+#pragma unroll
+        for (int i = 0; i < Cfg::NQ; ++i) {
+            const int idx = lt + i * Cfg::LQK;
+            const bool ok = idx < 64 * Cfg::QC && t0 + idx / Cfg::QC < T;
+            const half8 hv = bf16x8_to_h8(ok ? pf.a[i] : make_uint4(0, 0, 0, 0));
+            pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::NVI; ++i) {
+            const bool ok = t0 + (lane + i * 64) / (Cfg::SV / 8) < T;
+            const half8 hv = bf16x8_to_h8(ok ? pf.a[i] : make_uint4(0, 0, 0, 0));
+            pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
+        }
+        if (t0 + lane >= T) pf.alpha = 1.f;
+    }
+}
+
+template <int DK>
+__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int buf, bool misc, int lt,
+                                             int lane) {
+    using Cfg = MainCfg<DK>;
+    if (!misc) {
+#pragma unroll
+        for (int i = 0; i < Cfg::NQ; ++i) {
+            const int idx = lt + i * Cfg::LQK;
+            if (idx < 64 * Cfg::QC) {
+                const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
+                const half8 kh = *reinterpret_cast<const half8*>(&pf.a[i]);
+                *reinterpret_cast<half8*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = kh;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.KT[buf][swz_t(cq * 8 + e, t)] = kh[e];
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::NVI; ++i) {
+        const int idx = lane + i * 64;
+        const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
+        const half8 vh = *reinterpret_cast<const half8*>(&pf.a[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.VT[buf][swz_t(cv * 8 + e, t)] = vh[e];
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::NTI; ++i) {
+        const int idx = lane + i * 64;
+        const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
         // lower block index -> (I, J): (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
         const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
         const int J = blk - I * (I + 1) / 2;
-        *reinterpret_cast<uint4*>(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)]) = pf.t;
+        *reinterpret_cast<uint4*>(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)]) = pf.a[Cfg::NVI + i];
     }
-    if (gate_wave) {
-        float lg = fmaxf(logf(pf.alpha), kLogDecayFloor);
+    float lg = fmaxf(logf(pf.alpha), kLogDecayFloor);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float t = __shfl_up(lg, off, 64);
-            if (lane >= off) lg += t;
-        }
-        const float glast = __shfl(lg, C - 1, 64);
-        sm.g[buf][lane] = lg;
-        sm.gam[buf][lane] = expf(lg);
-        sm.dec[buf][lane] = expf(glast - lg);
+    for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(lg, off, 64);
+        if (lane >= off) lg += t;
     }
+    const float glast = __shfl(lg, C - 1, 64);
+    sm.g[buf][lane] = lg;
+    sm.gam[buf][lane] = expf(lg);
+    sm.dec[buf][lane] = expf(glast - lg);
 }
 
 template <int DK>
@@ -423,140 +440,269 @@ __device__ __forceinline__ void state_refresh_operand(StateRegs<DK>& st) {
     }
 }
 
-// One chunk of the state chain (state wave).
+// One chunk of the state chain (state wave), software-pipelined by hand: each
+// group of MFMAs finds its operand fragments already in registers because
+// their LDS reads were issued one group earlier.  Scheduling barriers keep the
+// compiler from sinking the reads back next to their uses (it would otherwise
+// wait on every read).
 template <int DK>
 __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int chunk, int lane) {
     using Cfg = MainCfg<DK>;
+    constexpr int KS = Cfg::KSTEP;
+    constexpr int NST = Cfg::NST;
+    constexpr int NH = NST / 2 > 0 ? NST / 2 : 1;   // state tiles per half of the update
     const int buf = chunk & 1;
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
-    // K S
+    const _Float16* Tb = sm.Tp[buf];
+    const _Float16* KTb = sm.KT[buf];
+    auto kfrag = [&](int I, int kk) {
+        return DK >= 32 ? ld_split<DK>(Kb, I * 16 + lr, kk * 32, lq) : ld_split_lo<DK>(Kb, I * 16 + lr, 0, lq);
+    };
+    // K S, one 32-wide K step at a time, the next step's fragments in flight
+    half8 ka[2][NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) ka[0][I] = kfrag(I, 0);
+    half4 vv[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) vv[I] = ld4_t(sm.VT[buf], lr, I * 16 + 4 * lq);
     float4v ks[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-        ks[I] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int I = 0; I < NB; ++I) ks[I] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < Cfg::KSTEP; ++kk) {
-            const half8 a = DK >= 32 ? ld_split<DK>(Kb, I * 16 + lr, kk * 32, lq)
-                                     : ld_split_lo<DK>(Kb, I * 16 + lr, 0, lq);
-            ks[I] = mma(a, st.Sb[kk], ks[I]);
+    for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+#pragma unroll
+            for (int I = 0; I < NB; ++I) ka[(kk + 1) & 1][I] = kfrag(I, kk + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) ks[I] = mma(ka[kk & 1][I], st.Sb[kk], ks[I]);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // T' and the first half of k^T, read while K S finishes
+    half8 ta[NB][2];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+        ta[I][0] = ld_split<C>(Tb, I * 16 + lr, 0, lq);
+        ta[I][1] = I >= 2 ? ld_split<C>(Tb, I * 16 + lr, 32, lq) : half8{};
+    }
+    half8 kt0[NH][2];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        kt0[r][0] = ld_split_t(KTb, r * 16 + lr, 0, lq);
+        kt0[r][1] = ld_split_t(KTb, r * 16 + lr, 32, lq);
+    }
+    float4 gm[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4*>(&sm.gam[buf][I * 16 + 4 * lq]);
+    __builtin_amdgcn_sched_barrier(0);
     // R = V - gamma K S, as the split-K B operand of T' R
     half4 rh[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-        const int t = I * 16 + 4 * lq;
-        const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[buf][t]);
-        const half4 vv = ld4<C>(sm.VT[buf], lr, t);
-        rh[I] = to_h4(static_cast<float>(vv[0]) - gm.x * ks[I][0], static_cast<float>(vv[1]) - gm.y * ks[I][1],
-                      static_cast<float>(vv[2]) - gm.z * ks[I][2], static_cast<float>(vv[3]) - gm.w * ks[I][3]);
-    }
+    for (int I = 0; I < NB; ++I)
+        rh[I] = to_h4(static_cast<float>(vv[I][0]) - gm[I].x * ks[I][0], static_cast<float>(vv[I][1]) - gm[I].y * ks[I][1],
+                      static_cast<float>(vv[I][2]) - gm[I].z * ks[I][2], static_cast<float>(vv[I][3]) - gm[I].w * ks[I][3]);
     const half8 Rb0 = cat(rh[0], rh[1]), Rb1 = cat(rh[2], rh[3]);
     // E = T' R (T' is zero above the diagonal blocks)
     float4v e[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-        e[I] = mma(ld_split<C>(sm.Tp[buf], I * 16 + lr, 0, lq), Rb0, float4v{0.f, 0.f, 0.f, 0.f});
-        if (I >= 2) e[I] = mma(ld_split<C>(sm.Tp[buf], I * 16 + lr, 32, lq), Rb1, e[I]);
+        e[I] = mma(ta[I][0], Rb0, float4v{0.f, 0.f, 0.f, 0.f});
+        if (I >= 2) e[I] = mma(ta[I][1], Rb1, e[I]);
     }
-    // publish E for the output waves; D E as the B operand of K^T (D E)
+    __builtin_amdgcn_sched_barrier(0);
+    // second half of k^T and the decay-to-chunk-end factors, read while T' R runs
+    half8 kt1[NH][2];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        if (NH + r < NST) {
+            kt1[r][0] = ld_split_t(KTb, (NH + r) * 16 + lr, 0, lq);
+            kt1[r][1] = ld_split_t(KTb, (NH + r) * 16 + lr, 32, lq);
+        }
+    }
+    float4 dc[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4*>(&sm.dec[buf][I * 16 + 4 * lq]);
+    const float gl = sm.gam[buf][C - 1];
+    __builtin_amdgcn_sched_barrier(0);
+    // D E as the B operand of K^T (D E)
     half4 eh[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-        const int t = I * 16 + 4 * lq;
-        *reinterpret_cast<half4*>(&sm.ET[swz<C>(lr, t)]) = to_h4(e[I]);
-        const float4 dc = *reinterpret_cast<const float4*>(&sm.dec[buf][t]);
-        eh[I] = to_h4(dc.x * e[I][0], dc.y * e[I][1], dc.z * e[I][2], dc.w * e[I][3]);
-    }
-    __hip_atomic_store(&sm.flagE, chunk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int I = 0; I < NB; ++I)
+        eh[I] = to_h4(dc[I].x * e[I][0], dc[I].y * e[I][1], dc[I].z * e[I][2], dc[I].w * e[I][3]);
     const half8 Eb0 = cat(eh[0], eh[1]), Eb1 = cat(eh[2], eh[3]);
     // S = gamma_last S + K^T D E
-    const float gl = sm.gam[buf][C - 1];
+    float4v u[NST];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        u[r] = mma(kt0[r][0], Eb0, float4v{0.f, 0.f, 0.f, 0.f});
+        u[r] = mma(kt0[r][1], Eb1, u[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        if (NH + r < NST) {
+            u[NH + r] = mma(kt1[r][0], Eb0, float4v{0.f, 0.f, 0.f, 0.f});
+            u[NH + r] = mma(kt1[r][1], Eb1, u[NH + r]);
+        }
+    }
+    // publish E for the output waves while the update runs
+#pragma unroll
+    for (int I = 0; I < NB; ++I) *reinterpret_cast<half4*>(&sm.ET[swz<C>(lr, I * 16 + 4 * lq)]) = to_h4(e[I]);
+    __hip_atomic_store(&sm.flagE, chunk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     _Float16* STn = sm.ST[buf ^ 1];
 #pragma unroll
-    for (int r = 0; r < Cfg::NST; ++r) {
-        float4v u = mma(ld_split<C>(sm.KT[buf], r * 16 + lr, 0, lq), Eb0, float4v{0.f, 0.f, 0.f, 0.f});
-        u = mma(ld_split<C>(sm.KT[buf], r * 16 + lr, 32, lq), Eb1, u);
+    for (int r = 0; r < NST; ++r) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st.S[r][j] = gl * st.S[r][j] + u[j];
+        for (int j = 0; j < 4; ++j) st.S[r][j] = gl * st.S[r][j] + u[r][j];
         *reinterpret_cast<half4*>(&STn[swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
     }
     state_refresh_operand(st);
 }
 
-// One chunk of output (output wave `rp`: token blocks {0,3} or {1,2}).
+// q rows of the output wave's two token blocks, as the raw bf16 pieces of its
+// MFMA operands (lane (r + 16 g) holds q[row r][32 kk + 8 g .. + 8] per step kk).
 template <int DK>
-__device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int rp, int lane, float* y,
-                                             long tok0, int T, int H, int DV, int col0, int h, float scale,
-                                             int* spin_error) {
+struct QRegs {
+    uint4 raw[2][MainCfg<DK>::KSTEP];   // bf16 as loaded; fp16 after q_convert
+    int chunk;
+};
+
+template <int DK>
+__device__ __forceinline__ void load_q(QRegs<DK>& qr, const uint16_t* q, int chunk, int rp, int lane, long tok0,
+                                       int T, int H, int h) {
     using Cfg = MainCfg<DK>;
-    const int buf = chunk & 1;
     const int lr = lane & 15, lq = lane >> 4;
-    const _Float16* Qb = sm.Q[buf];
-    const _Float16* Kb = sm.K[buf];
-    const _Float16* STb = sm.ST[buf];
-    float4v yacc[2];
-    half8 Pa[2][2];
+    qr.chunk = chunk;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-        const int I = (ii == 0) ? rp : 3 - rp;
-        // gamma Q S
-        float4v qs = {0.f, 0.f, 0.f, 0.f};
+        const int t = min(chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr, T - 1);   // clamped; zeroed later
 #pragma unroll
         for (int kk = 0; kk < Cfg::KSTEP; ++kk) {
-            if constexpr (DK >= 32)
-                qs = mma(ld_split<DK>(Qb, I * 16 + lr, kk * 32, lq), ld_split<DK>(STb, lr, kk * 32, lq), qs);
-            else
-                qs = mma(ld_split_lo<DK>(Qb, I * 16 + lr, 0, lq), ld_split_lo<DK>(STb, lr, 0, lq), qs);
+            const int col = DK >= 32 ? kk * 32 + 8 * lq : 8 * (lq & 1);
+            qr.raw[ii][kk] = *reinterpret_cast<const uint4*>(q + ((tok0 + t) * H + h) * DK + col);
         }
-        const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[buf][I * 16 + 4 * lq]);
-        yacc[ii] = float4v{gm.x * qs[0], gm.y * qs[1], gm.z * qs[2], gm.w * qs[3]};
-        // P rows of block I, built transposed: lane holds row t, columns 4 lq .. 4 lq + 3 of block J
-        const int t = I * 16 + lr;
+    }
+}
+
+// bf16 -> fp16 in place; rows past the end (and, for d_k = 16, the unused
+// upper K slices) become zero.
+template <int DK>
+__device__ __forceinline__ void q_convert(QRegs<DK>& qr, int rp, int lane, int T) {
+    const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const bool ok = qr.chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr < T && (DK >= 32 || lq < 2);
+#pragma unroll
+        for (int kk = 0; kk < MainCfg<DK>::KSTEP; ++kk) {
+            const half8 hv = bf16x8_to_h8(ok ? qr.raw[ii][kk] : make_uint4(0, 0, 0, 0));
+            qr.raw[ii][kk] = *reinterpret_cast<const uint4*>(&hv);
+        }
+    }
+}
+
+// One chunk of output (output wave `rp`: token blocks {0,3} or {1,2}).  Its q
+// rows arrive in registers (loaded during the previous chunk).  Everything is
+// computed transposed (K_J Q_I^T for P, S^T Q^T, E^T P^T), so that each lane
+// holds one token row: P feeds the last MFMA straight from registers in the
+// split-K order, and y leaves as one 16-byte store per lane and block.
+template <int DK>
+__device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, const QRegs<DK>& qr, int chunk, int rp, int lane,
+                                             float* y, long tok0, int T, int H, int DV, int col0, int h,
+                                             float scale, int* spin_error) {
+    using Cfg = MainCfg<DK>;
+    constexpr int KS = Cfg::KSTEP;
+    const int buf = chunk & 1;
+    const int lr = lane & 15, lq = lane >> 4;
+    const _Float16* Kb = sm.K[buf];
+    const _Float16* STb = sm.ST[buf];
+    const int Irow[2] = {rp, 3 - rp};
+    const int Jmax = 3 - rp;   // highest k block either q block needs
+    // contiguous K-slices (lane (r + 16 g) holds K-index 8 g .. 8 g + 7 of step kk)
+    auto kfrag = [&](int J, int kk) {
+        return (DK >= 32 || lq < 2) ? ld8<DK>(Kb, J * 16 + lr, kk * 32 + 8 * lq) : half8{};
+    };
+    half8 sf[KS], kf[2][KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        sf[kk] = (DK >= 32 || lq < 2) ? ld8<DK>(STb, lr, kk * 32 + 8 * lq) : half8{};
+        kf[0][kk] = kfrag(0, kk);
+    }
+    const half8* qf0 = reinterpret_cast<const half8*>(qr.raw[0]);
+    const half8* qf1 = reinterpret_cast<const half8*>(qr.raw[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // (Q S)^T = S^T Q^T for both blocks: lane (t + 16 g) gets columns 4 g .. 4 g + 3 of row t
+    float4v qs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        qs[0] = mma(sf[kk], qf0[kk], qs[0]);
+        qs[1] = mma(sf[kk], qf1[kk], qs[1]);
+    }
+    // (Q K^T)^T tiles: k block J is read once, one block ahead of its MFMAs
+    float4v pacc[2][NB];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int J = 0; J < NB; ++J) pacc[ii][J] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+        if (J > Jmax) break;
+        if (J + 1 <= Jmax) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) kf[(J + 1) & 1][kk] = kfrag(J + 1, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            if (J <= Irow[0]) pacc[0][J] = mma(kf[J & 1][kk], qf0[kk], pacc[0][J]);
+            pacc[1][J] = mma(kf[J & 1][kk], qf1[kk], pacc[1][J]);   // Irow[1] = Jmax >= J
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // P = Gamma o (Q K^T), masked to i <= t; lane holds row t = 16 I + lr.  The
+    // exponentials are taken for every entry and the mask applied afterwards
+    // (a masked entry may overflow to inf; the select discards it).
+    float4 gi4[NB];
+#pragma unroll
+    for (int J = 0; J < NB; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.g[buf][J * 16 + 4 * lq]);
+    half8 Pb[2][2];
+    float gam_t[2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+        const int t = Irow[ii] * 16 + lr;
         const float gt = sm.g[buf][t];
+        gam_t[ii] = sm.gam[buf][t];
         half4 ph[NB];
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-            ph[J] = half4{};
-            if (J <= I) {
-                float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kq = 0; kq < Cfg::KSTEP; ++kq) {
-                    if constexpr (DK >= 32)
-                        acc = mma(ld8<DK>(Kb, J * 16 + lr, kq * 32 + 8 * lq), ld8<DK>(Qb, I * 16 + lr, kq * 32 + 8 * lq),
-                                  acc);
-                    else
-                        acc = mma(lq < 2 ? ld8<DK>(Kb, J * 16 + lr, 8 * lq) : half8{},
-                                  lq < 2 ? ld8<DK>(Qb, I * 16 + lr, 8 * lq) : half8{}, acc);
-                }
-                const int i0 = J * 16 + 4 * lq;
-                const float4 gi = *reinterpret_cast<const float4*>(&sm.g[buf][i0]);
-                ph[J] = to_h4(i0 + 0 <= t ? expf(gt - gi.x) * acc[0] : 0.f,
-                              i0 + 1 <= t ? expf(gt - gi.y) * acc[1] : 0.f,
-                              i0 + 2 <= t ? expf(gt - gi.z) * acc[2] : 0.f,
-                              i0 + 3 <= t ? expf(gt - gi.w) * acc[3] : 0.f);
-            }
+            const int i0 = J * 16 + 4 * lq;
+            const float p0 = __expf(gt - gi4[J].x) * pacc[ii][J][0];
+            const float p1 = __expf(gt - gi4[J].y) * pacc[ii][J][1];
+            const float p2 = __expf(gt - gi4[J].z) * pacc[ii][J][2];
+            const float p3 = __expf(gt - gi4[J].w) * pacc[ii][J][3];
+            ph[J] = to_h4(i0 + 0 <= t ? p0 : 0.f, i0 + 1 <= t ? p1 : 0.f, i0 + 2 <= t ? p2 : 0.f,
+                          i0 + 3 <= t ? p3 : 0.f);
         }
-        Pa[ii][0] = cat(ph[0], ph[1]);
-        Pa[ii][1] = cat(ph[2], ph[3]);
+        Pb[ii][0] = cat(ph[0], ph[1]);
+        Pb[ii][1] = cat(ph[2], ph[3]);
     }
     // wait until the state wave has published E for this chunk
     for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
         if (it > (1 << 22)) { *spin_error = 1; break; }
         __builtin_amdgcn_s_sleep(1);
     }
-    const half8 Eb0 = ld_split<C>(sm.ET, lr, 0, lq), Eb1 = ld_split<C>(sm.ET, lr, 32, lq);
+    // Y^T = E^T P^T + gamma (Q S)^T: lane (t + 16 g) holds row t, columns 4 g .. 4 g + 3
+    const half8 Ea0 = ld_split<C>(sm.ET, lr, 0, lq), Ea1 = ld_split<C>(sm.ET, lr, 32, lq);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-        const int I = (ii == 0) ? rp : 3 - rp;
-        float4v yv = mma(Pa[ii][0], Eb0, yacc[ii]);
-        if (I >= 2) yv = mma(Pa[ii][1], Eb1, yv);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = chunk * C + I * 16 + 4 * lq + j;
-            if (t < T) y[((tok0 + t) * H + h) * static_cast<long>(DV) + col0 + lr] = scale * yv[j];
-        }
+        const int I = Irow[ii];
+        float4v yv = {gam_t[ii] * qs[ii][0], gam_t[ii] * qs[ii][1], gam_t[ii] * qs[ii][2], gam_t[ii] * qs[ii][3]};
+        yv = mma(Ea0, Pb[ii][0], yv);
+        if (I >= 2) yv = mma(Ea1, Pb[ii][1], yv);
+        const int t = chunk * C + I * 16 + lr;
+        if (t < T)
+            *reinterpret_cast<float4*>(&y[((tok0 + t) * H + h) * static_cast<long>(DV) + col0 + 4 * lq]) =
+                make_float4(scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]);
     }
 }
 
@@ -584,9 +730,8 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
 
     const bool is_state = (w == Cfg::W_STATE);
     const bool is_out = (w >= Cfg::W_OUT0 && w < Cfg::W_OUT0 + 2);
-    const bool is_load = (w >= Cfg::W_LOAD0);
-    const int lt = (w - Cfg::W_LOAD0) * 64 + lane;
-    const bool gate_wave = (w == Cfg::W_LOAD0 + Cfg::NLW - 1);
+    const bool misc = (w == Cfg::W_MISC);
+    const int lt = (w - Cfg::W_QK0) * 64 + lane;
 
     // T' is zero above its diagonal blocks; those halves of both buffers are never written again
     for (int idx = tid; idx < 2 * C * C; idx += Cfg::NT) (&sm.Tp[0][0])[idx] = static_cast<_Float16>(0.f);
@@ -620,41 +765,51 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
         }
     } else if (is_out) {
         int spin_error = 0;
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            output_chunk<DK>(sm, c, w - Cfg::W_OUT0, lane, y, tok0, T, H, DV, col0, h, scale, &spin_error);
+        const int rp = w - Cfg::W_OUT0;
+        // q of chunk c+1 is loaded into one register set at the start of
+        // chunk c, while chunk c runs from the other (converted at its start)
+        QRegs<DK> qa, qb;
+        auto step = [&](int c, QRegs<DK>& cur, QRegs<DK>& nxt) {
+            load_q<DK>(nxt, q, min(c + 1, nchunks - 1), rp, lane, tok0, T, H, h);
+            q_convert<DK>(cur, rp, lane, T);
+            output_chunk<DK>(sm, cur, c, rp, lane, y, tok0, T, H, DV, col0, h, scale, &spin_error);
             __syncthreads();
+        };
+        if (nchunks > 0) load_q<DK>(qa, q, 0, rp, lane, tok0, T, H, h);
+        __syncthreads();
+        for (int c = 0; c < nchunks; c += 2) {
+            step(c, qa, qb);
+            if (c + 1 < nchunks) step(c + 1, qb, qa);
         }
     } else {
-        // loader: during chunk c, chunk c+1 is loaded (L2 hits) and stored to
-        // the other buffer; chunk c+3 is touched so that it is in L2 by then.
-        Prefetch<DK> pf;
-        uint32_t sink = 0;
-        auto ld = [&](int c) {
-            loader_load<DK>(pf, c, lt, gate_wave, lane, q, k, v, alpha, ws, tok0, T, H, DV, col0, h, wsbase);
+        // loader: during chunk c the loads of chunk c+2 are issued into one
+        // register set, then chunk c+1 (loaded during chunk c-1, in the other
+        // set) is converted and stored to the other LDS buffer.
+        Prefetch<DK> pa, pb;
+        auto ld = [&](Prefetch<DK>& pf, int c) {
+            loader_load<DK>(pf, min(c, nchunks - 1), misc, lt, lane, k, v, alpha, ws, tok0, T, H, DV, col0, h,
+                            wsbase);
         };
-        auto touch = [&](int c) {
-            return c < nchunks ? loader_touch<DK>(c, lt, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase) : 0u;
+        auto put = [&](Prefetch<DK>& pf, int c) {
+            loader_convert<DK>(pf, misc, lt, lane, T);
+            loader_store<DK>(pf, sm, c & 1, misc, lt, lane);
         };
-        uint32_t tA = touch(1), tB = touch(2);
         if (nchunks > 0) {
-            ld(0);
-            loader_store<DK>(pf, sm, 0, lt, gate_wave, lane);
+            ld(pa, 0);
+            put(pa, 0);
+            ld(pa, 1);
         }
         __syncthreads();
-        auto step = [&](int c, uint32_t& slot) {
-            if (c + 1 < nchunks) ld(c + 1);
-            sink ^= slot;             // touched two chunks ago: long since arrived
-            slot = touch(c + 3);
-            if (c + 1 < nchunks) loader_store<DK>(pf, sm, (c + 1) & 1, lt, gate_wave, lane);
-            __syncthreads();
-        };
         for (int c = 0; c < nchunks; c += 2) {
-            step(c, tA);
-            if (c + 1 < nchunks) step(c + 1, tB);
+            ld(pb, c + 2);
+            if (c + 1 < nchunks) put(pa, c + 1);
+            __syncthreads();
+            if (c + 1 < nchunks) {
+                ld(pa, c + 3);
+                if (c + 2 < nchunks) put(pb, c + 2);
+                __syncthreads();
+            }
         }
-        sink ^= tA ^ tB;
-        if (sink == 0x9e3779b9u && T < 0) y[0] = 0.f;   // keeps the touch loads; never true (T >= 0)
     }
 }
 
