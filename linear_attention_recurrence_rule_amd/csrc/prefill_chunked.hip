@@ -8,8 +8,8 @@
 //   E  = T' (V - diag(gamma) K S)          (rows: beta_t times token t's miss)
 //   Y  = diag(gamma) Q S + P E,            P = lower(Gamma o Q K^T)
 //   S' = gamma_last S + K^T diag(d) E
-// T' depends only on k, alpha and beta, so a chunk-parallel kernel
-// (prep_kernel) computes it once per (head, chunk) into a workspace; the
+// T' and the gates depend only on k, alpha and beta, so a chunk-parallel
+// kernel (prep_kernel) computes them once per (head, chunk) into a workspace; the
 // sequential kernel (main_kernel) then runs the chunks of one (head,
 // 16-column value slice) in order.
 //
@@ -23,8 +23,8 @@
 //               straight from global memory into registers a chunk ahead; Q S
 //               and P (built transposed so it feeds the MFMA from registers),
 //               then, once the state wave has published E, Y += P E -> y.
-//   waves 3..7  loader waves (k and k^T on waves 3..6; v, T', alpha and the
-//               gates on wave 7): chunk c+1 goes to the other LDS buffer from
+//   waves 3..7  loader waves (k and k^T on waves 3..6; v, T' and the gates
+//               on wave 7): chunk c+1 goes to the other LDS buffer from
 //               registers loaded during the previous chunk.
 // Loads run one chunk ahead in two register sets; they are unconditional
 // (clamped addresses, out-of-range data zeroed afterwards) so that the
@@ -46,6 +46,8 @@ constexpr int C = 64;                    // tokens per chunk
 constexpr int NB = C / 16;               // 16-token blocks per chunk
 constexpr int NTB = NB * (NB + 1) / 2;   // lower 16x16 blocks of a chunk matrix
 constexpr int TBLK = 256;                // halfs per 16x16 block
+constexpr int NGATE = 3 * C;             // per-chunk gate floats: g, gamma, d
+constexpr int WS_CHUNK = NTB * TBLK + 2 * NGATE;   // workspace halfs per (head, chunk)
 constexpr float kLogDecayFloor = -30.0f; // exp(-30) ~ 9e-14: alpha = 0 stays finite
 constexpr int kXcds = 8;
 
@@ -179,8 +181,9 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
     }
 }
 
-// Workspace layout: for each (b*H + h, chunk), the NTB lower 16x16 blocks of
-// T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each row-major fp16.
+// Workspace layout: for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
+// 16x16 blocks of T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each
+// row-major fp16, then the float32 gates g[C], gamma[C], d[C].
 template <int DK>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
@@ -226,6 +229,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
         }
         sm.g[l] = lg;
         sm.beta[l] = be;
+        // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
+        const float glast = __shfl(lg, C - 1, 64);
+        float* gate = reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
+        gate[l] = lg;
+        gate[C + l] = expf(lg);
+        gate[2 * C + l] = expf(glast - lg);
     }
     __syncthreads();
 
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     build_T<Cfg>(sm, w, l);
 
     // T' = T diag(beta), lower blocks, 8 halfs per item
-    _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * NTB * TBLK;
+    _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK;
     for (int idx = tid; idx < NTB * TBLK / 8; idx += 256) {
         const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
         int u = blk, I = 0;
@@ -273,16 +282,19 @@ struct MainCfg {
     static constexpr int NT = 512;                 // 8 waves
     static constexpr int W_STATE = 0, W_OUT0 = 1;  // state wave, two output waves
     static constexpr int W_QK0 = 3, NQKW = 4;      // k loader waves 3..6
-    static constexpr int W_MISC = 7;               // v, T', alpha and gates loader
+    static constexpr int W_MISC = 7;               // v, T' and gates loader
     static constexpr int LQK = NQKW * 64;          // k loader threads
     static constexpr int QC = DK / 8;              // 16-byte pieces per q/k row
     static constexpr int NQ = (64 * QC + LQK - 1) / LQK;   // k pieces per thread
     static constexpr int NVI = 64 * (SV / 8) / 64;         // v pieces per misc lane
     static constexpr int NTI = NTB * TBLK / 8 / 64;        // T' pieces per misc lane
-    static constexpr int NA = NQ > NVI + NTI ? NQ : NVI + NTI;
+    static constexpr int NGI = (NGATE / 4 + 63) / 64;      // gate pieces per misc lane
+    static constexpr int NMI = NVI + NTI + NGI;            // misc pieces per lane
+    static constexpr int NA = NQ > NMI ? NQ : NMI;
     static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1; // 32-wide K steps over d_k
     static constexpr int NST = DK / 16;            // 16-row state tiles
     static_assert(NTB * TBLK / 8 == NTI * 64, "T' pieces fill the misc wave");
+    static_assert(NGATE / 4 <= 64 * NGI, "gate pieces fit the misc wave");
 };
 
 template <int DK>
@@ -294,7 +306,7 @@ struct MainSmem {
     _Float16 VT[2][Cfg::SV * C];
     _Float16 ST[2][Cfg::SV * DK];   // f16 state slice transposed, by chunk parity
     _Float16 ET[Cfg::SV * C];       // E of the current chunk, transposed
-    float g[2][C], gam[2][C], dec[2][C];
+    float gate[2][NGATE];           // g, gamma, d of each buffered chunk
     int flagE;
 };
 
@@ -312,26 +324,26 @@ __device__ __forceinline__ half8 bf16x8_to_h8(const uint4& r) {
 template <int DK>
 struct Prefetch {
     uint4 a[MainCfg<DK>::NA];
-    float alpha;
     int chunk;
 };
 
-// Loader pieces are 16 bytes.  k waves: (token t, piece cq) with consecutive
-// pieces of one row on consecutive lanes, so a wave's load covers whole rows.
-// Misc wave: a[0 .. NVI) hold v (token, piece of the slice), a[NVI ..) hold
-// T' (10 lower blocks, in order).  Loads are unconditional: tokens past the
-// end read the last token's row (always in bounds) and are zeroed later by
-// loader_convert, so no load sits behind a branch.
-template <int DK>
-__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, bool misc, int lt, int lane,
-                                            const uint16_t* k, const uint16_t* v, const float* alpha,
-                                            const _Float16* ws, long tok0, int T, int H, int DV, int col0,
-                                            int h, long wsbase) {
+// Loader pieces are 16 bytes.  k waves (MISC = false): (token t, piece cq)
+// with consecutive pieces of one row on consecutive lanes, so a wave's load
+// covers whole rows.  Misc wave: a[0 .. NVI) hold v (token, piece of the
+// slice), then NTI pieces of T' (its 10 lower blocks, in order), then the
+// gate pieces.  Loads are unconditional: tokens past the end read the last
+// token's row and pieces past the gates re-read the last one (always in
+// bounds); loader_convert zeroes what lies past the end, so no load sits
+// behind a branch.
+template <int DK, bool MISC>
+__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, int lane, const uint16_t* k,
+                                            const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
+                                            int DV, int col0, int h, long wsbase) {
     using Cfg = MainCfg<DK>;
     const int t0 = chunk * C;
     pf.chunk = chunk;
     auto row = [&](int t) { return (tok0 + min(t0 + t, T - 1)) * H + h; };
-    if (!misc) {
+    if constexpr (!MISC) {
 #pragma unroll
         for (int i = 0; i < Cfg::NQ; ++i) {
             const int idx = min(lt + i * Cfg::LQK, 64 * Cfg::QC - 1);
@@ -345,21 +357,20 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, bool mi
             const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
             pf.a[i] = *reinterpret_cast<const uint4*>(v + row(t) * DV + col0 + cv * 8);
         }
+        const uint4* src = reinterpret_cast<const uint4*>(ws + wsbase + static_cast<long>(chunk) * WS_CHUNK);
 #pragma unroll
-        for (int i = 0; i < Cfg::NTI; ++i)
-            pf.a[Cfg::NVI + i] = *reinterpret_cast<const uint4*>(ws + wsbase + static_cast<long>(chunk) * NTB * TBLK +
-                                                                 (lane + i * 64) * 8);
-        pf.alpha = alpha[row(lane)];
+        for (int i = 0; i < Cfg::NTI + Cfg::NGI; ++i)
+            pf.a[Cfg::NVI + i] = src[min(lane + i * 64, WS_CHUNK / 8 - 1)];
     }
 }
 
-// bf16 pieces (k, v) -> fp16 pieces in place, zero for tokens past the end;
-// alpha becomes 1 there.  T' pieces are fp16 already.
-template <int DK>
-__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf, bool misc, int lt, int lane, int T) {
+// bf16 pieces (k, v) -> fp16 pieces in place, zero for tokens past the end.
+// T' and gate pieces are stored as they are.
+template <int DK, bool MISC>
+__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf, int lt, int lane, int T) {
     using Cfg = MainCfg<DK>;
     const int t0 = pf.chunk * C;
-    if (!misc) {
+    if constexpr (!MISC) {
 #pragma unroll
         for (int i = 0; i < Cfg::NQ; ++i) {
             const int idx = lt + i * Cfg::LQK;
@@ -374,15 +385,13 @@ __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf, bool misc, int 
             const half8 hv = bf16x8_to_h8(ok ? pf.a[i] : make_uint4(0, 0, 0, 0));
             pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
         }
-        if (t0 + lane >= T) pf.alpha = 1.f;
     }
 }
 
-template <int DK>
-__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int buf, bool misc, int lt,
-                                             int lane) {
+template <int DK, bool MISC>
+__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int buf, int lt, int lane) {
     using Cfg = MainCfg<DK>;
-    if (!misc) {
+    if constexpr (!MISC) {
 #pragma unroll
         for (int i = 0; i < Cfg::NQ; ++i) {
             const int idx = lt + i * Cfg::LQK;
@@ -394,35 +403,69 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
                 for (int e = 0; e < 8; ++e) sm.KT[buf][swz_t(cq * 8 + e, t)] = kh[e];
             }
         }
-        return;
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < Cfg::NVI; ++i) {
-        const int idx = lane + i * 64;
-        const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
-        const half8 vh = *reinterpret_cast<const half8*>(&pf.a[i]);
+        for (int i = 0; i < Cfg::NVI; ++i) {
+            const int idx = lane + i * 64;
+            const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
+            const half8 vh = *reinterpret_cast<const half8*>(&pf.a[i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.VT[buf][swz_t(cv * 8 + e, t)] = vh[e];
-    }
+            for (int e = 0; e < 8; ++e) sm.VT[buf][swz_t(cv * 8 + e, t)] = vh[e];
+        }
 #pragma unroll
-    for (int i = 0; i < Cfg::NTI; ++i) {
-        const int idx = lane + i * 64;
-        const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-        // lower block index -> (I, J): (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
-        const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
-        const int J = blk - I * (I + 1) / 2;
-        *reinterpret_cast<uint4*>(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)]) = pf.a[Cfg::NVI + i];
-    }
-    float lg = fmaxf(logf(pf.alpha), kLogDecayFloor);
+        for (int i = 0; i < Cfg::NTI; ++i) {
+            const int idx = lane + i * 64;
+            const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
+            // lower block index -> (I, J): (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
+            const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
+            const int J = blk - I * (I + 1) / 2;
+            *reinterpret_cast<uint4*>(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)]) = pf.a[Cfg::NVI + i];
+        }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(lg, off, 64);
-        if (lane >= off) lg += t;
+        for (int i = 0; i < Cfg::NGI; ++i) {
+            const int idx = lane + i * 64;
+            if (idx < NGATE / 4)
+                *reinterpret_cast<uint4*>(&sm.gate[buf][4 * idx]) = pf.a[Cfg::NVI + Cfg::NTI + i];
+        }
     }
-    const float glast = __shfl(lg, C - 1, 64);
-    sm.g[buf][lane] = lg;
-    sm.gam[buf][lane] = expf(lg);
-    sm.dec[buf][lane] = expf(glast - lg);
+}
+
+// Loader role: during chunk c the loads of chunk c+2 are issued into one
+// register set, then chunk c+1 (loaded during chunk c-1, in the other set) is
+// converted and stored to the other LDS buffer.  One barrier after the
+// prologue and one per chunk, as in the other roles.
+template <int DK, bool MISC>
+__device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* k,
+                                            const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
+                                            int DV, int col0, int h, long wsbase) {
+    Prefetch<DK> pa, pb;
+    auto ld = [&](Prefetch<DK>& pf, int c) {
+        loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+    };
+    auto put = [&](Prefetch<DK>& pf, int c) {
+        loader_convert<DK, MISC>(pf, lt, lane, T);
+        loader_store<DK, MISC>(pf, sm, c & 1, lt, lane);
+    };
+    if (nchunks > 0) {
+        ld(pa, 0);
+        put(pa, 0);
+        ld(pa, 1);
+    }
+    __syncthreads();
+    // Chunk pairs in an unconditional body (exact wait counts), odd tail after.
+    // Loads past the last chunk re-read it (clamped).  When c + 2 == nchunks
+    // the second store writes that copy into the buffer of chunk c, which
+    // nothing reads any more (chunk c + 1 is the last).
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        ld(pb, c + 2);
+        put(pa, c + 1);
+        __syncthreads();
+        ld(pa, c + 3);
+        put(pb, c + 2);
+        __syncthreads();
+    }
+    if (c < nchunks) __syncthreads();
 }
 
 template <int DK>
@@ -495,7 +538,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     }
     float4 gm[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4*>(&sm.gam[buf][I * 16 + 4 * lq]);
+    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4*>(&sm.gate[buf][C + I * 16 + 4 * lq]);
     __builtin_amdgcn_sched_barrier(0);
     // R = V - gamma K S, as the split-K B operand of T' R
     half4 rh[NB];
@@ -523,8 +566,8 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     }
     float4 dc[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4*>(&sm.dec[buf][I * 16 + 4 * lq]);
-    const float gl = sm.gam[buf][C - 1];
+    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4*>(&sm.gate[buf][2 * C + I * 16 + 4 * lq]);
+    const float gl = sm.gate[buf][C + C - 1];
     __builtin_amdgcn_sched_barrier(0);
     // D E as the B operand of K^T (D E)
     half4 eh[NB];
@@ -664,14 +707,14 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, const QRegs<DK>& 
     // (a masked entry may overflow to inf; the select discards it).
     float4 gi4[NB];
 #pragma unroll
-    for (int J = 0; J < NB; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.g[buf][J * 16 + 4 * lq]);
+    for (int J = 0; J < NB; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.gate[buf][J * 16 + 4 * lq]);
     half8 Pb[2][2];
     float gam_t[2];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
         const int t = Irow[ii] * 16 + lr;
-        const float gt = sm.g[buf][t];
-        gam_t[ii] = sm.gam[buf][t];
+        const float gt = sm.gate[buf][t];
+        gam_t[ii] = sm.gate[buf][C + t];
         half4 ph[NB];
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
@@ -708,8 +751,7 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, const QRegs<DK>& 
 
 template <int DK>
 __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-                                                   const float* __restrict__ beta, const _Float16* __restrict__ ws,
+                                                   const uint16_t* __restrict__ v, const _Float16* __restrict__ ws,
                                                    const float* __restrict__ S0, float* __restrict__ S_out,
                                                    float* __restrict__ y, int B, int T, int H, int DV, int nsl,
                                                    float scale) {
@@ -726,7 +768,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     const int col0 = slice * Cfg::SV;
     const long tok0 = static_cast<long>(b) * T;
     const int nchunks = (T + C - 1) / C;
-    const long wsbase = static_cast<long>(bh) * nchunks * NTB * TBLK;
+    const long wsbase = static_cast<long>(bh) * nchunks * WS_CHUNK;
 
     const bool is_state = (w == Cfg::W_STATE);
     const bool is_out = (w >= Cfg::W_OUT0 && w < Cfg::W_OUT0 + 2);
@@ -777,39 +819,17 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
         };
         if (nchunks > 0) load_q<DK>(qa, q, 0, rp, lane, tok0, T, H, h);
         __syncthreads();
-        for (int c = 0; c < nchunks; c += 2) {
+        // chunk pairs in an unconditional body (exact wait counts), odd tail after
+        int c = 0;
+        for (; c + 1 < nchunks; c += 2) {
             step(c, qa, qb);
-            if (c + 1 < nchunks) step(c + 1, qb, qa);
+            step(c + 1, qb, qa);
         }
+        if (c < nchunks) step(c, qa, qb);
+    } else if (misc) {
+        loader_role<DK, true>(sm, nchunks, lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     } else {
-        // loader: during chunk c the loads of chunk c+2 are issued into one
-        // register set, then chunk c+1 (loaded during chunk c-1, in the other
-        // set) is converted and stored to the other LDS buffer.
-        Prefetch<DK> pa, pb;
-        auto ld = [&](Prefetch<DK>& pf, int c) {
-            loader_load<DK>(pf, min(c, nchunks - 1), misc, lt, lane, k, v, alpha, ws, tok0, T, H, DV, col0, h,
-                            wsbase);
-        };
-        auto put = [&](Prefetch<DK>& pf, int c) {
-            loader_convert<DK>(pf, misc, lt, lane, T);
-            loader_store<DK>(pf, sm, c & 1, misc, lt, lane);
-        };
-        if (nchunks > 0) {
-            ld(pa, 0);
-            put(pa, 0);
-            ld(pa, 1);
-        }
-        __syncthreads();
-        for (int c = 0; c < nchunks; c += 2) {
-            ld(pb, c + 2);
-            if (c + 1 < nchunks) put(pa, c + 1);
-            __syncthreads();
-            if (c + 1 < nchunks) {
-                ld(pa, c + 3);
-                if (c + 2 < nchunks) put(pb, c + 2);
-                __syncthreads();
-            }
-        }
+        loader_role<DK, false>(sm, nchunks, lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     }
 }
 
@@ -828,7 +848,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
     const int groups = (a.B * a.H + kXcds - 1) / kXcds;
     hipLaunchKernelGGL((main_kernel<DK>), dim3(groups * kXcds * nsl), dim3(Cfg::NT), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.alpha, a.beta, ws, a.initial_state, a.final_state, a.y,
+                       static_cast<const uint16_t*>(a.v), ws, a.initial_state, a.final_state, a.y,
                        a.B, a.T, a.H, a.dv, nsl, a.scale);
     return hipGetLastError();
 }
@@ -837,7 +857,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
 
 size_t prefill_bf16_workspace_bytes(int B, int T, int H) {
     const long nchunks = (T + chunked::C - 1) / chunked::C;
-    return static_cast<size_t>(B) * H * nchunks * chunked::NTB * chunked::TBLK * sizeof(_Float16);
+    return static_cast<size_t>(B) * H * nchunks * chunked::WS_CHUNK * sizeof(_Float16);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a) {

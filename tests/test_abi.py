@@ -80,9 +80,11 @@ def test_prefill_rejects(kwargs, status):
 
 def test_workspace_bytes():
     lib = gdn.load_library()
-    # bf16: one block set of 10 fp16 16x16 blocks per (sequence, head, 64-token chunk)
-    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 2 * 10 * 256 * 2
-    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 2 * 3 * 2 * 5120
+    # bf16: per (sequence, head, 64-token chunk) the 10 lower fp16 16x16 blocks
+    # of T' (5120 bytes) and three float32 gate vectors of 64 (768 bytes)
+    per_chunk = 10 * 256 * 2 + 3 * 64 * 4
+    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 2 * per_chunk
+    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 2 * 3 * 2 * per_chunk
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 0) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 0, 3, 128, 128, 1) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 48, 128, 1) == 0
