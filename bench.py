@@ -13,6 +13,7 @@ prefill workload.  Rank 0 prints one JSON line.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -53,6 +54,45 @@ def norm_bytes(rows, dv, in_bytes=2):
     return rows * dv * (4 + 2 * in_bytes)
 
 
+PREFILL_SOURCES = ("linear_attention_recurrence_rule_amd/csrc/prefill_chunked.hip",
+                   "linear_attention_recurrence_rule_amd/csrc/gdn_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_long_T32K_traffic.md")
+
+
+def prefill_source_hash():
+    h = hashlib.sha256()
+    for rel in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill call from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith(("traffic_bytes_per_call:",
+                                                                             "source_hash:")))
+    except OSError:
+        return None
+    if fields.get("source_hash", "").strip() != prefill_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_call"])
+
+
+def calibrate_copy(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,12 +101,19 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is per "
               "(sequence, head) and needs no collectives; see DESIGN.md for how it would shard.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
     import linear_attention_recurrence_rule_amd as gdn
@@ -150,10 +197,10 @@ def main():
                    "B": B, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": 64,
                    "qkv_dtype": "bf16", "state_dtype": "fp32", "y_dtype": "fp32",
                    "epilogue_out_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "prefill_kernel", "achieved": pf_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pf_gbps / HBM_PEAK_GBPS,
-                     "traffic": None, "algorithmic_bytes_per_launch": pf_bytes,
-                     "avg_launch_ms": prefill_ms,
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep_kernel + main_kernel)",
+                     "achieved": pf_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": pf_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": pf_bytes, "avg_launch_ms": prefill_ms,
                      "mfma_tflops": pf_tflops, "mfma_frac_of_bf16_peak": pf_tflops / BF16_MFMA_PEAK_TFLOPS},
         "epilogue": {"kernel": "gated_rmsnorm_kernel", "avg_launch_ms": norm_ms,
                      "achieved": nb / (norm_ms * 1e-3) / 1e9, "unit": "GB/s",
@@ -201,7 +248,7 @@ def main():
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import gated_delta_recurrence
-        Ts = 1024
+        Ts = args.cpu_tokens
         log(f"cpu oracle: B=1 H={H} T={Ts} (single thread)")
         ds = config_prefill_inputs(2, T=Ts)
         with threadpool_limits(limits=1):
