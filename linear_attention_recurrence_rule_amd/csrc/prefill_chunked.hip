@@ -23,17 +23,20 @@
 //               straight from global memory into registers a chunk ahead; Q S
 //               and P (built transposed so it feeds the MFMA from registers),
 //               then, once the state wave has published E, Y += P E -> y.
-//   waves 3..7  loader waves (k and k^T on waves 3..6; v, T' and the gates
+//   waves 3..7  loader waves (k on waves 3..6; v, T' and the gates
 //               on wave 7): chunk c+1 goes to the other LDS buffer from
 //               registers loaded during the previous chunk.
 // Loads run one chunk ahead in two register sets; they are unconditional
-// (clamped addresses, out-of-range data zeroed afterwards) so that the
-// compiler's wait counts stay exact across the chunk loop.
+// (addresses clamped to the last token, whose copies past the end of the
+// sequence are harmless: beta = 0 there) so that the compiler's wait counts
+// stay exact across the chunk loop.
 // Split-K operand layout: for a 16x16x32 MFMA, slot s of lane (m + 16 g) holds
 // K-index 16*(s/4) + 4 g + s%4 of its row/column.  Two 16x16 accumulator tiles
 // (lane (n + 16 g) holds rows 4 g .. 4 g + 3 of column n) stacked along K are
 // exactly such a B operand, and A operands are read from LDS in the same order.
-// LDS tiles are fp16 row-major with 16-byte chunks XOR-swizzled by row.
+// LDS tiles are fp16 row-major with 16-byte chunks XOR-swizzled by row; the
+// operands that need a tile transposed (K^T, and V in accumulator order) are
+// read with gfx950's transposing LDS load instead of a second, transposed copy.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -73,20 +76,14 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * LD + (((col >> 3) ^ row) & kMask) * 8 + (col & 7);
 }
 
-// Token-major tiles (rows = d_k index or value column, C tokens per row) are
-// written one 2-byte element at a time by the loaders, 16 rows 8 apart per
-// instruction, and read as 8-byte runs of 4 tokens from 16 consecutive rows by
-// the MFMA operand loads.  XORing the 4-token unit index with
-// (row & 15) ^ ((row >> 3) & 15) puts both access patterns on distinct banks.
-__device__ __forceinline__ int swz_t(int row, int tok) {
-    const int h = (row & 15) ^ ((row >> 3) & 15);
-    return row * C + ((((tok >> 2) ^ h) & 15) << 2) + (tok & 3);
-}
-__device__ __forceinline__ half4 ld4_t(const _Float16* base, int row, int tok) {
-    return *reinterpret_cast<const half4*>(base + swz_t(row, tok));
-}
-__device__ __forceinline__ half8 ld_split_t(const _Float16* base, int row, int k0, int g) {
-    return cat(ld4_t(base, row, k0 + 4 * g), ld4_t(base, row, k0 + 16 + 4 * g));
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4 a + b receives, in slot j, element b of the 4-element run addressed
+// by lane 4 j + a of the same group.
+typedef __fp16 fp16x4_tr __attribute__((__vector_size__(8)));
+__device__ __forceinline__ half4 ld_tr4(const _Float16* p) {
+    const fp16x4_tr r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+        (__attribute__((address_space(3))) fp16x4_tr*)(const_cast<_Float16*>(p)));
+    return __builtin_bit_cast(half4, r);
 }
 template <int LD>
 __device__ __forceinline__ half4 ld4(const _Float16* base, int row, int col) {
@@ -105,6 +102,17 @@ __device__ __forceinline__ half8 ld_split(const _Float16* base, int row, int k0,
 template <int LD>
 __device__ __forceinline__ half8 ld_split_lo(const _Float16* base, int row, int k0, int g) {
     return cat(ld4<LD>(base, row, k0 + 4 * g), half4{});
+}
+// Split-K operand of the transpose of a row-major (swz<LD>) tile X: lane
+// (m + 16 g) gets X[k0 + 16 (s / 4) + 4 g + s % 4][m0 + m] in slot s, so the
+// operand's rows are columns m0 .. m0 + 15 of X and its K index runs over rows
+// k0 .. k0 + 31 of X.  Lane (4 j + a) of group g addresses the run
+// X[k0 + 4 g + j][m0 + 4 a .. + 4] (and 16 rows further for slots 4 .. 7).
+template <int LD>
+__device__ __forceinline__ half8 ld_split_tr(const _Float16* base, int m0, int k0, int lane) {
+    const int g = lane >> 4, x = lane & 15;
+    const int row = k0 + 4 * g + (x >> 2), col = m0 + 4 * (x & 3);
+    return cat(ld_tr4(base + swz<LD>(row, col)), ld_tr4(base + swz<LD>(row + 16, col)));
 }
 
 // ===========================================================================
@@ -301,9 +309,8 @@ template <int DK>
 struct MainSmem {
     using Cfg = MainCfg<DK>;
     _Float16 K[2][C * DK];
-    _Float16 KT[2][DK * C];
     _Float16 Tp[2][C * C];
-    _Float16 VT[2][Cfg::SV * C];
+    _Float16 V[2][C * Cfg::SV];     // v slice, row-major (token, column)
     _Float16 ST[2][Cfg::SV * DK];   // f16 state slice transposed, by chunk parity
     _Float16 ET[Cfg::SV * C];       // E of the current chunk, transposed
     float gate[2][NGATE];           // g, gamma, d of each buffered chunk
@@ -333,8 +340,7 @@ struct Prefetch {
 // slice), then NTI pieces of T' (its 10 lower blocks, in order), then the
 // gate pieces.  Loads are unconditional: tokens past the end read the last
 // token's row and pieces past the gates re-read the last one (always in
-// bounds); loader_convert zeroes what lies past the end, so no load sits
-// behind a branch.
+// bounds), so no load sits behind a branch.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, int lane, const uint16_t* k,
                                             const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
@@ -364,27 +370,19 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt,
     }
 }
 
-// bf16 pieces (k, v) -> fp16 pieces in place, zero for tokens past the end.
-// T' and gate pieces are stored as they are.
+// bf16 pieces (k, v) -> fp16 pieces in place; T' and gate pieces are stored
+// as they are.  Rows past the end of the sequence hold a copy of the last
+// row and need no zeroing: there beta = 0 and alpha = 1 (set by prep_kernel),
+// so T' has zero rows and columns for them and they reach neither E, nor y,
+// nor the state.
 template <int DK, bool MISC>
-__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf, int lt, int lane, int T) {
+__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     using Cfg = MainCfg<DK>;
-    const int t0 = pf.chunk * C;
-    if constexpr (!MISC) {
+    constexpr int N = MISC ? Cfg::NVI : Cfg::NQ;
 #pragma unroll
-        for (int i = 0; i < Cfg::NQ; ++i) {
-            const int idx = lt + i * Cfg::LQK;
-            const bool ok = idx < 64 * Cfg::QC && t0 + idx / Cfg::QC < T;
-            const half8 hv = bf16x8_to_h8(ok ? pf.a[i] : make_uint4(0, 0, 0, 0));
-            pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < Cfg::NVI; ++i) {
-            const bool ok = t0 + (lane + i * 64) / (Cfg::SV / 8) < T;
-            const half8 hv = bf16x8_to_h8(ok ? pf.a[i] : make_uint4(0, 0, 0, 0));
-            pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
-        }
+    for (int i = 0; i < N; ++i) {
+        const half8 hv = bf16x8_to_h8(pf.a[i]);
+        pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
     }
 }
 
@@ -399,8 +397,6 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
                 const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
                 const half8 kh = *reinterpret_cast<const half8*>(&pf.a[i]);
                 *reinterpret_cast<half8*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = kh;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm.KT[buf][swz_t(cq * 8 + e, t)] = kh[e];
             }
         }
     } else {
@@ -408,9 +404,7 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
         for (int i = 0; i < Cfg::NVI; ++i) {
             const int idx = lane + i * 64;
             const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
-            const half8 vh = *reinterpret_cast<const half8*>(&pf.a[i]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.VT[buf][swz_t(cv * 8 + e, t)] = vh[e];
+            *reinterpret_cast<uint4*>(&sm.V[buf][t * Cfg::SV + cv * 8]) = pf.a[i];
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NTI; ++i) {
@@ -443,7 +437,7 @@ __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int l
         loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     };
     auto put = [&](Prefetch<DK>& pf, int c) {
-        loader_convert<DK, MISC>(pf, lt, lane, T);
+        loader_convert<DK, MISC>(pf);
         loader_store<DK, MISC>(pf, sm, c & 1, lt, lane);
     };
     if (nchunks > 0) {
@@ -498,7 +492,6 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
     const _Float16* Tb = sm.Tp[buf];
-    const _Float16* KTb = sm.KT[buf];
     auto kfrag = [&](int I, int kk) {
         return DK >= 32 ? ld_split<DK>(Kb, I * 16 + lr, kk * 32, lq) : ld_split_lo<DK>(Kb, I * 16 + lr, 0, lq);
     };
@@ -508,7 +501,8 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     for (int I = 0; I < NB; ++I) ka[0][I] = kfrag(I, 0);
     half4 vv[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) vv[I] = ld4_t(sm.VT[buf], lr, I * 16 + 4 * lq);
+    for (int I = 0; I < NB; ++I)
+        vv[I] = ld_tr4(&sm.V[buf][(I * 16 + 4 * lq + (lr >> 2)) * Cfg::SV + 4 * (lr & 3)]);
     float4v ks[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) ks[I] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -523,7 +517,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
         for (int I = 0; I < NB; ++I) ks[I] = mma(ka[kk & 1][I], st.Sb[kk], ks[I]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // T' and the first half of k^T, read while K S finishes
+    // T' and the first half of K^T, read while K S finishes
     half8 ta[NB][2];
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
@@ -533,8 +527,8 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     half8 kt0[NH][2];
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
-        kt0[r][0] = ld_split_t(KTb, r * 16 + lr, 0, lq);
-        kt0[r][1] = ld_split_t(KTb, r * 16 + lr, 32, lq);
+        kt0[r][0] = ld_split_tr<DK>(Kb, r * 16, 0, lane);
+        kt0[r][1] = ld_split_tr<DK>(Kb, r * 16, 32, lane);
     }
     float4 gm[NB];
 #pragma unroll
@@ -555,13 +549,13 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
         if (I >= 2) e[I] = mma(ta[I][1], Rb1, e[I]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // second half of k^T and the decay-to-chunk-end factors, read while T' R runs
+    // second half of K^T and the decay-to-chunk-end factors, read while T' R runs
     half8 kt1[NH][2];
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
         if (NH + r < NST) {
-            kt1[r][0] = ld_split_t(KTb, (NH + r) * 16 + lr, 0, lq);
-            kt1[r][1] = ld_split_t(KTb, (NH + r) * 16 + lr, 32, lq);
+            kt1[r][0] = ld_split_tr<DK>(Kb, (NH + r) * 16, 0, lane);
+            kt1[r][1] = ld_split_tr<DK>(Kb, (NH + r) * 16, 32, lane);
         }
     }
     float4 dc[NB];
@@ -619,7 +613,7 @@ __device__ __forceinline__ void load_q(QRegs<DK>& qr, const uint16_t* q, int chu
     qr.chunk = chunk;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-        const int t = min(chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr, T - 1);   // clamped; zeroed later
+        const int t = min(chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr, T - 1);   // clamped
 #pragma unroll
         for (int kk = 0; kk < Cfg::KSTEP; ++kk) {
             const int col = DK >= 32 ? kk * 32 + 8 * lq : 8 * (lq & 1);
@@ -628,20 +622,18 @@ __device__ __forceinline__ void load_q(QRegs<DK>& qr, const uint16_t* q, int chu
     }
 }
 
-// bf16 -> fp16 in place; rows past the end (and, for d_k = 16, the unused
-// upper K slices) become zero.
+// bf16 -> fp16 in place.  Rows past the end (copies of the last row) only
+// produce y rows that are never stored; for d_k = 16 the duplicated upper K
+// slices meet zero slices of the other operand.
 template <int DK>
-__device__ __forceinline__ void q_convert(QRegs<DK>& qr, int rp, int lane, int T) {
-    const int lr = lane & 15, lq = lane >> 4;
+__device__ __forceinline__ void q_convert(QRegs<DK>& qr) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const bool ok = qr.chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr < T && (DK >= 32 || lq < 2);
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
         for (int kk = 0; kk < MainCfg<DK>::KSTEP; ++kk) {
-            const half8 hv = bf16x8_to_h8(ok ? qr.raw[ii][kk] : make_uint4(0, 0, 0, 0));
+            const half8 hv = bf16x8_to_h8(qr.raw[ii][kk]);
             qr.raw[ii][kk] = *reinterpret_cast<const uint4*>(&hv);
         }
-    }
 }
 
 // One chunk of output (output wave `rp`: token blocks {0,3} or {1,2}).  Its q
@@ -813,7 +805,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
         QRegs<DK> qa, qb;
         auto step = [&](int c, QRegs<DK>& cur, QRegs<DK>& nxt) {
             load_q<DK>(nxt, q, min(c + 1, nchunks - 1), rp, lane, tok0, T, H, h);
-            q_convert<DK>(cur, rp, lane, T);
+            q_convert<DK>(cur);
             output_chunk<DK>(sm, cur, c, rp, lane, y, tok0, T, H, DV, col0, h, scale, &spin_error);
             __syncthreads();
         };
