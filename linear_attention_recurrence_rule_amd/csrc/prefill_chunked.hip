@@ -19,13 +19,13 @@
 //               operand it produces (S, R, E) is fed to the next MFMA straight
 //               from the accumulator registers (split-K operand layout below),
 //               so the chain has no LDS round trip.
-//   waves 1, 2  output waves (token blocks {0,3} and {1,2}): their q rows come
-//               straight from global memory into registers a chunk ahead; Q S
-//               and P (built transposed so it feeds the MFMA from registers),
-//               then, once the state wave has published E, Y += P E -> y.
-//   waves 3..7  loader waves (k on waves 3..6; v, T' and the gates
-//               on wave 7): chunk c+1 goes to the other LDS buffer from
-//               registers loaded during the previous chunk.
+//   waves 1, 2  output waves (token blocks {0,3} and {1,2}): Q S and P (built
+//               transposed so it feeds the MFMA from registers), then, once
+//               the state wave has published E, Y += P E -> y.
+//   waves 3..7  loader waves (q and k on waves 3, 5, 6, 7; v, T' and the
+//               gates on wave 4, which shares the state wave's SIMD): chunk
+//               c+1 goes to the other LDS buffer from registers loaded during
+//               the previous chunk.
 // Loads run one chunk ahead in two register sets; they are unconditional
 // (addresses clamped to the last token, whose copies past the end of the
 // sequence are harmless: beta = 0 there) so that the compiler's wait counts
@@ -288,17 +288,20 @@ template <int DK>
 struct MainCfg {
     static constexpr int SV = 16;                  // value columns per workgroup
     static constexpr int NT = 512;                 // 8 waves
-    static constexpr int W_STATE = 0, W_OUT0 = 1;  // state wave, two output waves
-    static constexpr int W_QK0 = 3, NQKW = 4;      // k loader waves 3..6
-    static constexpr int W_MISC = 7;               // v, T' and gates loader
-    static constexpr int LQK = NQKW * 64;          // k loader threads
+    // Waves w and w + 4 share a SIMD.  The state wave (0) shares its SIMD with
+    // the lightest role, the misc loader (4); the q/k loaders are waves 3, 5,
+    // 6 and 7.
+    static constexpr int W_STATE = 0, W_OUT0 = 1;  // state wave, output waves 1 and 2
+    static constexpr int W_MISC = 4;               // v, T' and gates loader
+    static constexpr int NQKW = 4;                 // q and k loader waves
+    static constexpr int LQK = NQKW * 64;          // q/k loader threads
     static constexpr int QC = DK / 8;              // 16-byte pieces per q/k row
-    static constexpr int NQ = (64 * QC + LQK - 1) / LQK;   // k pieces per thread
+    static constexpr int NQ = (64 * QC + LQK - 1) / LQK;   // k (and q) pieces per thread
     static constexpr int NVI = 64 * (SV / 8) / 64;         // v pieces per misc lane
     static constexpr int NTI = NTB * TBLK / 8 / 64;        // T' pieces per misc lane
     static constexpr int NGI = (NGATE / 4 + 63) / 64;      // gate pieces per misc lane
     static constexpr int NMI = NVI + NTI + NGI;            // misc pieces per lane
-    static constexpr int NA = NQ > NMI ? NQ : NMI;
+    static constexpr int NA = 2 * NQ > NMI ? 2 * NQ : NMI;
     static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1; // 32-wide K steps over d_k
     static constexpr int NST = DK / 16;            // 16-row state tiles
     static_assert(NTB * TBLK / 8 == NTI * 64, "T' pieces fill the misc wave");
@@ -309,6 +312,7 @@ template <int DK>
 struct MainSmem {
     using Cfg = MainCfg<DK>;
     _Float16 K[2][C * DK];
+    _Float16 Q[2][C * DK];
     _Float16 Tp[2][C * C];
     _Float16 V[2][C * Cfg::SV];     // v slice, row-major (token, column)
     _Float16 ST[2][Cfg::SV * DK];   // f16 state slice transposed, by chunk parity
@@ -334,17 +338,17 @@ struct Prefetch {
     int chunk;
 };
 
-// Loader pieces are 16 bytes.  k waves (MISC = false): (token t, piece cq)
-// with consecutive pieces of one row on consecutive lanes, so a wave's load
-// covers whole rows.  Misc wave: a[0 .. NVI) hold v (token, piece of the
+// Loader pieces are 16 bytes.  q/k waves (MISC = false): a[i] holds k and
+// a[NQ + i] q at (token t, piece cq), with consecutive pieces of one row on
+// consecutive lanes, so a wave's load covers whole rows.  Misc wave: a[0 .. NVI) hold v (token, piece of the
 // slice), then NTI pieces of T' (its 10 lower blocks, in order), then the
 // gate pieces.  Loads are unconditional: tokens past the end read the last
 // token's row and pieces past the gates re-read the last one (always in
 // bounds), so no load sits behind a branch.
 template <int DK, bool MISC>
-__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, int lane, const uint16_t* k,
-                                            const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
-                                            int DV, int col0, int h, long wsbase) {
+__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, int lane, const uint16_t* q,
+                                            const uint16_t* k, const uint16_t* v, const _Float16* ws, long tok0,
+                                            int T, int H, int DV, int col0, int h, long wsbase) {
     using Cfg = MainCfg<DK>;
     const int t0 = chunk * C;
     pf.chunk = chunk;
@@ -355,6 +359,7 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt,
             const int idx = min(lt + i * Cfg::LQK, 64 * Cfg::QC - 1);
             const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
             pf.a[i] = *reinterpret_cast<const uint4*>(k + row(t) * DK + cq * 8);
+            pf.a[Cfg::NQ + i] = *reinterpret_cast<const uint4*>(q + row(t) * DK + cq * 8);
         }
     } else {
 #pragma unroll
@@ -370,15 +375,15 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt,
     }
 }
 
-// bf16 pieces (k, v) -> fp16 pieces in place; T' and gate pieces are stored
-// as they are.  Rows past the end of the sequence hold a copy of the last
-// row and need no zeroing: there beta = 0 and alpha = 1 (set by prep_kernel),
-// so T' has zero rows and columns for them and they reach neither E, nor y,
-// nor the state.
+// bf16 pieces (q, k, v) -> fp16 pieces in place; T' and gate pieces are
+// stored as they are.  Rows past the end of the sequence hold a copy of the
+// last row and need no zeroing: there beta = 0 and alpha = 1 (set by
+// prep_kernel), so T' has zero rows and columns for them and they reach
+// neither E nor the state, and their y rows are never stored.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     using Cfg = MainCfg<DK>;
-    constexpr int N = MISC ? Cfg::NVI : Cfg::NQ;
+    constexpr int N = MISC ? Cfg::NVI : 2 * Cfg::NQ;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const half8 hv = bf16x8_to_h8(pf.a[i]);
@@ -386,8 +391,8 @@ __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     }
 }
 
-template <int DK, bool MISC>
-__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int buf, int lt, int lane) {
+template <int DK, bool MISC, int buf>
+__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int lt, int lane) {
     using Cfg = MainCfg<DK>;
     if constexpr (!MISC) {
 #pragma unroll
@@ -395,8 +400,8 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
             const int idx = lt + i * Cfg::LQK;
             if (idx < 64 * Cfg::QC) {
                 const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
-                const half8 kh = *reinterpret_cast<const half8*>(&pf.a[i]);
-                *reinterpret_cast<half8*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = kh;
+                *reinterpret_cast<uint4*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = pf.a[i];
+                *reinterpret_cast<uint4*>(&sm.Q[buf][swz<DK>(t, cq * 8)]) = pf.a[Cfg::NQ + i];
             }
         }
     } else {
@@ -429,20 +434,24 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
 // converted and stored to the other LDS buffer.  One barrier after the
 // prologue and one per chunk, as in the other roles.
 template <int DK, bool MISC>
-__device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* k,
+__device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* q,
+                                            const uint16_t* k,
                                             const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
                                             int DV, int col0, int h, long wsbase) {
     Prefetch<DK> pa, pb;
     auto ld = [&](Prefetch<DK>& pf, int c) {
-        loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+        loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     };
-    auto put = [&](Prefetch<DK>& pf, int c) {
+    // chunk c goes to LDS buffer c & 1 (a compile-time constant at each call)
+    auto put = [&](Prefetch<DK>& pf, auto buf) {
         loader_convert<DK, MISC>(pf);
-        loader_store<DK, MISC>(pf, sm, c & 1, lt, lane);
+        loader_store<DK, MISC, decltype(buf)::value>(pf, sm, lt, lane);
     };
+    const std::integral_constant<int, 0> even{};
+    const std::integral_constant<int, 1> odd{};
     if (nchunks > 0) {
         ld(pa, 0);
-        put(pa, 0);
+        put(pa, even);
         ld(pa, 1);
     }
     __syncthreads();
@@ -453,10 +462,10 @@ __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int l
     int c = 0;
     for (; c + 1 < nchunks; c += 2) {
         ld(pb, c + 2);
-        put(pa, c + 1);
+        put(pa, odd);    // chunk c + 1
         __syncthreads();
         ld(pa, c + 3);
-        put(pb, c + 2);
+        put(pb, even);   // chunk c + 2
         __syncthreads();
     }
     if (c < nchunks) __syncthreads();
@@ -482,13 +491,12 @@ __device__ __forceinline__ void state_refresh_operand(StateRegs<DK>& st) {
 // their LDS reads were issued one group earlier.  Scheduling barriers keep the
 // compiler from sinking the reads back next to their uses (it would otherwise
 // wait on every read).
-template <int DK>
+template <int DK, int buf>
 __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int chunk, int lane) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
     constexpr int NST = Cfg::NST;
     constexpr int NH = NST / 2 > 0 ? NST / 2 : 1;   // state tiles per half of the update
-    const int buf = chunk & 1;
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
     const _Float16* Tb = sm.Tp[buf];
@@ -597,133 +605,97 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     state_refresh_operand(st);
 }
 
-// q rows of the output wave's two token blocks, as the raw bf16 pieces of its
-// MFMA operands (lane (r + 16 g) holds q[row r][32 kk + 8 g .. + 8] per step kk).
-template <int DK>
-struct QRegs {
-    uint4 raw[2][MainCfg<DK>::KSTEP];   // bf16 as loaded; fp16 after q_convert
-    int chunk;
-};
-
-template <int DK>
-__device__ __forceinline__ void load_q(QRegs<DK>& qr, const uint16_t* q, int chunk, int rp, int lane, long tok0,
-                                       int T, int H, int h) {
-    using Cfg = MainCfg<DK>;
-    const int lr = lane & 15, lq = lane >> 4;
-    qr.chunk = chunk;
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const int t = min(chunk * C + (ii == 0 ? rp : 3 - rp) * 16 + lr, T - 1);   // clamped
-#pragma unroll
-        for (int kk = 0; kk < Cfg::KSTEP; ++kk) {
-            const int col = DK >= 32 ? kk * 32 + 8 * lq : 8 * (lq & 1);
-            qr.raw[ii][kk] = *reinterpret_cast<const uint4*>(q + ((tok0 + t) * H + h) * DK + col);
-        }
-    }
-}
-
-// bf16 -> fp16 in place.  Rows past the end (copies of the last row) only
-// produce y rows that are never stored; for d_k = 16 the duplicated upper K
-// slices meet zero slices of the other operand.
-template <int DK>
-__device__ __forceinline__ void q_convert(QRegs<DK>& qr) {
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int kk = 0; kk < MainCfg<DK>::KSTEP; ++kk) {
-            const half8 hv = bf16x8_to_h8(qr.raw[ii][kk]);
-            qr.raw[ii][kk] = *reinterpret_cast<const uint4*>(&hv);
-        }
-}
-
-// One chunk of output (output wave `rp`: token blocks {0,3} or {1,2}).  Its q
-// rows arrive in registers (loaded during the previous chunk).  Everything is
+// One chunk of output for output wave RP, which owns token blocks I0 = RP and
+// I1 = 3 - RP (so both waves build five of the ten lower P tiles).  Its q
+// rows, the k rows and the fp16 state slice come from LDS.  Everything is
 // computed transposed (K_J Q_I^T for P, S^T Q^T, E^T P^T), so that each lane
 // holds one token row: P feeds the last MFMA straight from registers in the
 // split-K order, and y leaves as one 16-byte store per lane and block.
-template <int DK>
-__device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, const QRegs<DK>& qr, int chunk, int rp, int lane,
-                                             float* y, long tok0, int T, int H, int DV, int col0, int h,
-                                             float scale, int* spin_error) {
+template <int DK, int buf, int RP>
+__device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int lane, float* ylane, long ytok,
+                                             int T, float scale) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
-    const int buf = chunk & 1;
+    constexpr int Irow[2] = {RP, 3 - RP};
+    constexpr int Jmax = 3 - RP;   // highest k block either q block needs
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
+    const _Float16* Qb = sm.Q[buf];
     const _Float16* STb = sm.ST[buf];
-    const int Irow[2] = {rp, 3 - rp};
-    const int Jmax = 3 - rp;   // highest k block either q block needs
-    // contiguous K-slices (lane (r + 16 g) holds K-index 8 g .. 8 g + 7 of step kk)
-    auto kfrag = [&](int J, int kk) {
-        return (DK >= 32 || lq < 2) ? ld8<DK>(Kb, J * 16 + lr, kk * 32 + 8 * lq) : half8{};
+    // contiguous K-slices: lane (r + 16 g) holds K-index 8 g .. 8 g + 7 of step
+    // kk (for d_k = 16 only g < 2 carry data; the rest are zero)
+    auto frag = [&](const _Float16* base, int row, int kk) {
+        return (DK >= 32 || lq < 2) ? ld8<DK>(base, row, kk * 32 + 8 * lq) : half8{};
     };
-    half8 sf[KS], kf[2][KS];
+    half8 sf[KS], qf[2][KS], kf[2][KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        sf[kk] = (DK >= 32 || lq < 2) ? ld8<DK>(STb, lr, kk * 32 + 8 * lq) : half8{};
-        kf[0][kk] = kfrag(0, kk);
+        sf[kk] = frag(STb, lr, kk);
+        qf[0][kk] = frag(Qb, Irow[0] * 16 + lr, kk);
+        qf[1][kk] = frag(Qb, Irow[1] * 16 + lr, kk);
+        kf[0][kk] = frag(Kb, lr, kk);
     }
-    const half8* qf0 = reinterpret_cast<const half8*>(qr.raw[0]);
-    const half8* qf1 = reinterpret_cast<const half8*>(qr.raw[1]);
     __builtin_amdgcn_sched_barrier(0);
     // (Q S)^T = S^T Q^T for both blocks: lane (t + 16 g) gets columns 4 g .. 4 g + 3 of row t
     float4v qs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        qs[0] = mma(sf[kk], qf0[kk], qs[0]);
-        qs[1] = mma(sf[kk], qf1[kk], qs[1]);
+        qs[0] = mma(sf[kk], qf[0][kk], qs[0]);
+        qs[1] = mma(sf[kk], qf[1][kk], qs[1]);
     }
-    // (Q K^T)^T tiles: k block J is read once, one block ahead of its MFMAs
+    // (Q K^T)^T tiles J <= I: k block J is read once, one block ahead of its MFMAs
     float4v pacc[2][NB];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int J = 0; J < NB; ++J) pacc[ii][J] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-        if (J > Jmax) break;
+    for (int J = 0; J <= Jmax; ++J) {
         if (J + 1 <= Jmax) {
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) kf[(J + 1) & 1][kk] = kfrag(J + 1, kk);
+            for (int kk = 0; kk < KS; ++kk) kf[(J + 1) & 1][kk] = frag(Kb, (J + 1) * 16 + lr, kk);
         }
         __builtin_amdgcn_sched_barrier(0);
+        pacc[0][J] = pacc[1][J] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            if (J <= Irow[0]) pacc[0][J] = mma(kf[J & 1][kk], qf0[kk], pacc[0][J]);
-            pacc[1][J] = mma(kf[J & 1][kk], qf1[kk], pacc[1][J]);   // Irow[1] = Jmax >= J
+            if (J <= Irow[0]) pacc[0][J] = mma(kf[J & 1][kk], qf[0][kk], pacc[0][J]);
+            pacc[1][J] = mma(kf[J & 1][kk], qf[1][kk], pacc[1][J]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // P = Gamma o (Q K^T), masked to i <= t; lane holds row t = 16 I + lr.  The
-    // exponentials are taken for every entry and the mask applied afterwards
-    // (a masked entry may overflow to inf; the select discards it).
+    // P = Gamma o (Q K^T) on the lower tiles, lane row t = 16 I + lr, columns
+    // i = 16 J + 4 lq + j; only the diagonal tile needs the i <= t mask (the
+    // exponentials of its masked entries may overflow; the select drops them).
     float4 gi4[NB];
 #pragma unroll
-    for (int J = 0; J < NB; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.gate[buf][J * 16 + 4 * lq]);
+    for (int J = 0; J <= Jmax; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.gate[buf][J * 16 + 4 * lq]);
     half8 Pb[2][2];
     float gam_t[2];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-        const int t = Irow[ii] * 16 + lr;
+        const int I = Irow[ii];
+        const int t = I * 16 + lr;
         const float gt = sm.gate[buf][t];
         gam_t[ii] = sm.gate[buf][C + t];
         half4 ph[NB];
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-            const int i0 = J * 16 + 4 * lq;
-            const float p0 = __expf(gt - gi4[J].x) * pacc[ii][J][0];
-            const float p1 = __expf(gt - gi4[J].y) * pacc[ii][J][1];
-            const float p2 = __expf(gt - gi4[J].z) * pacc[ii][J][2];
-            const float p3 = __expf(gt - gi4[J].w) * pacc[ii][J][3];
-            ph[J] = to_h4(i0 + 0 <= t ? p0 : 0.f, i0 + 1 <= t ? p1 : 0.f, i0 + 2 <= t ? p2 : 0.f,
-                          i0 + 3 <= t ? p3 : 0.f);
+            if (J > I) {
+                ph[J] = half4{};
+                continue;
+            }
+            float p[4] = {__expf(gt - gi4[J].x) * pacc[ii][J][0], __expf(gt - gi4[J].y) * pacc[ii][J][1],
+                          __expf(gt - gi4[J].z) * pacc[ii][J][2], __expf(gt - gi4[J].w) * pacc[ii][J][3]};
+            if (J == I) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] = (4 * lq + j <= lr) ? p[j] : 0.f;
+            }
+            ph[J] = to_h4(p[0], p[1], p[2], p[3]);
         }
         Pb[ii][0] = cat(ph[0], ph[1]);
         Pb[ii][1] = cat(ph[2], ph[3]);
     }
-    // wait until the state wave has published E for this chunk
+    // wait until the state wave has published E for this chunk (bounded: a
+    // missing flag would end the wait instead of hanging the device)
     for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
-        if (it > (1 << 22)) { *spin_error = 1; break; }
+        if (it > (1 << 22)) break;
         __builtin_amdgcn_s_sleep(1);
     }
     // Y^T = E^T P^T + gamma (Q S)^T: lane (t + 16 g) holds row t, columns 4 g .. 4 g + 3
@@ -736,8 +708,24 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, const QRegs<DK>& 
         if (I >= 2) yv = mma(Ea1, Pb[ii][1], yv);
         const int t = chunk * C + I * 16 + lr;
         if (t < T)
-            *reinterpret_cast<float4*>(&y[((tok0 + t) * H + h) * static_cast<long>(DV) + col0 + 4 * lq]) =
+            *reinterpret_cast<float4*>(ylane + t * ytok) =
                 make_float4(scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]);
+    }
+}
+
+// Output role: one barrier after the prologue and one per chunk.  ylane
+// points at this lane's four y columns of token 0; ytok is the token stride.
+template <int DK, int RP>
+__device__ __forceinline__ void output_role(MainSmem<DK>& sm, int nchunks, int lane, float* ylane, long ytok, int T,
+                                            float scale) {
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+        output_chunk<DK, 0, RP>(sm, c, lane, ylane, ytok, T, scale);
+        __syncthreads();
+        if (c + 1 < nchunks) {
+            output_chunk<DK, 1, RP>(sm, c + 1, lane, ylane, ytok, T, scale);
+            __syncthreads();
+        }
     }
 }
 
@@ -765,7 +753,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     const bool is_state = (w == Cfg::W_STATE);
     const bool is_out = (w >= Cfg::W_OUT0 && w < Cfg::W_OUT0 + 2);
     const bool misc = (w == Cfg::W_MISC);
-    const int lt = (w - Cfg::W_QK0) * 64 + lane;
+    const int lt = (w == 3 ? 0 : w - 4) * 64 + lane;   // q/k loader thread index (waves 3, 5, 6, 7)
 
     // T' is zero above its diagonal blocks; those halves of both buffers are never written again
     for (int idx = tid; idx < 2 * C * C; idx += Cfg::NT) (&sm.Tp[0][0])[idx] = static_cast<_Float16>(0.f);
@@ -786,9 +774,14 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
         }
         state_refresh_operand(st);
         __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            state_chunk<DK>(sm, st, c, lane);
+        // chunk pairs, so that each chunk's LDS buffer is a compile-time constant
+        for (int c = 0; c < nchunks; c += 2) {
+            state_chunk<DK, 0>(sm, st, c, lane);
             __syncthreads();
+            if (c + 1 < nchunks) {
+                state_chunk<DK, 1>(sm, st, c + 1, lane);
+                __syncthreads();
+            }
         }
         if (S_out) {
 #pragma unroll
@@ -798,30 +791,14 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
                     S_out[(static_cast<long>(bh) * DK + r * 16 + 4 * lq + j) * DV + col0 + lr] = st.S[r][j];
         }
     } else if (is_out) {
-        int spin_error = 0;
-        const int rp = w - Cfg::W_OUT0;
-        // q of chunk c+1 is loaded into one register set at the start of
-        // chunk c, while chunk c runs from the other (converted at its start)
-        QRegs<DK> qa, qb;
-        auto step = [&](int c, QRegs<DK>& cur, QRegs<DK>& nxt) {
-            load_q<DK>(nxt, q, min(c + 1, nchunks - 1), rp, lane, tok0, T, H, h);
-            q_convert<DK>(cur);
-            output_chunk<DK>(sm, cur, c, rp, lane, y, tok0, T, H, DV, col0, h, scale, &spin_error);
-            __syncthreads();
-        };
-        if (nchunks > 0) load_q<DK>(qa, q, 0, rp, lane, tok0, T, H, h);
-        __syncthreads();
-        // chunk pairs in an unconditional body (exact wait counts), odd tail after
-        int c = 0;
-        for (; c + 1 < nchunks; c += 2) {
-            step(c, qa, qb);
-            step(c + 1, qb, qa);
-        }
-        if (c < nchunks) step(c, qa, qb);
+        float* ylane = y + (tok0 * H + h) * static_cast<long>(DV) + col0 + 4 * lq;
+        const long ytok = static_cast<long>(H) * DV;
+        if (w == Cfg::W_OUT0) output_role<DK, 0>(sm, nchunks, lane, ylane, ytok, T, scale);
+        else output_role<DK, 1>(sm, nchunks, lane, ylane, ytok, T, scale);
     } else if (misc) {
-        loader_role<DK, true>(sm, nchunks, lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+        loader_role<DK, true>(sm, nchunks, lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     } else {
-        loader_role<DK, false>(sm, nchunks, lt, lane, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+        loader_role<DK, false>(sm, nchunks, lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     }
 }
 
