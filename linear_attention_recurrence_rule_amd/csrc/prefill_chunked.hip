@@ -309,7 +309,7 @@ struct MainCfg {
 };
 
 template <int DK>
-struct MainSmem {
+struct alignas(16) MainSmem {
     using Cfg = MainCfg<DK>;
     _Float16 K[2][C * DK];
     _Float16 Q[2][C * DK];
@@ -380,6 +380,8 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt,
 // last row and need no zeroing: there beta = 0 and alpha = 1 (set by
 // prep_kernel), so T' has zero rows and columns for them and they reach
 // neither E nor the state, and their y rows are never stored.
+// The empty asm pins every converted piece to this point: without it the
+// compiler sinks the conversion past the flag wait that precedes the stores.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     using Cfg = MainCfg<DK>;
@@ -388,7 +390,14 @@ __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     for (int i = 0; i < N; ++i) {
         const half8 hv = bf16x8_to_h8(pf.a[i]);
         pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
+        asm volatile("" : "+v"(pf.a[i].x), "+v"(pf.a[i].y), "+v"(pf.a[i].z), "+v"(pf.a[i].w));
     }
+}
+
+// 16-byte LDS store (half8 carries the 16-byte alignment that the uint4 type
+// lacks, so this is one ds_write_b128 rather than two 8-byte writes).
+__device__ __forceinline__ void st16(void* dst, const uint4& v) {
+    *reinterpret_cast<half8*>(dst) = *reinterpret_cast<const half8*>(&v);
 }
 
 template <int DK, bool MISC, int buf>
@@ -400,8 +409,8 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
             const int idx = lt + i * Cfg::LQK;
             if (idx < 64 * Cfg::QC) {
                 const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
-                *reinterpret_cast<uint4*>(&sm.K[buf][swz<DK>(t, cq * 8)]) = pf.a[i];
-                *reinterpret_cast<uint4*>(&sm.Q[buf][swz<DK>(t, cq * 8)]) = pf.a[Cfg::NQ + i];
+                st16(&sm.K[buf][swz<DK>(t, cq * 8)], pf.a[i]);
+                st16(&sm.Q[buf][swz<DK>(t, cq * 8)], pf.a[Cfg::NQ + i]);
             }
         }
     } else {
@@ -409,7 +418,7 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
         for (int i = 0; i < Cfg::NVI; ++i) {
             const int idx = lane + i * 64;
             const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
-            *reinterpret_cast<uint4*>(&sm.V[buf][t * Cfg::SV + cv * 8]) = pf.a[i];
+            st16(&sm.V[buf][t * Cfg::SV + cv * 8], pf.a[i]);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NTI; ++i) {
@@ -418,21 +427,33 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
             // lower block index -> (I, J): (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
             const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
             const int J = blk - I * (I + 1) / 2;
-            *reinterpret_cast<uint4*>(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)]) = pf.a[Cfg::NVI + i];
+            st16(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)], pf.a[Cfg::NVI + i]);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NGI; ++i) {
             const int idx = lane + i * 64;
             if (idx < NGATE / 4)
-                *reinterpret_cast<uint4*>(&sm.gate[buf][4 * idx]) = pf.a[Cfg::NVI + Cfg::NTI + i];
+                st16(&sm.gate[buf][4 * idx], pf.a[Cfg::NVI + Cfg::NTI + i]);
         }
     }
 }
 
+// Wait until the state wave has published E of `chunk` (it has then issued
+// all of its LDS reads of that chunk).  Bounded: a missing flag ends the wait
+// instead of hanging the device.
+template <int DK>
+__device__ __forceinline__ void wait_published(MainSmem<DK>& sm, int chunk) {
+    for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
+        if (it > (1 << 22)) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 // Loader role: during chunk c the loads of chunk c+2 are issued into one
-// register set, then chunk c+1 (loaded during chunk c-1, in the other set) is
-// converted and stored to the other LDS buffer.  One barrier after the
-// prologue and one per chunk, as in the other roles.
+// register set and chunk c+1 (loaded during chunk c-1, in the other set) is
+// converted; its LDS stores wait until the state wave has read what it needs
+// of chunk c, so that they do not queue in front of those reads.  One barrier
+// after the prologue and one per chunk, as in the other roles.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* q,
                                             const uint16_t* k,
@@ -443,14 +464,12 @@ __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int l
         loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     };
     // chunk c goes to LDS buffer c & 1 (a compile-time constant at each call)
-    auto put = [&](Prefetch<DK>& pf, auto buf) {
-        loader_convert<DK, MISC>(pf);
-        loader_store<DK, MISC, decltype(buf)::value>(pf, sm, lt, lane);
-    };
+    auto put = [&](Prefetch<DK>& pf, auto buf) { loader_store<DK, MISC, decltype(buf)::value>(pf, sm, lt, lane); };
     const std::integral_constant<int, 0> even{};
     const std::integral_constant<int, 1> odd{};
     if (nchunks > 0) {
         ld(pa, 0);
+        loader_convert<DK, MISC>(pa);
         put(pa, even);
         ld(pa, 1);
     }
@@ -462,9 +481,13 @@ __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int l
     int c = 0;
     for (; c + 1 < nchunks; c += 2) {
         ld(pb, c + 2);
+        loader_convert<DK, MISC>(pa);
+        wait_published(sm, c);
         put(pa, odd);    // chunk c + 1
         __syncthreads();
         ld(pa, c + 3);
+        loader_convert<DK, MISC>(pb);
+        wait_published(sm, c + 1);
         put(pb, even);   // chunk c + 2
         __syncthreads();
     }
@@ -538,16 +561,16 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
         kt0[r][0] = ld_split_tr<DK>(Kb, r * 16, 0, lane);
         kt0[r][1] = ld_split_tr<DK>(Kb, r * 16, 32, lane);
     }
-    float4 gm[NB];
+    float4v gm[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4*>(&sm.gate[buf][C + I * 16 + 4 * lq]);
+    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][C + I * 16 + 4 * lq]);
     __builtin_amdgcn_sched_barrier(0);
     // R = V - gamma K S, as the split-K B operand of T' R
     half4 rh[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I)
-        rh[I] = to_h4(static_cast<float>(vv[I][0]) - gm[I].x * ks[I][0], static_cast<float>(vv[I][1]) - gm[I].y * ks[I][1],
-                      static_cast<float>(vv[I][2]) - gm[I].z * ks[I][2], static_cast<float>(vv[I][3]) - gm[I].w * ks[I][3]);
+        rh[I] = to_h4(static_cast<float>(vv[I][0]) - gm[I][0] * ks[I][0], static_cast<float>(vv[I][1]) - gm[I][1] * ks[I][1],
+                      static_cast<float>(vv[I][2]) - gm[I][2] * ks[I][2], static_cast<float>(vv[I][3]) - gm[I][3] * ks[I][3]);
     const half8 Rb0 = cat(rh[0], rh[1]), Rb1 = cat(rh[2], rh[3]);
     // E = T' R (T' is zero above the diagonal blocks)
     float4v e[NB];
@@ -566,16 +589,16 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
             kt1[r][1] = ld_split_tr<DK>(Kb, (NH + r) * 16, 32, lane);
         }
     }
-    float4 dc[NB];
+    float4v dc[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4*>(&sm.gate[buf][2 * C + I * 16 + 4 * lq]);
+    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][2 * C + I * 16 + 4 * lq]);
     const float gl = sm.gate[buf][C + C - 1];
     __builtin_amdgcn_sched_barrier(0);
     // D E as the B operand of K^T (D E)
     half4 eh[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I)
-        eh[I] = to_h4(dc[I].x * e[I][0], dc[I].y * e[I][1], dc[I].z * e[I][2], dc[I].w * e[I][3]);
+        eh[I] = to_h4(dc[I][0] * e[I][0], dc[I][1] * e[I][1], dc[I][2] * e[I][2], dc[I][3] * e[I][3]);
     const half8 Eb0 = cat(eh[0], eh[1]), Eb1 = cat(eh[2], eh[3]);
     // S = gamma_last S + K^T D E
     float4v u[NST];
@@ -663,9 +686,9 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
     // P = Gamma o (Q K^T) on the lower tiles, lane row t = 16 I + lr, columns
     // i = 16 J + 4 lq + j; only the diagonal tile needs the i <= t mask (the
     // exponentials of its masked entries may overflow; the select drops them).
-    float4 gi4[NB];
+    float4v gi4[NB];
 #pragma unroll
-    for (int J = 0; J <= Jmax; ++J) gi4[J] = *reinterpret_cast<const float4*>(&sm.gate[buf][J * 16 + 4 * lq]);
+    for (int J = 0; J <= Jmax; ++J) gi4[J] = *reinterpret_cast<const float4v*>(&sm.gate[buf][J * 16 + 4 * lq]);
     half8 Pb[2][2];
     float gam_t[2];
 #pragma unroll
@@ -681,8 +704,8 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
                 ph[J] = half4{};
                 continue;
             }
-            float p[4] = {__expf(gt - gi4[J].x) * pacc[ii][J][0], __expf(gt - gi4[J].y) * pacc[ii][J][1],
-                          __expf(gt - gi4[J].z) * pacc[ii][J][2], __expf(gt - gi4[J].w) * pacc[ii][J][3]};
+            float p[4] = {__expf(gt - gi4[J][0]) * pacc[ii][J][0], __expf(gt - gi4[J][1]) * pacc[ii][J][1],
+                          __expf(gt - gi4[J][2]) * pacc[ii][J][2], __expf(gt - gi4[J][3]) * pacc[ii][J][3]};
             if (J == I) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) p[j] = (4 * lq + j <= lr) ? p[j] : 0.f;
@@ -692,12 +715,7 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
         Pb[ii][0] = cat(ph[0], ph[1]);
         Pb[ii][1] = cat(ph[2], ph[3]);
     }
-    // wait until the state wave has published E for this chunk (bounded: a
-    // missing flag would end the wait instead of hanging the device)
-    for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
-        if (it > (1 << 22)) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
+    wait_published(sm, chunk);
     // Y^T = E^T P^T + gamma (Q S)^T: lane (t + 16 g) holds row t, columns 4 g .. 4 g + 3
     const half8 Ea0 = ld_split<C>(sm.ET, lr, 0, lq), Ea1 = ld_split<C>(sm.ET, lr, 32, lq);
 #pragma unroll
