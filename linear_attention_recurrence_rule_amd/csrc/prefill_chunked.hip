@@ -380,8 +380,8 @@ __device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt,
 // last row and need no zeroing: there beta = 0 and alpha = 1 (set by
 // prep_kernel), so T' has zero rows and columns for them and they reach
 // neither E nor the state, and their y rows are never stored.
-// The empty asm pins every converted piece to this point: without it the
-// compiler sinks the conversion past the flag wait that precedes the stores.
+// The empty asm pins every converted piece to this point, so that the
+// conversion is not sunk next to the stores.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
     using Cfg = MainCfg<DK>;
@@ -438,9 +438,8 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
     }
 }
 
-// Wait until the state wave has published E of `chunk` (it has then issued
-// all of its LDS reads of that chunk).  Bounded: a missing flag ends the wait
-// instead of hanging the device.
+// Wait until the state wave has published E of `chunk`.  Bounded: a missing
+// flag ends the wait instead of hanging the device.
 template <int DK>
 __device__ __forceinline__ void wait_published(MainSmem<DK>& sm, int chunk) {
     for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
@@ -451,9 +450,8 @@ __device__ __forceinline__ void wait_published(MainSmem<DK>& sm, int chunk) {
 
 // Loader role: during chunk c the loads of chunk c+2 are issued into one
 // register set and chunk c+1 (loaded during chunk c-1, in the other set) is
-// converted; its LDS stores wait until the state wave has read what it needs
-// of chunk c, so that they do not queue in front of those reads.  One barrier
-// after the prologue and one per chunk, as in the other roles.
+// converted and stored to the other LDS buffer.  One barrier after the
+// prologue and one per chunk, as in the other roles.
 template <int DK, bool MISC>
 __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* q,
                                             const uint16_t* k,
@@ -482,12 +480,10 @@ __device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int l
     for (; c + 1 < nchunks; c += 2) {
         ld(pb, c + 2);
         loader_convert<DK, MISC>(pa);
-        wait_published(sm, c);
         put(pa, odd);    // chunk c + 1
         __syncthreads();
         ld(pa, c + 3);
         loader_convert<DK, MISC>(pb);
-        wait_published(sm, c + 1);
         put(pb, even);   // chunk c + 2
         __syncthreads();
     }
@@ -580,6 +576,10 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
         if (I >= 2) e[I] = mma(ta[I][1], Rb1, e[I]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // publish E for the output waves before the state update
+#pragma unroll
+    for (int I = 0; I < NB; ++I) *reinterpret_cast<half4*>(&sm.ET[swz<C>(lr, I * 16 + 4 * lq)]) = to_h4(e[I]);
+    __hip_atomic_store(&sm.flagE, chunk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     // second half of K^T and the decay-to-chunk-end factors, read while T' R runs
     half8 kt1[NH][2];
 #pragma unroll
@@ -614,10 +614,6 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
             u[NH + r] = mma(kt1[r][1], Eb1, u[NH + r]);
         }
     }
-    // publish E for the output waves while the update runs
-#pragma unroll
-    for (int I = 0; I < NB; ++I) *reinterpret_cast<half4*>(&sm.ET[swz<C>(lr, I * 16 + 4 * lq)]) = to_h4(e[I]);
-    __hip_atomic_store(&sm.flagE, chunk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     _Float16* STn = sm.ST[buf ^ 1];
 #pragma unroll
     for (int r = 0; r < NST; ++r) {
