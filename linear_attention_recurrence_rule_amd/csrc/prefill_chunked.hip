@@ -129,7 +129,7 @@ struct PrepCfg {
 };
 
 template <int DK>
-struct PrepSmem {
+struct alignas(16) PrepSmem {
     using Cfg = PrepCfg<DK>;
     _Float16 K[C * Cfg::LDQ];
     _Float16 A16[C * Cfg::LDC];
@@ -192,6 +192,13 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
 // Workspace layout: for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
 // 16x16 blocks of T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each
 // row-major fp16, then the float32 gates g[C], gamma[C], d[C].
+//
+// One workgroup handles kPrepChunks consecutive chunks of one head; the k
+// rows, alpha and beta of the next chunk are loaded into registers while the
+// current chunk is processed.  Rows past the end of the sequence load the last
+// row (their beta is 0, so A has zero rows there and they never matter).
+constexpr int kPrepChunks = 4;
+
 template <int DK>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
@@ -200,84 +207,109 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     using Cfg = PrepCfg<DK>;
     using M = Mma<_Float16>;
     constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDA = Cfg::LDA;
+    constexpr int NKP = (C * DK / 8 + 255) / 256;   // 16-byte k pieces per thread
     __shared__ PrepSmem<DK> sm;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int lr = l & 15, lq = l >> 4;
-    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int bh = blockIdx.y;
     const int b = bh / H, h = bh % H;
-    const int t0 = chunk * C;
     const long tok0 = static_cast<long>(b) * T;
+    const int c_begin = blockIdx.x * kPrepChunks;
+    const int c_end = min(c_begin + kPrepChunks, nchunks);
 
-    // k rows (bf16 -> fp16), zero past the end of the sequence
-    for (int idx = tid; idx < C * DK / 8; idx += 256) {
-        const int row = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (t0 + row < T) raw = *reinterpret_cast<const uint4*>(k + ((tok0 + t0 + row) * H + h) * DK + c8);
-        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-        half8 hv;
+    uint4 kr[NKP];
+    float ar = 1.f, br = 0.f;
+    auto load = [&](int chunk) {
+        const int t0 = chunk * C;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            hv[2 * i] = static_cast<_Float16>(__uint_as_float(wds[i] << 16));
-            hv[2 * i + 1] = static_cast<_Float16>(__uint_as_float(wds[i] & 0xffff0000u));
+        for (int i = 0; i < NKP; ++i) {
+            const int idx = min(tid + i * 256, C * DK / 8 - 1);
+            const int row = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            kr[i] = *reinterpret_cast<const uint4*>(k + ((tok0 + min(t0 + row, T - 1)) * H + h) * DK + c8);
         }
-        *reinterpret_cast<half8*>(&sm.K[row * LDQ + c8]) = hv;
-    }
-    if (w == 0) {
-        float a = 1.f, be = 0.f;
-        if (t0 + l < T) {
-            const long off = (tok0 + t0 + l) * H + h;
-            a = alpha[off];
-            be = beta[off];
+        if (w == 0) {
+            const long off = (tok0 + min(t0 + l, T - 1)) * H + h;
+            ar = alpha[off];
+            br = beta[off];
         }
-        float lg = fmaxf(logf(a), kLogDecayFloor);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float t = __shfl_up(lg, off, 64);
-            if (l >= off) lg += t;
-        }
-        sm.g[l] = lg;
-        sm.beta[l] = be;
-        // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
-        const float glast = __shfl(lg, C - 1, 64);
-        float* gate = reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
-        gate[l] = lg;
-        gate[C + l] = expf(lg);
-        gate[2 * C + l] = expf(glast - lg);
-    }
-    __syncthreads();
+    };
+    if (c_begin < c_end) load(c_begin);
 
-    // A = strictLower(diag(beta) (Gamma o K K^T)), tiles computed transposed
-    // (K_J K_I^T) so that each lane holds 4 consecutive columns of one row.
-    for (int tile = w; tile < NTB; tile += Cfg::NW) {
-        int u = tile, I = 0;
-        while (u > I) { u -= I + 1; ++I; }
-        const int J = u;
-        const float4v acc = M::range(sm.K + J * 16 * LDQ, LDQ, sm.K + I * 16 * LDQ, LDQ, 0, DK,
-                                     float4v{0.f, 0.f, 0.f, 0.f});
-        const int t = I * 16 + lr, i0 = J * 16 + 4 * lq;
-        const float gt = sm.g[t], bt = sm.beta[t];
-        float a[4];
+    for (int chunk = c_begin; chunk < c_end; ++chunk) {
+        const int t0 = chunk * C;
+        // k rows (bf16 -> fp16) into LDS
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = (i0 + j < t) ? bt * expf(gt - sm.g[i0 + j]) * acc[j] : 0.f;
-        *reinterpret_cast<float4*>(&sm.Af[t * LDA + i0]) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<half4*>(&sm.A16[t * LDC + i0]) = to_h4(a[0], a[1], a[2], a[3]);
-    }
-    __syncthreads();
-    build_T<Cfg>(sm, w, l);
+        for (int i = 0; i < NKP; ++i) {
+            const int idx = tid + i * 256;
+            if (idx < C * DK / 8) {
+                const int row = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+                const uint32_t wds[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+                half8 hv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hv[2 * j] = static_cast<_Float16>(__uint_as_float(wds[j] << 16));
+                    hv[2 * j + 1] = static_cast<_Float16>(__uint_as_float(wds[j] & 0xffff0000u));
+                }
+                *reinterpret_cast<half8*>(&sm.K[row * LDQ + c8]) = hv;
+            }
+        }
+        if (w == 0) {
+            // past the end: identity steps (alpha = 1, beta = 0)
+            const float a = (t0 + l < T) ? ar : 1.f, be = (t0 + l < T) ? br : 0.f;
+            float lg = fmaxf(logf(a), kLogDecayFloor);
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float t = __shfl_up(lg, off, 64);
+                if (l >= off) lg += t;
+            }
+            sm.g[l] = lg;
+            sm.beta[l] = be;
+            // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
+            const float glast = __shfl(lg, C - 1, 64);
+            float* gate =
+                reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
+            gate[l] = lg;
+            gate[C + l] = expf(lg);
+            gate[2 * C + l] = expf(glast - lg);
+        }
+        __syncthreads();
+        // the next chunk's loads fly while this one is processed
+        if (chunk + 1 < c_end) load(chunk + 1);
 
-    // T' = T diag(beta), lower blocks, 8 halfs per item
-    _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK;
-    for (int idx = tid; idx < NTB * TBLK / 8; idx += 256) {
-        const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-        int u = blk, I = 0;
-        while (u > I) { u -= I + 1; ++I; }
-        const int J = u;
-        const half8 tv = *reinterpret_cast<const half8*>(&sm.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
-        half8 o;
+        // A = strictLower(diag(beta) (Gamma o K K^T)), tiles computed transposed
+        // (K_J K_I^T) so that each lane holds 4 consecutive columns of one row.
+        for (int tile = w; tile < NTB; tile += Cfg::NW) {
+            int u = tile, I = 0;
+            while (u > I) { u -= I + 1; ++I; }
+            const int J = u;
+            const float4v acc = M::range(sm.K + J * 16 * LDQ, LDQ, sm.K + I * 16 * LDQ, LDQ, 0, DK,
+                                         float4v{0.f, 0.f, 0.f, 0.f});
+            const int t = I * 16 + lr, i0 = J * 16 + 4 * lq;
+            const float gt = sm.g[t], bt = sm.beta[t];
+            float a[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o[e] = static_cast<_Float16>(static_cast<float>(tv[e]) * sm.beta[J * 16 + 8 * hh + e]);
-        *reinterpret_cast<half8*>(dst + blk * TBLK + r * 16 + 8 * hh) = o;
+            for (int j = 0; j < 4; ++j) a[j] = (i0 + j < t) ? bt * expf(gt - sm.g[i0 + j]) * acc[j] : 0.f;
+            *reinterpret_cast<float4v*>(&sm.Af[t * LDA + i0]) = float4v{a[0], a[1], a[2], a[3]};
+            *reinterpret_cast<half4*>(&sm.A16[t * LDC + i0]) = to_h4(a[0], a[1], a[2], a[3]);
+        }
+        __syncthreads();
+        build_T<Cfg>(sm, w, l);
+
+        // T' = T diag(beta), lower blocks, 8 halfs per item
+        _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK;
+        for (int idx = tid; idx < NTB * TBLK / 8; idx += 256) {
+            const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
+            int u = blk, I = 0;
+            while (u > I) { u -= I + 1; ++I; }
+            const int J = u;
+            const half8 tv = *reinterpret_cast<const half8*>(&sm.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
+            half8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] = static_cast<_Float16>(static_cast<float>(tv[e]) * sm.beta[J * 16 + 8 * hh + e]);
+            *reinterpret_cast<half8*>(dst + blk * TBLK + r * 16 + 8 * hh) = o;
+        }
+        __syncthreads();   // LDS is reused by the next chunk
     }
 }
 
@@ -822,7 +854,8 @@ static hipError_t launch_t(const PrefillArgs& a) {
     const int nchunks = (a.T + C - 1) / C;
     _Float16* ws = static_cast<_Float16*>(a.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK>), dim3(nchunks, a.B * a.H), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((prep_kernel<DK>), dim3((nchunks + kPrepChunks - 1) / kPrepChunks, a.B * a.H), dim3(256), 0,
+                           a.stream,
                            static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, a.T, a.H, nchunks);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
