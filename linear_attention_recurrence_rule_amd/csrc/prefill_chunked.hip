@@ -122,31 +122,38 @@ template <int DK>
 struct PrepCfg {
     static constexpr int LDQ = DK + 8;   // padded rows (fp16)
     static constexpr int LDC = C + 8;
-    static constexpr int LDA = C + 4;    // float rows, 16-byte aligned
+    static constexpr int LDA = 16 + 4;   // float rows of a diagonal block, 16-byte aligned
     static constexpr int LDX = 16 + 8;
     static constexpr int NB = chunked::NB;
     static constexpr int NW = 4;
 };
 
+// K is dead once A is formed, so T (row-major and transposed) reuses its
+// space; the whole set fits four workgroups in a CU's LDS.
 template <int DK>
 struct alignas(16) PrepSmem {
     using Cfg = PrepCfg<DK>;
-    _Float16 K[C * Cfg::LDQ];
+    struct TPair {
+        _Float16 Tm[C * Cfg::LDC];
+        _Float16 TT[C * Cfg::LDC];
+    };
+    union {
+        _Float16 K[C * Cfg::LDQ];
+        TPair tp;
+    };
     _Float16 A16[C * Cfg::LDC];
-    _Float16 Tm[C * Cfg::LDC];
-    _Float16 TT[C * Cfg::LDC];
     _Float16 X[Cfg::NW][16 * Cfg::LDX];
-    float Af[C * Cfg::LDA];
+    float Ad[NB][16 * Cfg::LDA];   // the diagonal 16x16 blocks of A in float32
     float g[C], beta[C];
 };
 
 // T = (I + A)^-1 for the unit lower-triangular chunk system, from A in
-// sm.Af (float32) and sm.A16 (its fp16 copy).  The 16x16 diagonal blocks are
+// sm.A16 (fp16) and its diagonal blocks in sm.Ad (float32).  The 16x16 diagonal blocks are
 // inverted by forward substitution in float32 (one block per wave, one column
 // per lane); then one block sub-diagonal per step,
 //     T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ,
-// whose terms all lie on earlier sub-diagonals.  Writes sm.Tm (row-major) and
-// sm.TT (transposed).  Contains workgroup barriers: call from all 4 waves.
+// whose terms all lie on earlier sub-diagonals.  Writes sm.tp.Tm (row-major)
+// and sm.tp.TT (transposed).  Contains workgroup barriers: call from all 4 waves.
 template <class Cfg, class Smem>
 __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
     using M = Mma<_Float16>;
@@ -159,13 +166,13 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
         for (int t = 0; t < 16; ++t) {
             float acc = (t == l) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < t; ++i) acc -= sm.Af[(base + t) * LDA + base + i] * x[i];
+            for (int i = 0; i < t; ++i) acc -= sm.Ad[w][t * LDA + i] * x[i];
             x[t] = acc;
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            sm.Tm[(base + t) * LDC + base + l] = static_cast<_Float16>(x[t]);
-            sm.TT[(base + l) * LDC + base + t] = static_cast<_Float16>(x[t]);
+            sm.tp.Tm[(base + t) * LDC + base + l] = static_cast<_Float16>(x[t]);
+            sm.tp.TT[(base + l) * LDC + base + t] = static_cast<_Float16>(x[t]);
         }
     }
     __syncthreads();
@@ -173,16 +180,16 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
     for (int lev = 1; lev < NB; ++lev) {
         for (int J = w; J + lev < NB; J += NW) {
             const int I = J + lev;
-            const float4v x = M::range(sm.A16 + I * 16 * LDC, LDC, sm.TT + J * 16 * LDC, LDC, J * 16, I * 16,
+            const float4v x = M::range(sm.A16 + I * 16 * LDC, LDC, sm.tp.TT + J * 16 * LDC, LDC, J * 16, I * 16,
                                        float4v{0.f, 0.f, 0.f, 0.f});
             _Float16* Xw = sm.X[w];
             *reinterpret_cast<half4*>(&Xw[lr * LDX + 4 * lq]) = to_h4(x);   // X transposed
-            const float4v t = M::range(sm.Tm + I * 16 * LDC + I * 16, LDC, Xw, LDX, 0, 16,
+            const float4v t = M::range(sm.tp.Tm + I * 16 * LDC + I * 16, LDC, Xw, LDX, 0, 16,
                                        float4v{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                sm.Tm[(I * 16 + 4 * lq + j) * LDC + J * 16 + lr] = static_cast<_Float16>(-t[j]);
-            *reinterpret_cast<half4*>(&sm.TT[(J * 16 + lr) * LDC + I * 16 + 4 * lq]) =
+                sm.tp.Tm[(I * 16 + 4 * lq + j) * LDC + J * 16 + lr] = static_cast<_Float16>(-t[j]);
+            *reinterpret_cast<half4*>(&sm.tp.TT[(J * 16 + lr) * LDC + I * 16 + 4 * lq]) =
                 to_h4(-t[0], -t[1], -t[2], -t[3]);
         }
         __syncthreads();
@@ -200,7 +207,7 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
 constexpr int kPrepChunks = 4;
 
 template <int DK>
-__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 4) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
                                                    _Float16* __restrict__ ws, int T, int H, int nchunks) {
@@ -288,8 +295,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
             const float gt = sm.g[t], bt = sm.beta[t];
             float a[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a[j] = (i0 + j < t) ? bt * expf(gt - sm.g[i0 + j]) * acc[j] : 0.f;
-            *reinterpret_cast<float4v*>(&sm.Af[t * LDA + i0]) = float4v{a[0], a[1], a[2], a[3]};
+            for (int j = 0; j < 4; ++j) a[j] = (i0 + j < t) ? bt * __expf(gt - sm.g[i0 + j]) * acc[j] : 0.f;
+            if (I == J) *reinterpret_cast<float4v*>(&sm.Ad[I][lr * LDA + 4 * lq]) = float4v{a[0], a[1], a[2], a[3]};
             *reinterpret_cast<half4*>(&sm.A16[t * LDC + i0]) = to_h4(a[0], a[1], a[2], a[3]);
         }
         __syncthreads();
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
             int u = blk, I = 0;
             while (u > I) { u -= I + 1; ++I; }
             const int J = u;
-            const half8 tv = *reinterpret_cast<const half8*>(&sm.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
+            const half8 tv = *reinterpret_cast<const half8*>(&sm.tp.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
             half8 o;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
