@@ -54,6 +54,10 @@ constexpr int WS_CHUNK = NTB * TBLK + 2 * NGATE;   // workspace halfs per (head,
 constexpr float kLogDecayFloor = -30.0f; // exp(-30) ~ 9e-14: alpha = 0 stays finite
 constexpr int kXcds = 8;
 
+// Row I of lower block number b in the order (0,0),(1,0),(1,1),(2,0),(2,1),
+// (2,2),(3,0),...; its column is b - I (I + 1) / 2.
+__device__ __forceinline__ int lower_block_row(int b) { return b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0; }
+
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4v mma(half8 a, half8 b, float4v c) {
@@ -176,9 +180,11 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
         }
     }
     __syncthreads();
+    static_assert(NW >= NB - 1, "one block of each sub-diagonal per wave");
 #pragma unroll
     for (int lev = 1; lev < NB; ++lev) {
-        for (int J = w; J + lev < NB; J += NW) {
+        const int J = w;
+        if (J + lev < NB) {
             const int I = J + lev;
             const float4v x = M::range(sm.A16 + I * 16 * LDC, LDC, sm.tp.TT + J * 16 * LDC, LDC, J * 16, I * 16,
                                        float4v{0.f, 0.f, 0.f, 0.f});
@@ -207,7 +213,7 @@ __device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
 constexpr int kPrepChunks = 4;
 
 template <int DK>
-__global__ __launch_bounds__(256, 4) void prep_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
                                                    _Float16* __restrict__ ws, int T, int H, int nchunks) {
@@ -271,13 +277,6 @@ __global__ __launch_bounds__(256, 4) void prep_kernel(const uint16_t* __restrict
             }
             sm.g[l] = lg;
             sm.beta[l] = be;
-            // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
-            const float glast = __shfl(lg, C - 1, 64);
-            float* gate =
-                reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
-            gate[l] = lg;
-            gate[C + l] = expf(lg);
-            gate[2 * C + l] = expf(glast - lg);
         }
         __syncthreads();
         // the next chunk's loads fly while this one is processed
@@ -285,10 +284,13 @@ __global__ __launch_bounds__(256, 4) void prep_kernel(const uint16_t* __restrict
 
         // A = strictLower(diag(beta) (Gamma o K K^T)), tiles computed transposed
         // (K_J K_I^T) so that each lane holds 4 consecutive columns of one row.
-        for (int tile = w; tile < NTB; tile += Cfg::NW) {
-            int u = tile, I = 0;
-            while (u > I) { u -= I + 1; ++I; }
-            const int J = u;
+        // (Straight-line code: a loop header here would make the compiler wait
+        // for the next chunk's loads.)
+#pragma unroll
+        for (int it = 0; it < (NTB + Cfg::NW - 1) / Cfg::NW; ++it) {
+            const int tile = w + it * Cfg::NW;
+            if (tile >= NTB) break;
+            const int I = lower_block_row(tile), J = tile - I * (I + 1) / 2;
             const float4v acc = M::range(sm.K + J * 16 * LDQ, LDQ, sm.K + I * 16 * LDQ, LDQ, 0, DK,
                                          float4v{0.f, 0.f, 0.f, 0.f});
             const int t = I * 16 + lr, i0 = J * 16 + 4 * lq;
@@ -304,17 +306,28 @@ __global__ __launch_bounds__(256, 4) void prep_kernel(const uint16_t* __restrict
 
         // T' = T diag(beta), lower blocks, 8 halfs per item
         _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK;
-        for (int idx = tid; idx < NTB * TBLK / 8; idx += 256) {
+#pragma unroll
+        for (int it = 0; it < (NTB * TBLK / 8 + 255) / 256; ++it) {
+            const int idx = tid + it * 256;
+            if (idx >= NTB * TBLK / 8) break;
             const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-            int u = blk, I = 0;
-            while (u > I) { u -= I + 1; ++I; }
-            const int J = u;
+            const int I = lower_block_row(blk), J = blk - I * (I + 1) / 2;
             const half8 tv = *reinterpret_cast<const half8*>(&sm.tp.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
             half8 o;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 o[e] = static_cast<_Float16>(static_cast<float>(tv[e]) * sm.beta[J * 16 + 8 * hh + e]);
             *reinterpret_cast<half8*>(dst + blk * TBLK + r * 16 + 8 * hh) = o;
+        }
+        // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
+        // (stored after the next chunk's loads have been issued)
+        if (w == 0) {
+            const float lg = sm.g[l], glast = sm.g[C - 1];
+            float* gate =
+                reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
+            gate[l] = lg;
+            gate[C + l] = expf(lg);
+            gate[2 * C + l] = expf(glast - lg);
         }
         __syncthreads();   // LDS is reused by the next chunk
     }
@@ -463,9 +476,7 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
         for (int i = 0; i < Cfg::NTI; ++i) {
             const int idx = lane + i * 64;
             const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-            // lower block index -> (I, J): (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
-            const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
-            const int J = blk - I * (I + 1) / 2;
+            const int I = lower_block_row(blk), J = blk - I * (I + 1) / 2;
             st16(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)], pf.a[Cfg::NVI + i]);
         }
 #pragma unroll
