@@ -610,6 +610,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     float4v gm[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][C + I * 16 + 4 * lq]);
+    const float gl = sm.gate[buf][C + C - 1];
     __builtin_amdgcn_sched_barrier(0);
     // R = V - gamma K S, as the split-K B operand of T' R
     half4 rh[NB];
@@ -625,6 +626,9 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
         e[I] = mma(ta[I][0], Rb0, float4v{0.f, 0.f, 0.f, 0.f});
         if (I >= 2) e[I] = mma(ta[I][1], Rb1, e[I]);
     }
+    // gamma_last S, the accumulator input of the update (computed while T' R runs)
+#pragma unroll
+    for (int r = 0; r < NST; ++r) st.S[r] *= gl;
     __builtin_amdgcn_sched_barrier(0);
     // publish E for the output waves before the state update
 #pragma unroll
@@ -642,7 +646,6 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     float4v dc[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][2 * C + I * 16 + 4 * lq]);
-    const float gl = sm.gate[buf][C + C - 1];
     __builtin_amdgcn_sched_barrier(0);
     // D E as the B operand of K^T (D E)
     half4 eh[NB];
@@ -650,27 +653,22 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     for (int I = 0; I < NB; ++I)
         eh[I] = to_h4(dc[I][0] * e[I][0], dc[I][1] * e[I][1], dc[I][2] * e[I][2], dc[I][3] * e[I][3]);
     const half8 Eb0 = cat(eh[0], eh[1]), Eb1 = cat(eh[2], eh[3]);
-    // S = gamma_last S + K^T D E
-    float4v u[NST];
+    // S = gamma_last S + K^T D E, accumulated onto the scaled state
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
-        u[r] = mma(kt0[r][0], Eb0, float4v{0.f, 0.f, 0.f, 0.f});
-        u[r] = mma(kt0[r][1], Eb1, u[r]);
+        st.S[r] = mma(kt0[r][0], Eb0, st.S[r]);
+        st.S[r] = mma(kt0[r][1], Eb1, st.S[r]);
     }
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
         if (NH + r < NST) {
-            u[NH + r] = mma(kt1[r][0], Eb0, float4v{0.f, 0.f, 0.f, 0.f});
-            u[NH + r] = mma(kt1[r][1], Eb1, u[NH + r]);
+            st.S[NH + r] = mma(kt1[r][0], Eb0, st.S[NH + r]);
+            st.S[NH + r] = mma(kt1[r][1], Eb1, st.S[NH + r]);
         }
     }
     _Float16* STn = sm.ST[buf ^ 1];
 #pragma unroll
-    for (int r = 0; r < NST; ++r) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st.S[r][j] = gl * st.S[r][j] + u[r][j];
-        *reinterpret_cast<half4*>(&STn[swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
-    }
+    for (int r = 0; r < NST; ++r) *reinterpret_cast<half4*>(&STn[swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
     state_refresh_operand(st);
 }
 
