@@ -769,9 +769,11 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
         yv = mma(Ea0, Pb[ii][0], yv);
         if (I >= 2) yv = mma(Ea1, Pb[ii][1], yv);
         const int t = chunk * C + I * 16 + lr;
-        if (t < T)   // streaming store: y is not read again by this kernel
-            __builtin_nontemporal_store(float4v{scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]},
-                                        reinterpret_cast<float4v*>(ylane + t * ytok));
+        // a plain store: the slices of a head write 64-byte pieces of each y
+        // row, which merge in L2 (streaming stores measured 28% more HBM writes)
+        if (t < T)
+            *reinterpret_cast<float4v*>(ylane + t * ytok) =
+                float4v{scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]};
     }
 }
 
