@@ -9,7 +9,9 @@ Every function is the plain definition written out, token by token, in
 float64, following "On the Design of Qwen3.8-Next Architecture" as summarised
 on the slinene ai-papers-daily page (Module A, Gated DeltaNet: the four-line
 delta form of the recurrence and the output parameterisation) and on the
-paper.rainbus.top digest (method step (1)).
+paper.rainbus.top digest (method step (1)); the front end (short causal
+convolutions, SiLU, L2 normalisation and the gates) follows the
+parameterisation block of the same Module A.
 """
 
 from .gdn_ref import (  # noqa: F401
@@ -18,3 +20,4 @@ from .gdn_ref import (  # noqa: F401
     gated_rmsnorm,
     rel_err,
 )
+from .frontend_ref import gdn_frontend, short_conv, silu, l2norm  # noqa: F401
