@@ -129,6 +129,41 @@ gdn_status gdn_gated_rmsnorm(const float* y, const void* z, const float* weight,
                              float eps, void* out, long rows, int d_v,
                              gdn_dtype io_dtype, void* hip_stream);
 
+/*
+ * Front end of the mixer (slinene page, Module A, parameterisation block; the
+ * mixer figure of the rainbus digest): the recurrence inputs from the
+ * projected streams, per (b, t, h):
+ *
+ *     q = L2Norm(SiLU(ShortConv(q_proj)))       k = L2Norm(SiLU(ShortConv(k_proj)))
+ *     v = SiLU(ShortConv(v_proj))
+ *     beta = sigmoid(b_logit)    alpha = exp(-exp(A[h]) * softplus(a_logit + b_alpha[h]))
+ *
+ * ShortConv is a causal depthwise convolution over time with one filter of
+ * conv_width taps per (head, channel) and no bias:
+ *     conv_t[c] = sum_{j < W} conv[h][c][j] * x_{t-W+1+j}[c]
+ * L2Norm(x) = x / sqrt(sum_c x[c]^2 + norm_eps).  SiLU(x) = x * sigmoid(x).
+ *
+ *   q_proj, k_proj     [B, T, H, d_k]  io_dtype
+ *   v_proj             [B, T, H, d_v]  io_dtype
+ *   conv_q, conv_k     [H, d_k, conv_width] float32;  conv_v [H, d_v, conv_width]
+ *   a_logit, b_logit   [B, T, H] float32
+ *   A, b_alpha         [H] float32
+ *   q_hist, k_hist, v_hist  [B, conv_width - 1, H, d] io_dtype: the rows just
+ *                      before t = 0 (a previous segment's last rows), or NULL
+ *                      for zeros (the sequence starts at t = 0)
+ *   q, k, v            outputs, same shapes and dtype as the projections
+ *   alpha, beta        [B, T, H] float32 outputs
+ *   conv_width in 1..4; norm_eps >= 0 (1e-6 recommended).  The outputs feed
+ *   gdn_prefill_fwd / gdn_decode_step directly.
+ */
+gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* v_proj,
+                            const float* conv_q, const float* conv_k, const float* conv_v,
+                            const float* a_logit, const float* b_logit, const float* A, const float* b_alpha,
+                            const void* q_hist, const void* k_hist, const void* v_hist,
+                            void* q, void* k, void* v, float* alpha, float* beta,
+                            int B, int T, int H, int d_k, int d_v, int conv_width,
+                            gdn_dtype io_dtype, float norm_eps, void* hip_stream);
+
 /* Static, never-NULL description of a status code. */
 const char* gdn_status_string(gdn_status status);
 

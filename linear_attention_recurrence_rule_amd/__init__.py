@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
     "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
-    "gdn_status_string",
+    "gdn_frontend_fwd", "gdn_status_string",
 ]
 
 GDN_F32 = 0
@@ -60,6 +60,9 @@ def load_library():
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [fp, vp, fp, f, vp, lg, i, i, vp]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_frontend_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp, vp, vp, vp, vp, fp, fp,
+                                     i, i, i, i, i, i, i, f, vp]
+    lib.gdn_frontend_fwd.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -191,3 +194,49 @@ def gdn_gated_rmsnorm(y, z, weight=None, eps=1e-6, out=None, stream=None):
     if st:
         raise GdnError(st, "gdn_gated_rmsnorm")
     return out
+
+
+def gdn_frontend_fwd(q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, a_logit, b_logit, A, b_alpha,
+                     q_hist=None, k_hist=None, v_hist=None, eps=1e-6, out=None, stream=None):
+    """Front end: q, k = L2Norm(SiLU(ShortConv(proj))), v = SiLU(ShortConv(v_proj)),
+    beta = sigmoid(b_logit), alpha = exp(-exp(A) softplus(a_logit + b_alpha)).
+    q_proj, k_proj [B, T, H, d_k]; v_proj [B, T, H, d_v] (bf16 or fp32, one dtype);
+    conv_* [H, d, W] fp32 (W <= 4); a_logit, b_logit [B, T, H] fp32; A, b_alpha [H]
+    fp32; *_hist [B, W-1, H, d] or None.  ``out`` may be a tuple (q, k, v, alpha,
+    beta) of preallocated tensors.  Returns (q, k, v, alpha, beta)."""
+    lib = load_library()
+    _require_gpu(q_proj, "q_proj")
+    B, T, H, dk = q_proj.shape
+    dv = v_proj.shape[-1]
+    W = conv_q.shape[-1]
+    dev, dt = q_proj.device, q_proj.dtype
+    _check(k_proj, "k_proj", (B, T, H, dk), dt, dev)
+    _check(v_proj, "v_proj", (B, T, H, dv), dt, dev)
+    _check(conv_q, "conv_q", (H, dk, W), torch.float32, dev)
+    _check(conv_k, "conv_k", (H, dk, W), torch.float32, dev)
+    _check(conv_v, "conv_v", (H, dv, W), torch.float32, dev)
+    _check(a_logit, "a_logit", (B, T, H), torch.float32, dev)
+    _check(b_logit, "b_logit", (B, T, H), torch.float32, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(b_alpha, "b_alpha", (H,), torch.float32, dev)
+    _check(q_hist, "q_hist", (B, W - 1, H, dk), dt, dev)
+    _check(k_hist, "k_hist", (B, W - 1, H, dk), dt, dev)
+    _check(v_hist, "v_hist", (B, W - 1, H, dv), dt, dev)
+    if out is None:
+        out = (torch.empty((B, T, H, dk), dtype=dt, device=dev), torch.empty((B, T, H, dk), dtype=dt, device=dev),
+               torch.empty((B, T, H, dv), dtype=dt, device=dev),
+               torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               torch.empty((B, T, H), dtype=torch.float32, device=dev))
+    q, k, v, alpha, beta = out
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    st = lib.gdn_frontend_fwd(_ptr(q_proj), _ptr(k_proj), _ptr(v_proj), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v),
+                              _ptr(a_logit), _ptr(b_logit), _ptr(A), _ptr(b_alpha), _ptr(q_hist), _ptr(k_hist),
+                              _ptr(v_hist), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B, T, H, dk, dv, W,
+                              _dtype_code(q_proj), float(eps), _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_frontend_fwd")
+    return q, k, v, alpha, beta

@@ -1,0 +1,179 @@
+// Front end of the Gated DeltaNet mixer (slinene ai-papers-daily page on
+// Qwen3.8-Next, Module A, parameterisation block; the mixer figure of the
+// paper.rainbus.top digest): from the projected streams to the recurrence
+// inputs,
+//     q = L2Norm(SiLU(ShortConv(q_proj)))      k likewise
+//     v = SiLU(ShortConv(v_proj))
+//     beta = sigmoid(b_logit),  alpha = exp(-exp(A_h) softplus(a_logit + b_alpha_h))
+// ShortConv is a causal depthwise convolution over time of width W (1..4),
+// one filter per (head, channel), no bias; the W-1 rows before the first
+// token come from the caller's history or are zero.  L2Norm divides by
+// sqrt(sum(x^2) + eps) over the head dimension.
+//
+// One pass per stream (q, k, v), each a pure stream over its input and output
+// (HBM-bound).  A row group of D/4 lanes owns one (sequence, head) and a run
+// of kRun consecutive tokens; each lane owns 4 channels, keeps its filter
+// taps and the last W-1 input rows in registers and slides along the run,
+// loading the next token's row while the current one is processed.  The L2
+// norm is a shuffle reduction inside the row group.  Row groups of a wave
+// take consecutive heads, so a wave's loads and stores cover adjacent rows.
+// The v pass also writes alpha and beta (one lane per row group).
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace frontend {
+
+constexpr int kRun = 32;   // tokens per row group
+
+template <bool kBf16>
+__device__ __forceinline__ float4v load4(const void* p, long i) {
+    if constexpr (kBf16) {
+        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return float4v{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    } else {
+        return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
+    }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void store4(void* p, long i, float4v x) {
+    if constexpr (kBf16) {
+        uint2 r;
+        r.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+        r.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = r;
+    } else {
+        *reinterpret_cast<float4v*>(static_cast<float*>(p) + i) = x;
+    }
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float softplus(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
+
+template <int D, int W, bool kNorm, bool kGates, bool kBf16>
+__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x, const float* __restrict__ w,
+                                                     const void* __restrict__ hist, void* __restrict__ out,
+                                                     const float* __restrict__ a_logit,
+                                                     const float* __restrict__ b_logit,
+                                                     const float* __restrict__ A, const float* __restrict__ b_alpha,
+                                                     float* __restrict__ alpha, float* __restrict__ beta, int B,
+                                                     int T, int H, float eps) {
+    constexpr int LPR = D / 4;              // lanes per row
+    constexpr int RPB = 256 / LPR;          // row groups per block
+    const int tid = threadIdx.x;
+    const int sub = tid % LPR;
+    const long task = static_cast<long>(blockIdx.x) * RPB + tid / LPR;
+    const int nruns = (T + kRun - 1) / kRun;
+    const int h = static_cast<int>(task % H);
+    const long rest = task / H;
+    const int run = static_cast<int>(rest % nruns);
+    const int b = static_cast<int>(rest / nruns);
+    if (b >= B) return;                      // whole row groups drop out together
+    const int t0 = run * kRun, t1 = min(t0 + kRun, T);
+    const long row_stride = static_cast<long>(H) * D;
+    const long base = (static_cast<long>(b) * T * H + h) * D + 4 * sub;   // element (b, t = 0, h, 4 sub)
+
+    // filter taps of this lane's 4 channels: wt[j][c] = w[h][4 sub + c][j]
+    float4v wt[W];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) wt[j][c] = w[(static_cast<long>(h) * D + 4 * sub + c) * W + j];
+
+    // the W-1 rows before t0: from the sequence, the caller's history, or zero
+    float4v win[W > 1 ? W - 1 : 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int t = t0 - (W - 1) + j;
+        if (t >= 0) {
+            win[j] = load4<kBf16>(x, base + t * row_stride);
+        } else if (hist) {
+            const long hb = ((static_cast<long>(b) * (W - 1) + (W - 1 + t)) * H + h) * D + 4 * sub;
+            win[j] = load4<kBf16>(hist, hb);
+        } else {
+            win[j] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    float4v cur = load4<kBf16>(x, base + t0 * row_stride);
+    for (int t = t0; t < t1; ++t) {
+        // the next row is in flight while this one is processed
+        const float4v nxt = load4<kBf16>(x, base + min(t + 1, t1 - 1) * static_cast<long>(row_stride));
+        float4v c = wt[W - 1] * cur;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) c += wt[j] * win[j];
+        float4v s = float4v{silu(c[0]), silu(c[1]), silu(c[2]), silu(c[3])};
+        if constexpr (kNorm) {
+            float ss = s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+#pragma unroll
+            for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off);
+            s *= 1.0f / sqrtf(ss + eps);
+        }
+        store4<kBf16>(out, base + t * row_stride, s);
+        if constexpr (kGates) {
+            if (sub == 0) {
+                const long g = (static_cast<long>(b) * T + t) * H + h;
+                beta[g] = sigmoid(b_logit[g]);
+                alpha[g] = __expf(-__expf(A[h]) * softplus(a_logit[g] + b_alpha[h]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j + 1 < W - 1; ++j) win[j] = win[j + 1];
+        if constexpr (W > 1) win[W - 2] = cur;
+        cur = nxt;
+    }
+}
+
+template <int D, int W, bool kNorm, bool kGates, bool kBf16>
+static hipError_t launch_stream(const void* x, const float* w, const void* hist, void* out, const FrontendArgs& a) {
+    constexpr int RPB = 256 / (D / 4);
+    const long tasks = static_cast<long>(a.B) * a.H * ((a.T + kRun - 1) / kRun);
+    const long blocks = (tasks + RPB - 1) / RPB;
+    hipLaunchKernelGGL((stream_kernel<D, W, kNorm, kGates, kBf16>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, a.stream, x, w, hist, out, a.a_logit, a.b_logit, a.A, a.b_alpha, a.alpha, a.beta, a.B, a.T,
+                       a.H, a.eps);
+    return hipGetLastError();
+}
+
+template <int W, bool kNorm, bool kGates, bool kBf16>
+static hipError_t launch_d(int d, const void* x, const float* w, const void* hist, void* out, const FrontendArgs& a) {
+    switch (d) {
+        case 16: return launch_stream<16, W, kNorm, kGates, kBf16>(x, w, hist, out, a);
+        case 32: return launch_stream<32, W, kNorm, kGates, kBf16>(x, w, hist, out, a);
+        case 64: return launch_stream<64, W, kNorm, kGates, kBf16>(x, w, hist, out, a);
+        case 128: return launch_stream<128, W, kNorm, kGates, kBf16>(x, w, hist, out, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int W, bool kBf16>
+static hipError_t launch_all(const FrontendArgs& a) {
+    hipError_t e = launch_d<W, true, false, kBf16>(a.dk, a.q_proj, a.conv_q, a.q_hist, a.q, a);
+    if (e != hipSuccess) return e;
+    e = launch_d<W, true, false, kBf16>(a.dk, a.k_proj, a.conv_k, a.k_hist, a.k, a);
+    if (e != hipSuccess) return e;
+    return launch_d<W, false, true, kBf16>(a.dv, a.v_proj, a.conv_v, a.v_hist, a.v, a);
+}
+
+template <bool kBf16>
+static hipError_t launch_w(const FrontendArgs& a) {
+    switch (a.width) {
+        case 1: return launch_all<1, kBf16>(a);
+        case 2: return launch_all<2, kBf16>(a);
+        case 3: return launch_all<3, kBf16>(a);
+        case 4: return launch_all<4, kBf16>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace frontend
+
+hipError_t launch_frontend(const FrontendArgs& a) {
+    if (a.T == 0) return hipSuccess;
+    return a.bf16 ? frontend::launch_w<true>(a) : frontend::launch_w<false>(a);
+}
+
+}  // namespace gdn

@@ -105,6 +105,33 @@ gdn_status gdn_gated_rmsnorm(const float* y, const void* z, const float* weight,
     return from_hip(gdn::launch_gated_rmsnorm(a));
 }
 
+gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* v_proj, const float* conv_q,
+                            const float* conv_k, const float* conv_v, const float* a_logit, const float* b_logit,
+                            const float* A, const float* b_alpha, const void* q_hist, const void* k_hist,
+                            const void* v_hist, void* q, void* k, void* v, float* alpha, float* beta, int B, int T,
+                            int H, int d_k, int d_v, int conv_width, gdn_dtype io_dtype, float norm_eps,
+                            void* hip_stream) {
+    if (!dtype_ok(io_dtype)) return GDN_ERR_DTYPE;
+    if (B <= 0 || H <= 0 || T < 0 || conv_width < 1 || !(norm_eps >= 0.f)) return GDN_ERR_SHAPE;
+    if (conv_width > 4 || !head_size_ok(d_k) || !head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, 128) || static_cast<long long>(B) * H * ((T + 31) / 32) / 2 >= INT_MAX)
+        return GDN_ERR_UNSUPPORTED;
+    if (T == 0) return GDN_OK;
+    for (const void* p : {q_proj, k_proj, v_proj, static_cast<const void*>(conv_q), static_cast<const void*>(conv_k),
+                          static_cast<const void*>(conv_v), static_cast<const void*>(a_logit),
+                          static_cast<const void*>(b_logit), static_cast<const void*>(A),
+                          static_cast<const void*>(b_alpha), static_cast<const void*>(q), static_cast<const void*>(k),
+                          static_cast<const void*>(v), static_cast<const void*>(alpha), static_cast<const void*>(beta)})
+        if (!p) return GDN_ERR_NULL;
+    for (const void* p : {q_proj, k_proj, v_proj, q_hist, k_hist, v_hist, static_cast<const void*>(q),
+                          static_cast<const void*>(k), static_cast<const void*>(v)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::FrontendArgs a{q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, a_logit, b_logit, A, b_alpha,
+                        q_hist, k_hist, v_hist, q, k, v, alpha, beta, B, T, H, d_k, d_v, conv_width,
+                        io_dtype == GDN_BF16, norm_eps, static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_frontend(a));
+}
+
 const char* gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "ok";

@@ -48,10 +48,36 @@ struct NormArgs {
     hipStream_t stream;
 };
 
+struct FrontendArgs {
+    const void* q_proj;
+    const void* k_proj;
+    const void* v_proj;
+    const float* conv_q;        // [H, d_k, width]
+    const float* conv_k;
+    const float* conv_v;        // [H, d_v, width]
+    const float* a_logit;       // [B, T, H]
+    const float* b_logit;
+    const float* A;             // [H]
+    const float* b_alpha;       // [H]
+    const void* q_hist;         // [B, width-1, H, d] or null (zeros)
+    const void* k_hist;
+    const void* v_hist;
+    void* q;
+    void* k;
+    void* v;
+    float* alpha;
+    float* beta;
+    int B, T, H, dk, dv, width;
+    bool bf16;
+    float eps;
+    hipStream_t stream;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
+hipError_t launch_frontend(const FrontendArgs& a);
 
 }  // namespace gdn

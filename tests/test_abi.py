@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gdn_decode_step", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
+    assert declared_functions() == ["gdn_decode_step", "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
                                     "gdn_prefill_workspace_bytes", "gdn_status_string"]
 
 
@@ -149,3 +149,36 @@ def test_python_binding_refuses_host_tensors():
         gdn.gdn_decode_step(q[0], q[0], q[0], a[0], a[0], torch.zeros(4, 2, 16, 16))
     with pytest.raises(ValueError, match="GPU tensor"):
         gdn.gdn_gated_rmsnorm(q, q)
+
+
+def _frontend(qp=FAKE, kp=FAKE, vp=FAKE, cq=FAKE, ck=FAKE, cv=FAKE, al=FAKE, bl=FAKE, A=FAKE, ba=FAKE,
+              qh=None, kh=None, vh=None, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE,
+              B=1, T=8, H=2, dk=64, dv=64, W=4, dtype=1, eps=1e-6):
+    lib = gdn.load_library()
+    return lib.gdn_frontend_fwd(qp, kp, vp, cq, ck, cv, al, bl, A, ba, qh, kh, vh, q, k, v, a, b,
+                                B, T, H, dk, dv, W, dtype, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(B=0), ERR_SHAPE),
+    (dict(T=-2), ERR_SHAPE),
+    (dict(W=0), ERR_SHAPE),
+    (dict(eps=-1.0), ERR_SHAPE),
+    (dict(eps=float("nan")), ERR_SHAPE),
+    (dict(W=5), ERR_UNSUPPORTED),
+    (dict(dk=96), ERR_UNSUPPORTED),
+    (dict(qp=None), ERR_NULL),
+    (dict(cv=None), ERR_NULL),
+    (dict(A=None), ERR_NULL),
+    (dict(b=None), ERR_NULL),
+    (dict(kp=MISALIGNED), ERR_ALIGN),
+    (dict(vh=MISALIGNED), ERR_ALIGN),
+    (dict(v=MISALIGNED), ERR_ALIGN),
+])
+def test_frontend_rejects(kwargs, status):
+    assert _frontend(**kwargs) == status
+
+
+def test_frontend_empty_sequence_is_a_no_op():
+    assert _frontend(T=0, qp=None, q=None) == OK

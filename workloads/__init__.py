@@ -12,4 +12,5 @@ from .synth import (  # noqa: F401
     config_prefill_inputs,
     decode_initial_state,
     decode_step_inputs,
+    frontend_inputs,
 )

@@ -150,3 +150,33 @@ def decode_step_inputs(step, index=3, N=None, H=None):
     seg = _draw_segment(np.random.default_rng([c["seed"], step]), N, 1, H, c["dk"], c["dv"],
                         c["A"], c["b"], c["dtype"], False)
     return {key: val[:, 0] for key, val in seg.items()}
+
+
+def frontend_inputs(B, T, H, dk, dv, dtype="bf16", A=-1.0, b=0.5, width=4, seed=0, history=False):
+    """Inputs of the front end (projected streams, filters, gate logits).
+
+    q_proj, k_proj, v_proj ~ N(0, 1) (rounded to bf16 unless dtype is f32);
+    filters conv_* ~ N(0, 1/width); a_logit, b_logit ~ N(0, 1); A[h] = A and
+    b_alpha[h] = b for every head, so the gates follow the workload recipe
+    above; with ``history`` the width-1 rows before t = 0 are drawn too.
+    Draw order: q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, b_logit,
+    a_logit, then the histories.
+    """
+    rng = np.random.default_rng([seed, 7])
+    out = dict(
+        q_proj=_cast(rng.standard_normal((B, T, H, dk)), dtype),
+        k_proj=_cast(rng.standard_normal((B, T, H, dk)), dtype),
+        v_proj=_cast(rng.standard_normal((B, T, H, dv)), dtype),
+        conv_q=(rng.standard_normal((H, dk, width)) / np.sqrt(width)).astype(np.float32),
+        conv_k=(rng.standard_normal((H, dk, width)) / np.sqrt(width)).astype(np.float32),
+        conv_v=(rng.standard_normal((H, dv, width)) / np.sqrt(width)).astype(np.float32),
+        b_logit=rng.standard_normal((B, T, H)).astype(np.float32),
+        a_logit=rng.standard_normal((B, T, H)).astype(np.float32),
+        A=np.full(H, A, dtype=np.float32),
+        b_alpha=np.full(H, b, dtype=np.float32),
+    )
+    if history:
+        out["q_hist"] = _cast(rng.standard_normal((B, width - 1, H, dk)), dtype)
+        out["k_hist"] = _cast(rng.standard_normal((B, width - 1, H, dk)), dtype)
+        out["v_hist"] = _cast(rng.standard_normal((B, width - 1, H, dv)), dtype)
+    return out
