@@ -101,6 +101,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -242,6 +243,52 @@ def main():
                             "all_bytes_GBps": all_bytes / (step_ms * 1e-3) / 1e9,
                             "tokens_per_s": N / (step_ms * 1e-3)}
         del state, steps_in, yd
+        torch.cuda.empty_cache()
+
+    # ---------------- front end: projected streams -> q, k, v, alpha, beta ----------------
+    if not args.no_frontend:
+        W = 4
+        log(f"front end: B={B} T={T} H={H} d={dk} conv width {W}")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        fe = dict(q_proj=torch.randn((B, T, H, dk), generator=gen, device=dev).to(torch.bfloat16),
+                  k_proj=torch.randn((B, T, H, dk), generator=gen, device=dev).to(torch.bfloat16),
+                  v_proj=torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16),
+                  conv_q=torch.randn((H, dk, W), generator=gen, device=dev) / 2,
+                  conv_k=torch.randn((H, dk, W), generator=gen, device=dev) / 2,
+                  conv_v=torch.randn((H, dv, W), generator=gen, device=dev) / 2,
+                  a_logit=torch.randn((B, T, H), generator=gen, device=dev),
+                  b_logit=torch.randn((B, T, H), generator=gen, device=dev),
+                  A=torch.full((H,), -2.0, device=dev), b_alpha=torch.full((H,), 0.5, device=dev))
+        outs = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, T, H), device=dev), torch.empty((B, T, H), device=dev))
+
+        def fe_call():
+            gdn.gdn_frontend_fwd(fe["q_proj"], fe["k_proj"], fe["v_proj"], fe["conv_q"], fe["conv_k"],
+                                 fe["conv_v"], fe["a_logit"], fe["b_logit"], fe["A"], fe["b_alpha"],
+                                 out=outs, stream=stream)
+        for _ in range(3):
+            fe_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_fe = 20
+        e0.record(stream)
+        for _ in range(n_fe):
+            fe_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fe_ms = e0.elapsed_time(e1) / n_fe
+        fe_bytes = B * T * H * ((2 * dk + dv) * 2 * 2 + 4 * 4)
+        result["frontend"] = {"workload": f"front end, B={B} T={T} H={H} d={dk}, conv width {W}, bf16",
+                              "kernel": "frontend stream_kernel x3", "avg_call_ms": fe_ms,
+                              "algorithmic_bytes_per_call": fe_bytes,
+                              "achieved": fe_bytes / (fe_ms * 1e-3) / 1e9, "unit": "GB/s",
+                              "frac": fe_bytes / (fe_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "tokens_per_s": B * T / (fe_ms * 1e-3)}
+        log(f"front end {fe_ms * 1e3:.1f} us, {fe_bytes / (fe_ms * 1e-3) / 1e9:.0f} GB/s")
+        del fe, outs
         torch.cuda.empty_cache()
 
     # ---------------- float64 CPU oracle on a bounded sample ----------------

@@ -13,9 +13,10 @@
 // One pass per stream (q, k, v), each a pure stream over its input and output
 // (HBM-bound).  A row group of D/4 lanes owns one (sequence, head) and a run
 // of kRun consecutive tokens; each lane owns 4 channels, keeps its filter
-// taps and the last W-1 input rows in registers and slides along the run,
-// loading the next token's row while the current one is processed.  The L2
-// norm is a shuffle reduction inside the row group.  Row groups of a wave
+// taps and the last W-1 input rows in registers and slides along the run
+// kStep tokens at a time (their norms reduce together), loading the next
+// step's rows while the current ones are processed.  The L2 norm is a
+// shuffle reduction inside the row group.  Row groups of a wave
 // take consecutive heads, so a wave's loads and stores cover adjacent rows.
 // The v pass also writes alpha and beta (one lane per row group).
 #include "gdn_device.hpp"
@@ -25,6 +26,7 @@ namespace gdn {
 namespace frontend {
 
 constexpr int kRun = 32;   // tokens per row group
+constexpr int kStep = 4;   // tokens processed together (kRun is a multiple)
 
 template <bool kBf16>
 __device__ __forceinline__ float4v load4(const void* p, long i) {
@@ -41,16 +43,18 @@ template <bool kBf16>
 __device__ __forceinline__ void store4(void* p, long i, float4v x) {
     if constexpr (kBf16) {
         uint2 r;
-        r.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-        r.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+        r.x = pack_bf16x2(x[0], x[1]);
+        r.y = pack_bf16x2(x[2], x[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = r;
     } else {
         *reinterpret_cast<float4v*>(static_cast<float*>(p) + i) = x;
     }
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// hardware reciprocal (about 1 ulp): the outputs are rounded to bf16 or
+// compared at float32 tolerance, and x -> -inf still gives x * 0 = -0
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
 __device__ __forceinline__ float softplus(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
 
 template <int D, int W, bool kNorm, bool kGates, bool kBf16>
@@ -98,32 +102,59 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         }
     }
 
-    float4v cur = load4<kBf16>(x, base + t0 * row_stride);
-    for (int t = t0; t < t1; ++t) {
-        // the next row is in flight while this one is processed
-        const float4v nxt = load4<kBf16>(x, base + min(t + 1, t1 - 1) * static_cast<long>(row_stride));
-        float4v c = wt[W - 1] * cur;
+    // kStep tokens per step, independent of each other given the inputs, so
+    // their reductions overlap; the next step's rows are loaded meanwhile.
+    auto load_rows = [&](float4v (&r)[kStep], int t) {
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) c += wt[j] * win[j];
-        float4v s = float4v{silu(c[0]), silu(c[1]), silu(c[2]), silu(c[3])};
-        if constexpr (kNorm) {
-            float ss = s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+        for (int u = 0; u < kStep; ++u)
+            r[u] = load4<kBf16>(x, base + min(t + u, t1 - 1) * static_cast<long>(row_stride));
+    };
+    float4v cur[kStep], nxt[kStep];
+    load_rows(cur, t0);
+    for (int t = t0; t < t1; t += kStep) {
+        if (t + kStep < t1) load_rows(nxt, t + kStep);
+        float4v s[kStep];
 #pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off);
-            s *= 1.0f / sqrtf(ss + eps);
+        for (int u = 0; u < kStep; ++u) {
+            // conv over rows t+u-(W-1) .. t+u: the window holds the W-1 rows
+            // before t, cur the rows t .. t+kStep-1
+            float4v c = wt[W - 1] * cur[u];
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) {
+                const int src = u - (W - 1) + j;   // row t + src
+                c += wt[j] * (src >= 0 ? cur[src >= 0 ? src : 0] : win[(W - 1) + src >= 0 ? (W - 1) + src : 0]);
+            }
+            s[u] = float4v{silu(c[0]), silu(c[1]), silu(c[2]), silu(c[3])};
         }
-        store4<kBf16>(out, base + t * row_stride, s);
+        if constexpr (kNorm) {
+            float ss[kStep];
+#pragma unroll
+            for (int u = 0; u < kStep; ++u) ss[u] = s[u][0] * s[u][0] + s[u][1] * s[u][1] + s[u][2] * s[u][2] + s[u][3] * s[u][3];
+#pragma unroll
+            for (int off = 1; off < LPR; off <<= 1)
+#pragma unroll
+                for (int u = 0; u < kStep; ++u) ss[u] += __shfl_xor(ss[u], off);
+#pragma unroll
+            for (int u = 0; u < kStep; ++u) s[u] *= __builtin_amdgcn_rsqf(ss[u] + eps);
+        }
+#pragma unroll
+        for (int u = 0; u < kStep; ++u)
+            if (t + u < t1) store4<kBf16>(out, base + (t + u) * row_stride, s[u]);
         if constexpr (kGates) {
-            if (sub == 0) {
-                const long g = (static_cast<long>(b) * T + t) * H + h;
+            if (sub < kStep && t + sub < t1) {
+                const long g = (static_cast<long>(b) * T + t + sub) * H + h;
                 beta[g] = sigmoid(b_logit[g]);
                 alpha[g] = __expf(-__expf(A[h]) * softplus(a_logit[g] + b_alpha[h]));
             }
         }
+        // the window moves to the last W-1 rows of this step
 #pragma unroll
-        for (int j = 0; j + 1 < W - 1; ++j) win[j] = win[j + 1];
-        if constexpr (W > 1) win[W - 2] = cur;
-        cur = nxt;
+        for (int j = 0; j < W - 1; ++j) {
+            const int src = kStep - (W - 1) + j;   // row t + src
+            win[j] = src >= 0 ? cur[src >= 0 ? src : 0] : win[j + kStep < W - 1 ? j + kStep : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kStep; ++u) cur[u] = nxt[u];
     }
 }
 

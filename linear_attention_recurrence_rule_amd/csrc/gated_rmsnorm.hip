@@ -55,19 +55,20 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
 #pragma unroll
         for (int off = 1; off < kLanesPerRow; off <<= 1) ss += __shfl_xor(ss, off);
         if (row >= rows) continue;
-        const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+        // hardware reciprocal square root and reciprocal (about 1 ulp each)
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + eps);
         const float yy[4] = {yv[p].x, yv[p].y, yv[p].z, yv[p].w};
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float gate = 1.0f / (1.0f + expf(-zv[p][i]));
+            const float gate = __builtin_amdgcn_rcpf(1.0f + __expf(-zv[p][i]));
             o[i] = gate * (yy[i] * inv) * (1.0f + w[i]);
         }
         const long base = row * DV + sub * 4;
         // streaming stores: the output is not read again here
         if constexpr (kBf16) {
-            const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(o[0])) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16);
-            const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(o[2])) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16);
+            const uint32_t lo = pack_bf16x2(o[0], o[1]);
+            const uint32_t hi = pack_bf16x2(o[2], o[3]);
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base));
         } else {
