@@ -16,9 +16,11 @@
 // taps and the last W-1 input rows in registers and slides along the run
 // kStep tokens at a time (their norms reduce together), loading the next
 // step's rows while the current ones are processed.  The L2 norm is a
-// shuffle reduction inside the row group.  Row groups of a wave
+// DPP / swizzle reduction inside the row group.  Row groups of a wave
 // take consecutive heads, so a wave's loads and stores cover adjacent rows.
 // The v pass also writes alpha and beta (one lane per row group).
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -56,6 +58,22 @@ __device__ __forceinline__ void store4(void* p, long i, float4v x) {
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
 __device__ __forceinline__ float softplus(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
+
+// Sum over aligned groups of N lanes (N a power of two up to 32), every lane
+// getting the group's total: DPP quad permutations and row mirrors inside a
+// row of 16, then a 32-lane swizzle that swaps the two rows.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    if constexpr (N > 1) x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+    if constexpr (N > 2) x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+    if constexpr (N > 4) x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    if constexpr (N > 8) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+    if constexpr (N > 16) x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));   // lane ^ 16
+    return x;
+}
 
 template <int D, int W, bool kNorm, bool kGates, bool kBf16>
 __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x, const float* __restrict__ w,
@@ -104,24 +122,25 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 
     // kStep tokens per step, independent of each other given the inputs, so
     // their reductions overlap; the next step's rows are loaded meanwhile.
-    auto load_rows = [&](float4v (&r)[kStep], int t) {
+    // Offsets inside the run are 32-bit (a run spans kRun rows).
+    const int last = t1 - 1 - t0;
+    const int rs = static_cast<int>(row_stride);
+    const long run_base = base + t0 * row_stride;
+    auto load_rows = [&](float4v (&r)[kStep], int r0) {
 #pragma unroll
-        for (int u = 0; u < kStep; ++u)
-            r[u] = load4<kBf16>(x, base + min(t + u, t1 - 1) * static_cast<long>(row_stride));
+        for (int u = 0; u < kStep; ++u) r[u] = load4<kBf16>(x, run_base + min(r0 + u, last) * rs);
     };
-    float4v cur[kStep], nxt[kStep];
-    load_rows(cur, t0);
-    for (int t = t0; t < t1; t += kStep) {
-        if (t + kStep < t1) load_rows(nxt, t + kStep);
+    auto step = [&](float4v (&cur)[kStep], float4v (&nxt)[kStep], int r0) {
+        if (r0 + kStep <= last) load_rows(nxt, r0 + kStep);
         float4v s[kStep];
 #pragma unroll
         for (int u = 0; u < kStep; ++u) {
-            // conv over rows t+u-(W-1) .. t+u: the window holds the W-1 rows
-            // before t, cur the rows t .. t+kStep-1
+            // conv over rows r0+u-(W-1) .. r0+u: the window holds the W-1 rows
+            // before r0, cur the rows r0 .. r0+kStep-1
             float4v c = wt[W - 1] * cur[u];
 #pragma unroll
             for (int j = 0; j < W - 1; ++j) {
-                const int src = u - (W - 1) + j;   // row t + src
+                const int src = u - (W - 1) + j;   // row r0 + src
                 c += wt[j] * (src >= 0 ? cur[src >= 0 ? src : 0] : win[(W - 1) + src >= 0 ? (W - 1) + src : 0]);
             }
             s[u] = float4v{silu(c[0]), silu(c[1]), silu(c[2]), silu(c[3])};
@@ -131,18 +150,16 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 #pragma unroll
             for (int u = 0; u < kStep; ++u) ss[u] = s[u][0] * s[u][0] + s[u][1] * s[u][1] + s[u][2] * s[u][2] + s[u][3] * s[u][3];
 #pragma unroll
-            for (int off = 1; off < LPR; off <<= 1)
-#pragma unroll
-                for (int u = 0; u < kStep; ++u) ss[u] += __shfl_xor(ss[u], off);
+            for (int u = 0; u < kStep; ++u) ss[u] = row_sum<LPR>(ss[u]);
 #pragma unroll
             for (int u = 0; u < kStep; ++u) s[u] *= __builtin_amdgcn_rsqf(ss[u] + eps);
         }
 #pragma unroll
         for (int u = 0; u < kStep; ++u)
-            if (t + u < t1) store4<kBf16>(out, base + (t + u) * row_stride, s[u]);
+            if (r0 + u <= last) store4<kBf16>(out, run_base + (r0 + u) * rs, s[u]);
         if constexpr (kGates) {
-            if (sub < kStep && t + sub < t1) {
-                const long g = (static_cast<long>(b) * T + t + sub) * H + h;
+            if (sub < kStep && r0 + sub <= last) {
+                const long g = (static_cast<long>(b) * T + t0 + r0 + sub) * H + h;
                 beta[g] = sigmoid(b_logit[g]);
                 alpha[g] = __expf(-__expf(A[h]) * softplus(a_logit[g] + b_alpha[h]));
             }
@@ -150,11 +167,16 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         // the window moves to the last W-1 rows of this step
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
-            const int src = kStep - (W - 1) + j;   // row t + src
+            const int src = kStep - (W - 1) + j;   // row r0 + src
             win[j] = src >= 0 ? cur[src >= 0 ? src : 0] : win[j + kStep < W - 1 ? j + kStep : 0];
         }
-#pragma unroll
-        for (int u = 0; u < kStep; ++u) cur[u] = nxt[u];
+    };
+    // steps in pairs over two register sets, so that no copies are needed
+    float4v ra[kStep], rb[kStep];
+    load_rows(ra, 0);
+    for (int r0 = 0; r0 <= last; r0 += 2 * kStep) {
+        step(ra, rb, r0);
+        if (r0 + kStep <= last) step(rb, ra, r0 + kStep);
     }
 }
 
