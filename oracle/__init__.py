@@ -11,7 +11,9 @@ on the slinene ai-papers-daily page (Module A, Gated DeltaNet: the four-line
 delta form of the recurrence and the output parameterisation) and on the
 paper.rainbus.top digest (method step (1)); the front end (short causal
 convolutions, SiLU, L2 normalisation and the gates) follows the
-parameterisation block of the same Module A.
+parameterisation block of the same Module A; multi-token (speculative)
+decode is the same recurrence over a block of draft tokens, with a commit step
+that advances the live state by the accepted prefix only.
 """
 
 from .gdn_ref import (  # noqa: F401
@@ -21,3 +23,4 @@ from .gdn_ref import (  # noqa: F401
     rel_err,
 )
 from .frontend_ref import gdn_frontend, short_conv, silu, l2norm  # noqa: F401
+from .mtp_ref import mtp_verify, mtp_commit  # noqa: F401

@@ -13,4 +13,5 @@ from .synth import (  # noqa: F401
     decode_initial_state,
     decode_step_inputs,
     frontend_inputs,
+    mtp_draft_inputs,
 )

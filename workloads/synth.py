@@ -24,7 +24,8 @@ numpy.random.default_rng(seed); longer ones draw segment s (SEGMENT tokens
 each) from default_rng([seed, s]).  An optional prefill initial state draws
 from default_rng([seed, STATE_STREAM]).  Draw order inside a segment: q, k, v,
 beta-logit, alpha-logit, z.  Decode step j draws from default_rng([seed, j]);
-the decode initial state draws from default_rng(seed).
+the decode initial state draws from default_rng(seed); a block of draft
+tokens for multi-token decode draws from default_rng([seed, MTP_STREAM, block]).
 """
 
 import numpy as np
@@ -180,3 +181,16 @@ def frontend_inputs(B, T, H, dk, dv, dtype="bf16", A=-1.0, b=0.5, width=4, seed=
         out["k_hist"] = _cast(rng.standard_normal((B, width - 1, H, dk)), dtype)
         out["v_hist"] = _cast(rng.standard_normal((B, width - 1, H, dv)), dtype)
     return out
+
+
+MTP_STREAM = 2**31 - 2       # second seed word of the draft-block stream
+
+
+def mtp_draft_inputs(rnd, K=4, index=3, N=None, H=None):
+    """q, k, v [N, K, H, d], alpha, beta [N, K, H] for draft block ``rnd`` of
+    the decode config: K draft tokens per sequence with the config's
+    distributions, drawn from default_rng([seed, MTP_STREAM, rnd])."""
+    c = CONFIGS[index]
+    N, H = N or c["N"], H or c["H"]
+    return _draw_segment(np.random.default_rng([c["seed"], MTP_STREAM, rnd]), N, K, H, c["dk"], c["dv"],
+                         c["A"], c["b"], c["dtype"], False)
