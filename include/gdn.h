@@ -164,6 +164,54 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
                             int B, int T, int H, int d_k, int d_v, int conv_width,
                             gdn_dtype io_dtype, float norm_eps, void* hip_stream);
 
+/*
+ * Multi-token (speculative) decode, part 1: verify a block of K draft tokens
+ * per sequence from the live states (rainbus digest, inference section:
+ * multi-token prediction drafts, the target model verifies; each draft token
+ * is one step of the delta form, slinene page, Module A).  For t = 0 .. K-1,
+ * starting from S = state:
+ *     e_t = v_t - (alpha_t S)^T k_t;   S = alpha_t S + beta_t k_t e_t^T;
+ *     y_t = scale * S^T q_t
+ * The live state is read once and NOT modified.
+ *
+ *   q, k           [N, K, H, d_k]  qkv_dtype  (token t of sequence n: row (n K + t) H + h)
+ *   v              [N, K, H, d_v]  qkv_dtype
+ *   alpha, beta    [N, K, H]       float32
+ *   state          [N, H, d_k, d_v] float32, read only
+ *   y              [N, K, H, d_v]  float32 out
+ *   e              [N, K, H, d_v]  float32 out: the misses e_t, the input of
+ *                  gdn_decode_mtp_commit; NULL = not written
+ *   prefix_states  [N, K, H, d_k, d_v] float32 out: S after each draft token
+ *                  (K state writes: only for callers that keep snapshots);
+ *                  NULL = not written
+ *   K in 0..8 (K == 0: nothing to do); other sizes as gdn_decode_step.
+ */
+gdn_status gdn_decode_mtp_verify(const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta,
+                                 const float* state, float* y, float* e, float* prefix_states,
+                                 int N, int K, int H, int d_k, int d_v,
+                                 gdn_dtype qkv_dtype, float scale, void* hip_stream);
+
+/*
+ * Multi-token decode, part 2: advance each live state by the accepted prefix
+ * of its verified block, which rolls back the rejected drafts:
+ *     for t < accepted[n]:  S = alpha_t S + beta_t k_t e_t^T
+ * with the e_t that gdn_decode_mtp_verify wrote for the same block.  The
+ * result is exactly that call's prefix state after accepted[n] tokens; one
+ * read and one write of the state per sequence with accepted[n] > 0, nothing
+ * for sequences with accepted[n] == 0.
+ *
+ *   k              [N, K, H, d_k]  qkv_dtype (the block's keys)
+ *   alpha, beta    [N, K, H]       float32
+ *   e              [N, K, H, d_v]  float32 (from gdn_decode_mtp_verify)
+ *   accepted       [N] int32 in device memory; values are clamped to 0..K
+ *   state          [N, H, d_k, d_v] float32, updated in place
+ */
+gdn_status gdn_decode_mtp_commit(const void* k, const float* alpha, const float* beta,
+                                 const float* e, const int* accepted, float* state,
+                                 int N, int K, int H, int d_k, int d_v,
+                                 gdn_dtype qkv_dtype, void* hip_stream);
+
 /* Static, never-NULL description of a status code. */
 const char* gdn_status_string(gdn_status status);
 

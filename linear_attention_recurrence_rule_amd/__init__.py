@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
     "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
-    "gdn_frontend_fwd", "gdn_status_string",
+    "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit", "gdn_status_string",
 ]
 
 GDN_F32 = 0
@@ -63,6 +63,10 @@ def load_library():
     lib.gdn_frontend_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, vp, vp, vp, vp, vp, vp, fp, fp,
                                      i, i, i, i, i, i, i, f, vp]
     lib.gdn_frontend_fwd.restype = ctypes.c_int
+    lib.gdn_decode_mtp_verify.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, i, i, i, i, i, i, f, vp]
+    lib.gdn_decode_mtp_verify.restype = ctypes.c_int
+    lib.gdn_decode_mtp_commit.argtypes = [vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, vp]
+    lib.gdn_decode_mtp_commit.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -240,3 +244,58 @@ def gdn_frontend_fwd(q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, a_logit, b_
     if st:
         raise GdnError(st, "gdn_frontend_fwd")
     return q, k, v, alpha, beta
+
+
+def gdn_decode_mtp_verify(q, k, v, alpha, beta, state, y=None, e=None, prefix_states=None, scale=1.0,
+                          return_e=True, return_prefix_states=False, stream=None):
+    """Verify a block of K draft tokens per sequence from the live states (read only).
+    q, k [N, K, H, d_k]; v [N, K, H, d_v] (bf16 or fp32, one dtype); alpha, beta
+    [N, K, H] fp32; state [N, H, d_k, d_v] fp32.  Returns (y [N, K, H, d_v],
+    e [N, K, H, d_v] or None, prefix_states [N, K, H, d_k, d_v] or None), fp32."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (N, K, H, dk), q.dtype, dev)
+    _check(v, "v", (N, K, H, dv), q.dtype, dev)
+    _check(alpha, "alpha", (N, K, H), torch.float32, dev)
+    _check(beta, "beta", (N, K, H), torch.float32, dev)
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    _check(y, "y", (N, K, H, dv), torch.float32, dev)
+    if e is None and return_e:
+        e = torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    _check(e, "e", (N, K, H, dv), torch.float32, dev)
+    if prefix_states is None and return_prefix_states:
+        prefix_states = torch.empty((N, K, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(prefix_states, "prefix_states", (N, K, H, dk, dv), torch.float32, dev)
+    st = lib.gdn_decode_mtp_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
+                                   _ptr(e), _ptr(prefix_states), N, K, H, dk, dv, _dtype_code(q), float(scale),
+                                   _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_decode_mtp_verify")
+    return y, e, prefix_states
+
+
+def gdn_decode_mtp_commit(k, alpha, beta, e, accepted, state, stream=None):
+    """Advance each live state by its accepted drafts (int32 ``accepted`` [N] on the
+    device, clamped to 0..K), using the misses ``e`` of gdn_decode_mtp_verify.
+    k [N, K, H, d_k]; alpha, beta [N, K, H] fp32; e [N, K, H, d_v] fp32;
+    state [N, H, d_k, d_v] fp32, updated in place.  Returns state."""
+    lib = load_library()
+    _require_gpu(k, "k")
+    N, K, H, dk = k.shape
+    dv = state.shape[-1]
+    dev = k.device
+    _check(alpha, "alpha", (N, K, H), torch.float32, dev)
+    _check(beta, "beta", (N, K, H), torch.float32, dev)
+    _check(e, "e", (N, K, H, dv), torch.float32, dev)
+    _check(accepted, "accepted", (N,), torch.int32, dev)
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    st = lib.gdn_decode_mtp_commit(_ptr(k), _ptr(alpha), _ptr(beta), _ptr(e), _ptr(accepted), _ptr(state),
+                                   N, K, H, dk, dv, _dtype_code(k), _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_decode_mtp_commit")
+    return state

@@ -132,6 +132,52 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
     return from_hip(gdn::launch_frontend(a));
 }
 
+namespace {
+
+gdn_status mtp_check(int N, int K, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
+    if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
+    if (N < 0 || K < 0 || H <= 0) return GDN_ERR_SHAPE;
+    if (K > 8 || !head_size_ok(d_k) || !head_size_ok(d_v)) return GDN_ERR_UNSUPPORTED;
+    if (!fits(N, K, H, static_cast<long long>(d_k) * d_v) || static_cast<long long>(N) * K * H > INT_MAX)
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status gdn_decode_mtp_verify(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, const float* state, float* y, float* e,
+                                 float* prefix_states, int N, int K, int H, int d_k, int d_v,
+                                 gdn_dtype qkv_dtype, float scale, void* hip_stream) {
+    const gdn_status st = mtp_check(N, K, H, d_k, d_v, qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (N == 0 || K == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !y) return GDN_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(state), static_cast<const void*>(y),
+                          static_cast<const void*>(e), static_cast<const void*>(prefix_states)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::MtpArgs a{false, q, k, v, alpha, beta, const_cast<float*>(state), y, e, prefix_states, nullptr,
+                   N, K, H, d_k, d_v, qkv_dtype == GDN_BF16, scale, static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_mtp(a));
+}
+
+gdn_status gdn_decode_mtp_commit(const void* k, const float* alpha, const float* beta, const float* e,
+                                 const int* accepted, float* state, int N, int K, int H, int d_k, int d_v,
+                                 gdn_dtype qkv_dtype, void* hip_stream) {
+    const gdn_status st = mtp_check(N, K, H, d_k, d_v, qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (N == 0 || K == 0) return GDN_OK;
+    if (!k || !alpha || !beta || !e || !accepted || !state) return GDN_ERR_NULL;
+    for (const void* p : {k, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(e), static_cast<const void*>(accepted),
+                          static_cast<const void*>(state)})
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::MtpArgs a{true, nullptr, k, nullptr, alpha, beta, state, nullptr, const_cast<float*>(e), nullptr,
+                   accepted, N, K, H, d_k, d_v, qkv_dtype == GDN_BF16, 1.f, static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_mtp(a));
+}
+
 const char* gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "ok";

@@ -73,11 +73,30 @@ struct FrontendArgs {
     hipStream_t stream;
 };
 
+struct MtpArgs {
+    bool commit;                // false: verify a draft block; true: commit the accepted prefix
+    const void* q;              // [N, K, H, d_k] (verify only)
+    const void* k;              // [N, K, H, d_k]
+    const void* v;              // [N, K, H, d_v] (verify only)
+    const float* alpha;         // [N, K, H]
+    const float* beta;
+    float* state;               // [N, H, d_k, d_v]; read only when verifying
+    float* y;                   // [N, K, H, d_v] (verify)
+    float* e;                   // [N, K, H, d_v] misses: written by verify (may be null), read by commit
+    float* prefix;              // [N, K, H, d_k, d_v] or null (verify)
+    const int* accepted;        // [N] (commit)
+    int N, K, H, dk, dv;
+    bool bf16;
+    float scale;
+    hipStream_t stream;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
+hipError_t launch_mtp(const MtpArgs& a);
 
 }  // namespace gdn

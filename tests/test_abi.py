@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gdn_decode_step", "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
+    assert declared_functions() == ["gdn_decode_mtp_commit", "gdn_decode_mtp_verify", "gdn_decode_step",
+                                    "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
                                     "gdn_prefill_workspace_bytes", "gdn_status_string"]
 
 
@@ -182,3 +183,58 @@ def test_frontend_rejects(kwargs, status):
 
 def test_frontend_empty_sequence_is_a_no_op():
     assert _frontend(T=0, qp=None, q=None) == OK
+
+
+def _verify(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, y=FAKE, e=None, p=None,
+            N=4, K=4, H=2, dk=128, dv=128, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_decode_mtp_verify(q, k, v, a, b, s, y, e, p, N, K, H, dk, dv, dtype, 1.0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=4), ERR_DTYPE),
+    (dict(N=-1), ERR_SHAPE),
+    (dict(K=-1), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(K=9), ERR_UNSUPPORTED),
+    (dict(dv=48), ERR_UNSUPPORTED),
+    (dict(q=None), ERR_NULL),
+    (dict(s=None), ERR_NULL),
+    (dict(y=None), ERR_NULL),
+    (dict(e=MISALIGNED), ERR_ALIGN),
+    (dict(p=MISALIGNED), ERR_ALIGN),
+    (dict(s=MISALIGNED), ERR_ALIGN),
+])
+def test_mtp_verify_rejects(kwargs, status):
+    assert _verify(**kwargs) == status
+
+
+def test_mtp_verify_empty_is_a_no_op():
+    assert _verify(N=0, q=None) == OK
+    assert _verify(K=0, q=None) == OK
+
+
+def _commit(k=FAKE, a=FAKE, b=FAKE, e=FAKE, acc=FAKE, s=FAKE, N=4, K=4, H=2, dk=128, dv=128, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_decode_mtp_commit(k, a, b, e, acc, s, N, K, H, dk, dv, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), ERR_DTYPE),
+    (dict(N=-3), ERR_SHAPE),
+    (dict(K=-1), ERR_SHAPE),
+    (dict(K=12), ERR_UNSUPPORTED),
+    (dict(dk=8), ERR_UNSUPPORTED),
+    (dict(acc=None), ERR_NULL),
+    (dict(e=None), ERR_NULL),
+    (dict(s=None), ERR_NULL),
+    (dict(e=MISALIGNED), ERR_ALIGN),
+    (dict(s=MISALIGNED), ERR_ALIGN),
+])
+def test_mtp_commit_rejects(kwargs, status):
+    assert _commit(**kwargs) == status
+
+
+def test_mtp_commit_empty_is_a_no_op():
+    assert _commit(N=0, s=None) == OK
+    assert _commit(K=0, s=None) == OK
