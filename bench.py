@@ -102,6 +102,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -118,7 +119,8 @@ def main():
 
     import torch
     import linear_attention_recurrence_rule_amd as gdn
-    from workloads import CONFIGS, config_prefill_inputs, decode_initial_state, decode_step_inputs
+    from workloads import (CONFIGS, config_prefill_inputs, decode_initial_state, decode_step_inputs,
+                           mtp_draft_inputs)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -243,6 +245,63 @@ def main():
                             "all_bytes_GBps": all_bytes / (step_ms * 1e-3) / 1e9,
                             "tokens_per_s": N / (step_ms * 1e-3)}
         del state, steps_in, yd
+        torch.cuda.empty_cache()
+
+    # ---------------- multi-token decode: verify a 4-token draft block, commit ----------------
+    if not args.no_mtp:
+        c3 = CONFIGS[3]
+        N, H3, d3, K = c3["N"], c3["H"], c3["dk"], 4
+        log(f"multi-token decode: N={N} H={H3} d={d3}, {K}-token drafts")
+        state = to_dev(decode_initial_state(), False)
+        blocks = []
+        for r in range(4):
+            di = mtp_draft_inputs(r, K=K)
+            blocks.append(tuple(to_dev(di[n], True) for n in ("q", "k", "v"))
+                          + (to_dev(di["alpha"], False), to_dev(di["beta"], False)))
+        ym = torch.empty((N, K, H3, d3), dtype=torch.float32, device=dev)
+        em = torch.empty_like(ym)
+        all_acc = torch.full((N,), K, dtype=torch.int32, device=dev)
+        n_rounds = 200
+
+        def timed(fn):
+            for r in range(3):
+                fn(r)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for r in range(n_rounds):
+                fn(r)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n_rounds
+
+        def verify(r):
+            q_, k_, v_, a_, b_ = blocks[r % len(blocks)]
+            gdn.gdn_decode_mtp_verify(q_, k_, v_, a_, b_, state, y=ym, e=em, stream=stream)
+
+        def commit(r):
+            q_, k_, v_, a_, b_ = blocks[r % len(blocks)]
+            gdn.gdn_decode_mtp_commit(k_, a_, b_, em, all_acc, state, stream=stream)
+
+        def round_(r):
+            verify(r)
+            commit(r)
+        v_ms, c_ms, r_ms = timed(verify), timed(commit), timed(round_)
+        sb = N * H3 * d3 * d3 * 4
+        tok_io = N * H3 * K * (3 * d3 * 2 + 8)
+        v_bytes = sb + tok_io + 2 * N * H3 * K * d3 * 4                  # state, q/k/v/gates, y and e
+        c_bytes = 2 * sb + N * H3 * K * (d3 * 2 + 8 + d3 * 4)              # state in/out, k, gates, e
+        result["mtp"] = {"workload": f"multi-token decode, {N} sequences x {H3} heads, d={d3}, {K}-token drafts, "
+                                     "all accepted", "verify_us": v_ms * 1e3, "commit_us": c_ms * 1e3,
+                         "round_us": r_ms * 1e3,
+                         "verify_GBps": v_bytes / (v_ms * 1e-3) / 1e9,
+                         "verify_frac": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "commit_GBps": c_bytes / (c_ms * 1e-3) / 1e9,
+                         "commit_frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "tokens_per_s": N * K / (r_ms * 1e-3)}
+        log(f"mtp verify {v_ms * 1e3:.1f} us ({v_bytes / (v_ms * 1e-3) / 1e9:.0f} GB/s), "
+            f"commit {c_ms * 1e3:.1f} us ({c_bytes / (c_ms * 1e-3) / 1e9:.0f} GB/s), round {r_ms * 1e3:.1f} us")
+        del state, blocks, ym, em
         torch.cuda.empty_cache()
 
     # ---------------- front end: projected streams -> q, k, v, alpha, beta ----------------

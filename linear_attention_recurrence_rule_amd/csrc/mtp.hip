@@ -46,9 +46,21 @@ __device__ __forceinline__ float4v fma4(float a, float4v x, float4v acc) {
     return float4v{acc.x + a * x.x, acc.y + a * x.y, acc.z + a * x.z, acc.w + a * x.w};
 }
 
+// Sum over the 16 lanes of a DPP row (quad permutations, then the half-row
+// and row mirrors); every lane of the row ends with the total.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));  // row_mirror
+    return x;
+}
+
 // KM: compile-time upper bound of the block length K (tokens K..KM-1 are
 // padding: zero q, k, v, alpha = 1, beta = 0, outputs not written).
-template <int DK, int DV, int KM, bool kBf16>
+// kPrefix: also write every prefix state (keeps the state slice in registers
+// to the end; without it the slice dies after the column sums).
+template <int DK, int DV, int KM, bool kBf16, bool kPrefix>
 __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ state,
@@ -56,6 +68,8 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
     float scale) {
     using Sh = MtpShape<DK, DV>;
     constexpr int KQ = 2 * KM;                 // k_0..k_{KM-1}, q_0..q_{KM-1}
+    constexpr int kIn = (KQ * DK + Sh::kThreads - 1) / Sh::kThreads;
+    constexpr int kVin = (KM * Sh::kColGroups + Sh::kThreads - 1) / Sh::kThreads;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int cg = tid % Sh::kColGroups;
@@ -63,11 +77,46 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
     const int nh = blockIdx.x;
     const int n = nh / H, h = nh - n * H;
 
-    // the whole state slice of this thread first, so the loads overlap the set-up below
+    // the block's q, k, v and gates first: the set-up below then waits only
+    // for these, while the state stream issued after them is still in flight.
+    // Token t of the block, head h, is row ((n K + t) H + h).  Every load is
+    // unconditional (indices clamped into the block, padding selected to zero
+    // afterwards) so that no branch makes the compiler wait for each load.
+    float xin[kIn];
+#pragma unroll
+    for (int m = 0; m < kIn; ++m) {
+        const int i = tid + m * Sh::kThreads;
+        const int ic = i < KQ * DK ? i : KQ * DK - 1;
+        const int t2 = ic / DK, r = ic - t2 * DK;
+        const int t = t2 < KM ? t2 : t2 - KM;
+        const int tc = t < K ? t : K - 1;
+        const float x = load_in<kBf16>(t2 < KM ? k : q, (static_cast<long>(n * K + tc) * H + h) * DK + r);
+        xin[m] = t < K ? x : 0.f;
+    }
+    float4v vin[kVin];
+#pragma unroll
+    for (int m = 0; m < kVin; ++m) {
+        const int i = tid + m * Sh::kThreads;
+        const int ic = i < KM * Sh::kColGroups ? i : KM * Sh::kColGroups - 1;
+        const int t = ic / Sh::kColGroups, c = ic - t * Sh::kColGroups;
+        const int tc = t < K ? t : K - 1;
+        const long b = (static_cast<long>(n * K + tc) * H + h) * DV + 4 * c;
+        const float4v x = float4v{load_in<kBf16>(v, b), load_in<kBf16>(v, b + 1), load_in<kBf16>(v, b + 2),
+                                  load_in<kBf16>(v, b + 3)};
+        vin[m] = t < K ? x : float4v{0.f, 0.f, 0.f, 0.f};
+    }
+    const int tg = tid < K ? tid : K - 1;
+    const long g = static_cast<long>(n * K + tg) * H + h;
+    const float a_ld = alpha[g], b_ld = beta[g];
+    const float ain = tid < K ? a_ld : 1.f;
+    const float bin = tid < K ? b_ld : 0.f;
+
+    // the state slice of this thread: a read-once stream
     const float4v* S = reinterpret_cast<const float4v*>(state + static_cast<long>(nh) * DK * DV);
     float4v s[Sh::kRpt];
 #pragma unroll
-    for (int j = 0; j < Sh::kRpt; ++j) s[j] = S[(rg + j * Sh::kRowGroups) * Sh::kColGroups + cg];
+    for (int j = 0; j < Sh::kRpt; ++j)
+        s[j] = __builtin_nontemporal_load(&S[(rg + j * Sh::kRowGroups) * Sh::kColGroups + cg]);
 
     __shared__ __align__(16) float skq[DK][KQ];                    // row r: k_t[r] then q_t[r]
     __shared__ float4v sv[KM][Sh::kColGroups];
@@ -75,43 +124,44 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
     __shared__ float skk[KM][KM], sqk[KM][KM];                     // k_i.k_t (i < t), k_i.q_t (i <= t)
     __shared__ float sa[KM], sb[KM];
 
-    // token t of the block, head h: row ((n K + t) H + h)
-    for (int i = tid; i < KQ * DK; i += Sh::kThreads) {
+#pragma unroll
+    for (int m = 0; m < kIn; ++m) {
+        const int i = tid + m * Sh::kThreads;
         const int t2 = i / DK, r = i - t2 * DK;
-        const int t = t2 < KM ? t2 : t2 - KM;
-        float x = 0.f;
-        if (t < K) x = load_in<kBf16>(t2 < KM ? k : q, (static_cast<long>(n * K + t) * H + h) * DK + r);
-        skq[r][t2] = x;
+        if (i < KQ * DK) skq[r][t2] = xin[m];
     }
-    for (int i = tid; i < KM * Sh::kColGroups; i += Sh::kThreads) {
+#pragma unroll
+    for (int m = 0; m < kVin; ++m) {
+        const int i = tid + m * Sh::kThreads;
         const int t = i / Sh::kColGroups, c = i - t * Sh::kColGroups;
-        float4v x = {0.f, 0.f, 0.f, 0.f};
-        if (t < K) {
-            const long b = (static_cast<long>(n * K + t) * H + h) * DV + 4 * c;
-            x = float4v{load_in<kBf16>(v, b), load_in<kBf16>(v, b + 1), load_in<kBf16>(v, b + 2),
-                        load_in<kBf16>(v, b + 3)};
-        }
-        sv[t][c] = x;
+        if (i < KM * Sh::kColGroups) sv[t][c] = vin[m];
     }
     if (tid < KM) {
-        const bool live = tid < K;
-        const long g = static_cast<long>(n * K + tid) * H + h;
-        sa[tid] = live ? alpha[g] : 1.f;
-        sb[tid] = live ? beta[g] : 0.f;
+        sa[tid] = ain;
+        sb[tid] = bin;
     }
     __syncthreads();
 
-    // K x K dot products of the block, one wave-wide sum each: pair (a, b)
-    // gives k_a.k_b when a < b and k_b.q_a when a >= b
-    for (int d = wave; d < KM * KM; d += Sh::kWaves) {
-        const int a = d / KM, b = d - a * KM;
-        float x = 0.f;
-        for (int r = lane; r < DK; r += 64)
-            x += a < b ? skq[r][a] * skq[r][b] : skq[r][b] * skq[r][KM + a];
-        x = wave_sum(x);
-        if (lane == 0) {
-            if (a < b) skk[a][b] = x;
-            else sqk[b][a] = x;
+    // K x K dot products of the block, 16 lanes each: pair (a, b) gives
+    // k_a.k_b when a < b and k_b.q_a when a >= b
+    {
+        constexpr int kGroups = Sh::kThreads / 16;
+        const int grp = tid >> 4, sub = tid & 15;
+#pragma unroll
+        for (int d0 = 0; d0 < KM * KM; d0 += kGroups) {
+            const int d = d0 + grp;
+            const int a = d / KM, b = d - a * KM;
+            const int c0 = a < b ? a : b, c1 = a < b ? b : KM + a;
+            float x = 0.f;
+            if (d < KM * KM) {
+#pragma unroll
+                for (int r = sub; r < DK; r += 16) x += skq[r][c0] * skq[r][c1];
+            }
+            x = row16_sum(x);
+            if (sub == 0 && d < KM * KM) {
+                if (a < b) skk[a][b] = x;
+                else sqk[b][a] = x;
+            }
         }
     }
 
@@ -185,7 +235,7 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
     }
 
     // optional prefix states S_t = alpha_t S_{t-1} + k_t u_t^T
-    if (prefix) {
+    if constexpr (kPrefix) {
 #pragma unroll
         for (int t = 0; t < KM; ++t) {
             if (t < K) {
@@ -259,9 +309,12 @@ static hipError_t launch_mtp_t(const MtpArgs& a) {
     if (a.commit)
         hipLaunchKernelGGL((mtp_commit_kernel<DK, DV, KM, kBf16>), grid, block, 0, a.stream, a.k, a.alpha,
                            a.beta, a.e, a.accepted, a.state, a.K, a.H);
+    else if (a.prefix)
+        hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16, true>), grid, block, 0, a.stream, a.q, a.k,
+                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale);
     else
-        hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16>), grid, block, 0, a.stream, a.q, a.k, a.v,
-                           a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale);
+        hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16, false>), grid, block, 0, a.stream, a.q, a.k,
+                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale);
     return hipGetLastError();
 }
 
