@@ -13,7 +13,8 @@ paper.rainbus.top digest (method step (1)); the front end (short causal
 convolutions, SiLU, L2 normalisation and the gates) follows the
 parameterisation block of the same Module A; multi-token (speculative)
 decode is the same recurrence over a block of draft tokens, with a commit step
-that advances the live state by the accepted prefix only.
+that advances the live state by the accepted prefix only; the backward is the
+chain rule through the same recurrence, written out step by step in reverse.
 """
 
 from .gdn_ref import (  # noqa: F401
@@ -24,3 +25,4 @@ from .gdn_ref import (  # noqa: F401
 )
 from .frontend_ref import gdn_frontend, short_conv, silu, l2norm  # noqa: F401
 from .mtp_ref import mtp_verify, mtp_commit  # noqa: F401
+from .bwd_ref import gated_delta_backward  # noqa: F401
