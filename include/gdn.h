@@ -165,6 +165,41 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
                             gdn_dtype io_dtype, float norm_eps, void* hip_stream);
 
 /*
+ * Backward of gdn_prefill_fwd (the chain rule through the delta form of the
+ * slinene page, Module A; the pages mention a backward kernel only as part
+ * of the FlashQLA library).  For the loss L = sum <dy, y> + <d_final_state,
+ * final_state> it returns the gradients with respect to q, k, v, alpha, beta
+ * and the initial state, evaluated in 64-token chunks.
+ *
+ *   q, k, v, alpha, beta, initial_state   as for gdn_prefill_fwd (initial_state NULL = zeros)
+ *   dy             [B, T, H, d_v]  float32, the gradient of y
+ *   d_final_state  [B, H, d_k, d_v] float32 or NULL (zero)
+ *   dq, dk         [B, T, H, d_k]  float32 out
+ *   dv             [B, T, H, d_v]  float32 out
+ *   dalpha, dbeta  [B, T, H]       float32 out (dalpha is 0 where log(alpha)
+ *                                  is below the forward's floor of -30)
+ *   d_initial_state [B, H, d_k, d_v] float32 out, or NULL (not written)
+ *   workspace      caller-owned device memory of at least
+ *                  gdn_prefill_bwd_workspace_bytes(...) bytes, 16-byte aligned
+ *                  (per 64-token chunk and head: the chunk's T, P and M
+ *                  matrices, its start state and end-state gradient, and two
+ *                  64 x d_v products, all float32)
+ *   d_k == d_v in {16, 32, 64, 128}.  With T == 0 only d_initial_state is
+ *   written (a copy of d_final_state, or zeros); no workspace is needed.
+ */
+gdn_status gdn_prefill_bwd(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* initial_state,
+                           const float* dy, const float* d_final_state,
+                           float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                           float* d_initial_state,
+                           int B, int T, int H, int d_k, int d_v,
+                           gdn_dtype qkv_dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes gdn_prefill_bwd needs (0 for T == 0 or invalid arguments). */
+size_t gdn_prefill_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype);
+
+/*
  * Multi-token (speculative) decode, part 1: verify a block of K draft tokens
  * per sequence from the live states (rainbus digest, inference section:
  * multi-token prediction drafts, the target model verifies; each draft token

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
     "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
-    "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit", "gdn_status_string",
+    "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit",
+    "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_status_string",
 ]
 
 GDN_F32 = 0
@@ -67,6 +68,11 @@ def load_library():
     lib.gdn_decode_mtp_verify.restype = ctypes.c_int
     lib.gdn_decode_mtp_commit.argtypes = [vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, vp]
     lib.gdn_decode_mtp_commit.restype = ctypes.c_int
+    lib.gdn_prefill_bwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                    i, i, i, i, i, i, f, vp, sz, vp]
+    lib.gdn_prefill_bwd.restype = ctypes.c_int
+    lib.gdn_prefill_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gdn_prefill_bwd_workspace_bytes.restype = sz
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -299,3 +305,55 @@ def gdn_decode_mtp_commit(k, alpha, beta, e, accepted, state, stream=None):
     if st:
         raise GdnError(st, "gdn_decode_mtp_commit")
     return state
+
+
+def gdn_prefill_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype):
+    """Scratch bytes gdn_prefill_bwd needs (dtype: torch.bfloat16 or torch.float32)."""
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(load_library().gdn_prefill_bwd_workspace_bytes(B, T, H, d_k, d_v, code))
+
+
+def gdn_prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, d_final_state=None, scale=1.0,
+                    need_d_initial_state=True, workspace=None, out=None, stream=None):
+    """Gradients of sum <dy, y> + <d_final_state, final_state> for gdn_prefill_fwd.
+    q, k [B, T, H, d]; v [B, T, H, d] (bf16 or fp32, one dtype); alpha, beta
+    [B, T, H] fp32; dy [B, T, H, d] fp32; initial_state, d_final_state
+    [B, H, d, d] fp32 or None.  Returns (dq, dk, dv, dalpha, dbeta,
+    d_initial_state or None), all fp32.  ``out`` may hold preallocated tensors
+    in that order."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(dy, "dy", (B, T, H, dv), torch.float32, dev)
+    _check(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
+    _check(d_final_state, "d_final_state", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = (torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32),
+               torch.empty((B, T, H, dv), **f32), torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32),
+               torch.empty((B, H, dk, dv), **f32) if need_d_initial_state else None)
+    dq, dk_, dv_, da, db, dS0 = out
+    _check(dq, "dq", (B, T, H, dk), torch.float32, dev)
+    _check(dk_, "dk", (B, T, H, dk), torch.float32, dev)
+    _check(dv_, "dv", (B, T, H, dv), torch.float32, dev)
+    _check(da, "dalpha", (B, T, H), torch.float32, dev)
+    _check(db, "dbeta", (B, T, H), torch.float32, dev)
+    _check(dS0, "d_initial_state", (B, H, dk, dv), torch.float32, dev)
+    code = _dtype_code(q)
+    need = int(lib.gdn_prefill_bwd_workspace_bytes(B, T, H, dk, dv, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(dy),
+                             _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(da), _ptr(db), _ptr(dS0),
+                             B, T, H, dk, dv, code, float(scale), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_prefill_bwd")
+    return dq, dk_, dv_, da, db, dS0

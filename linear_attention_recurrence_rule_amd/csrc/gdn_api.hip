@@ -134,6 +134,49 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
 
 namespace {
 
+gdn_status bwd_check(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
+    if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
+    if (B <= 0 || H <= 0 || T < 0) return GDN_ERR_SHAPE;
+    if (!head_size_ok(d_k) || d_k != d_v) return GDN_ERR_UNSUPPORTED;
+    if (!fits(B, T, H, 128) || static_cast<long long>(B) * H > 65535 || (T + 63) / 64 > 65535)
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+size_t gdn_prefill_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
+    if (bwd_check(B, T, H, d_k, d_v, qkv_dtype) != GDN_OK || T == 0) return 0;
+    return gdn::prefill_bwd_workspace_bytes(B, T, H, d_k, d_v);
+}
+
+gdn_status gdn_prefill_bwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                           const float* initial_state, const float* dy, const float* d_final_state, float* dq,
+                           float* dk, float* dv, float* dalpha, float* dbeta, float* d_initial_state, int B, int T,
+                           int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = bwd_check(B, T, H, d_k, d_v, qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !dy || !dq || !dk || !dv || !dalpha || !dbeta))
+        return GDN_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(initial_state), static_cast<const void*>(dy),
+                          static_cast<const void*>(d_final_state), static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv),
+                          static_cast<const void*>(dalpha), static_cast<const void*>(dbeta),
+                          static_cast<const void*>(d_initial_state)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = T == 0 ? 0 : gdn::prefill_bwd_workspace_bytes(B, T, H, d_k, d_v);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return GDN_ERR_ALIGN;
+    gdn::PrefillBwdArgs a{q, k, v, alpha, beta, initial_state, dy, d_final_state, dq, dk, dv, dalpha, dbeta,
+                          d_initial_state, B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale, workspace,
+                          static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_prefill_bwd(a));
+}
+
+namespace {
+
 gdn_status mtp_check(int N, int K, int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
     if (!dtype_ok(qkv_dtype)) return GDN_ERR_DTYPE;
     if (N < 0 || K < 0 || H <= 0) return GDN_ERR_SHAPE;

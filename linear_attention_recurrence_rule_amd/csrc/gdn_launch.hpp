@@ -91,6 +91,28 @@ struct MtpArgs {
     hipStream_t stream;
 };
 
+struct PrefillBwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* initial_state;  // may be null (zero state)
+    const float* dy;             // [B, T, H, d_v]
+    const float* d_final_state;  // may be null (zero)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dalpha;
+    float* dbeta;
+    float* d_initial_state;      // may be null (not written)
+    int B, T, H, dk_, dv_;
+    bool bf16;
+    float scale;
+    void* workspace;             // prefill_bwd_workspace_bytes
+    hipStream_t stream;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
@@ -98,5 +120,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_mtp(const MtpArgs& a);
+hipError_t launch_prefill_bwd(const PrefillBwdArgs& a);
+size_t prefill_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
 
 }  // namespace gdn

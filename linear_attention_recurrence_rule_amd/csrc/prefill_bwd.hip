@@ -1,0 +1,806 @@
+// Chunked backward of the gated delta rule on gfx950.
+//
+// The forward is the delta form of the slinene ai-papers-daily page on
+// "On the Design of Qwen3.8-Next Architecture" (Module A), evaluated in
+// chunks of C = 64 tokens (UT form):
+//     g = in-chunk cumsum of log alpha,  gamma = exp(g),  lam_t = exp(g_n - g_t)
+//     T = (I + A)^-1,  A_ti = beta_t Gamma_ti k_t.k_i (i < t) = beta_t M_ti
+//     E = T diag(beta) (V - diag(gamma) K S)
+//     Y = scale (diag(gamma) Q S + P E),  P_ti = Gamma_ti q_t.k_i (i <= t)
+//     S' = gamma_n S + K^T diag(lam) E
+// The backward applies the chain rule to these chunk equations in four
+// passes (the pages only mention a backward kernel as part of the FlashQLA
+// library; this is the plain reverse-mode derivation):
+//   1. prep (chunk-parallel): g, T, P and M per chunk.
+//   2. states (sequential over chunks, per 16-column slice of the state):
+//      the chunk-start states S_c and the chunk products E_c.
+//   3. reverse states (sequential, reverse order, per slice): the gradient of
+//      each chunk's end state dS'_c, and with it
+//          dE = scale P^T dY + diag(lam) K dS',   dR = T^T dE,   dV = diag(beta) dR
+//          dS = gamma_n dS' + scale Q^T diag(gamma) dY - K^T diag(beta gamma) dR
+//   4. gradients (chunk-parallel): with X1 = dY S^T, X2 = dR S^T, X3 = E dS'^T,
+//      X4 = dY E^T, X5 = dR E^T,  dP = scale X4 (i <= t),  dA = -X5 (i < t):
+//          dq = scale gamma X1 + (dP o Gamma) K
+//          dk = lam X3 - beta gamma X2 + (Dm + Dm^T) K + (dP o Gamma)^T Q,
+//               Dm_ti = beta_t dA_ti Gamma_ti
+//          dbeta_t = dR_t.v_t - gamma_t k_t.X2_t + sum_i dA_ti M_ti
+//          dg_t = gamma_t (scale q_t.X1_t - beta_t k_t.X2_t) + rows/cols of dP o P
+//                 and dA o A - lam_t k_t.X3_t  (+ the chunk-end terms at t = n)
+//          dalpha_s = (sum_{t >= s} dg_t) / alpha_s.
+// Every contraction is an fp32 MFMA (16x16x4) on LDS tiles; the workspace
+// holds the per-chunk matrices and states in fp32.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace bwd {
+
+constexpr int C = 64;
+constexpr float kLogFloor = -30.f;   // same floor of log(alpha) as the forward
+
+// acc += A * B for one 16x16 tile, A (16 x K) read transposed from At
+// (At[k][r] = A[r][k], leading dimension lda), B given as Bt (16 x K, row-major).
+__device__ __forceinline__ float4v mma_at(const float* At, int lda, const float* Bt, int ldb, int k0, int k1,
+                                          float4v acc) {
+    const int l = threadIdx.x & 63;
+    for (int k = k0; k < k1; k += 4) {
+        const float a = At[(k + (l >> 4)) * lda + (l & 15)];
+        const float b = Bt[(l & 15) * ldb + k + (l >> 4)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// acc += (A + A^T) * B with A read both ways from the same row-major storage.
+__device__ __forceinline__ float4v mma_sym(const float* A, int lda, int r0, const float* Bt, int ldb, int k0,
+                                           int k1, float4v acc) {
+    const int l = threadIdx.x & 63;
+    for (int k = k0; k < k1; k += 4) {
+        const int r = r0 + (l & 15), kk = k + (l >> 4);
+        const float a = A[r * lda + kk] + A[kk * lda + r];
+        const float b = Bt[(l & 15) * ldb + k + (l >> 4)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float dpp_sum4(float x) {          // sum over a quad
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+__device__ __forceinline__ float dpp_sum8(float x) {          // sum over 8 consecutive lanes
+    x = dpp_sum4(x);
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_sum16(float x) {         // sum over a row of 16 lanes
+    x = dpp_sum8(x);
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));
+}
+
+// Four consecutive elements (index i, a multiple of 4) of a float32 or bf16 array.
+template <bool kBf16>
+__device__ __forceinline__ float4v load4(const void* p, long i) {
+    if constexpr (kBf16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return float4v{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                       bf16_to_f32(u.y >> 16)};
+    } else {
+        return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
+    }
+}
+
+// Row tg of the chunk as 4 values at column c4*4 (zero past the sequence end;
+// the load itself is clamped so that it is always in bounds).
+template <bool kBf16>
+__device__ __forceinline__ float4v load_row4(const void* p, int b, int tg, int T, int H, int h, int D, int col) {
+    const int tc = tg < T ? tg : T - 1;
+    const float4v x = load4<kBf16>(p, ((static_cast<long>(b) * T + tc) * H + h) * D + col);
+    return tg < T ? x : float4v{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: gates, T, P and M of one chunk.  grid (nch, B*H), 256 threads.
+// ---------------------------------------------------------------------------
+template <int DK, bool kBf16>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ q, const void* __restrict__ k,
+                                                       const float* __restrict__ alpha,
+                                                       const float* __restrict__ beta, float* __restrict__ ws_g,
+                                                       float* __restrict__ ws_T, float* __restrict__ ws_P,
+                                                       float* __restrict__ ws_M, int T, int H, int nch) {
+    constexpr int LDK = DK + 4, LDA = C + 4;
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const long bhn = static_cast<long>(bh) * nch + c;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+
+    __shared__ __align__(16) float sQ[C * LDK];
+    __shared__ __align__(16) float sK[C * LDK];
+    __shared__ __align__(16) float sA[C * LDA];
+    __shared__ float sg[C], sb[C];
+
+    for (int i = tid; i < C * DK / 4; i += 256) {
+        const int t = i / (DK / 4), c4 = i - t * (DK / 4);
+        *reinterpret_cast<float4v*>(&sQ[t * LDK + 4 * c4]) = load_row4<kBf16>(q, b, c * C + t, T, H, h, DK, 4 * c4);
+        *reinterpret_cast<float4v*>(&sK[t * LDK + 4 * c4]) = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
+    }
+    if (wave == 0) {
+        const int tg = c * C + l;
+        const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
+        const float a = alpha[gi], be = beta[gi];
+        float x = tg < T ? fmaxf(__logf(a), kLogFloor) : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {             // inclusive prefix sum over the chunk
+            const float y = __shfl_up(x, off);
+            if (l >= off) x += y;
+        }
+        sg[l] = x;
+        sb[l] = tg < T ? be : 0.f;
+        ws_g[bhn * C + l] = x;
+    }
+    __syncthreads();
+
+    // Gram tiles: 16 of K K^T and 16 of Q K^T, the upper ones are zero
+    float* gP = ws_P + bhn * C * C;
+    float* gM = ws_M + bhn * C * C;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int p = wave * 4 + u, ti = p >> 2, tj = p & 3;
+        float4v kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+        if (tj <= ti) {
+            kk = Mma<float>::range(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, kk);
+            qk = Mma<float>::range(&sQ[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, qk);
+        }
+        const int col = 16 * tj + (l & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * ti + 4 * (l >> 4) + j;
+            const float gam = row >= col ? __expf(sg[row] - sg[col]) : 0.f;
+            const float m = row > col ? gam * kk[j] : 0.f;
+            const float pv = row >= col ? gam * qk[j] : 0.f;
+            gM[row * C + col] = m;
+            gP[row * C + col] = pv;
+            sA[row * LDA + col] = sb[row] * m;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 by forward substitution, one column per quad of lanes:
+    // T[t][j] = [t == j] - sum_{i<t} A[t][i] T[i][j]; lane `part` of the quad
+    // keeps the rows i = part (mod 4) of its column in registers.
+    const int j = tid >> 2, part = tid & 3;
+    float tcol[C / 4];
+#pragma unroll
+    for (int m = 0; m < C / 4; ++m) tcol[m] = 0.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < (t + 3) / 4; ++m) {
+            const int i = 4 * m + part;
+            if (i < t) s += sA[t * LDA + i] * tcol[m];
+        }
+        s = dpp_sum4(s);
+        const float v = (t == j ? 1.f : 0.f) - s;
+        if (part == (t & 3)) tcol[t >> 2] = v;
+    }
+    float* gT = ws_T + bhn * C * C;
+#pragma unroll
+    for (int m = 0; m < C / 4; ++m) gT[(4 * m + part) * C + j] = tcol[m];
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: chunk-start states and E, walking the chunks forward.
+// grid (DV / 16, B*H), 256 threads; the 16-column slice of S lives in the
+// accumulators of the waves that own its row blocks.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool kBf16>
+__global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ S0,
+                                                         const float* __restrict__ ws_g,
+                                                         const float* __restrict__ ws_T, float* __restrict__ ws_S,
+                                                         float* __restrict__ ws_E, int T, int H, int nch) {
+    constexpr int SV = 16, LDKT = C + 4, LDT = C + 4, LDS_ = DK + 4, LDR = C + 4;
+    constexpr int NST = DK / 16;                       // state row blocks
+    constexpr int SPW = (NST + 3) / 4;                 // state row blocks per wave
+    const int slice = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int col0 = slice * SV;
+
+    __shared__ __align__(16) float sKT[DK * LDKT];     // K^T of the chunk
+    __shared__ __align__(16) float sT[C * LDT];
+    __shared__ __align__(16) float sSt[SV * LDS_];     // S^T (the slice)
+    __shared__ __align__(16) float sRt[SV * LDR];      // R^T
+    __shared__ __align__(16) float sEt[SV * LDR];      // (lam E)^T
+    __shared__ float sV[C][SV];
+    __shared__ float sg[C], sb[C];
+
+    float4v st[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int m = wave + 4 * u;
+        st[u] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (m < NST && S0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                st[u][j] = S0[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
+        }
+        if (m < NST) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = st[u][j];
+        }
+    }
+
+    for (int c = 0; c < nch; ++c) {
+        const long bhn = static_cast<long>(bh) * nch + c;
+        // chunk-start state out
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int m = wave + 4 * u;
+            if (m < NST) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ws_S[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = st[u][j];
+            }
+        }
+        for (int i = tid; i < C * DK / 4; i += 256) {
+            const int t = i / (DK / 4), c4 = i - t * (DK / 4);
+            const float4v x = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sKT[(4 * c4 + e) * LDKT + t] = x[e];
+        }
+        for (int i = tid; i < C * C / 4; i += 256) {
+            const int t = i / (C / 4), c4 = i - t * (C / 4);
+            *reinterpret_cast<float4v*>(&sT[t * LDT + 4 * c4]) =
+                *reinterpret_cast<const float4v*>(&ws_T[bhn * C * C + t * C + 4 * c4]);
+        }
+        {
+            const int t = tid >> 2, c4 = tid & 3;
+            const float4v x = load_row4<kBf16>(v, b, c * C + t, T, H, h, DV, col0 + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sV[t][4 * c4 + e] = x[e];
+        }
+        if (tid < C) {
+            const int tg = c * C + tid;
+            sg[tid] = ws_g[bhn * C + tid];
+            sb[tid] = tg < T ? beta[(static_cast<long>(b) * T + tg) * H + h] : 0.f;
+        }
+        __syncthreads();
+
+        // R = diag(beta) (V - diag(gamma) K S), one row block per wave
+        {
+            float4v ks = {0.f, 0.f, 0.f, 0.f};
+            ks = mma_at(&sKT[16 * wave], LDKT, sSt, LDS_, 0, DK, ks);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * wave + 4 * (l >> 4) + j;
+                sRt[(l & 15) * LDR + r] = sb[r] * (sV[r][l & 15] - __expf(sg[r]) * ks[j]);
+            }
+        }
+        __syncthreads();
+        // E = T R (T lower triangular), written out; (lam E)^T kept for the update
+        {
+            float4v e = {0.f, 0.f, 0.f, 0.f};
+            e = Mma<float>::range(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, 16 * (wave + 1), e);
+            const float gn = sg[C - 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * wave + 4 * (l >> 4) + j;
+                ws_E[(bhn * C + r) * DV + col0 + (l & 15)] = e[j];
+                sEt[(l & 15) * LDR + r] = __expf(gn - sg[r]) * e[j];
+            }
+        }
+        __syncthreads();
+        // S' = gamma_n S + K^T (lam E)
+        {
+            const float gam_n = __expf(sg[C - 1]);
+#pragma unroll
+            for (int u = 0; u < SPW; ++u) {
+                const int m = wave + 4 * u;
+                if (m < NST) {
+                    float4v acc = gam_n * st[u];
+                    acc = Mma<float>::range(&sKT[16 * m * LDKT], LDKT, sEt, LDR, 0, C, acc);
+                    st[u] = acc;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = acc[j];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: state gradients, walking the chunks backward.  grid (DV / 16, B*H).
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool kBf16>
+__global__ __launch_bounds__(256) void bwd_dstates_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ dy, const float* __restrict__ dST, const float* __restrict__ ws_g,
+    const float* __restrict__ ws_T, const float* __restrict__ ws_P, float* __restrict__ ws_dS,
+    float* __restrict__ ws_dR, float* __restrict__ dv_out, float* __restrict__ dS0, int T, int H, int nch,
+    float scale) {
+    constexpr int SV = 16, LDX = C + 4, LDS_ = DK + 4;
+    constexpr int NST = DK / 16, SPW = (NST + 3) / 4;
+    const int slice = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int col0 = slice * SV;
+
+    __shared__ __align__(16) float sQT[DK * LDX];
+    __shared__ __align__(16) float sKT[DK * LDX];
+    __shared__ __align__(16) float sT[C * LDX];
+    __shared__ __align__(16) float sP[C * LDX];
+    __shared__ __align__(16) float sdYt[SV * LDX];     // dY^T
+    __shared__ __align__(16) float sB1t[SV * LDX];     // (scale gamma dY)^T
+    __shared__ __align__(16) float sB2t[SV * LDX];     // (-beta gamma dR)^T
+    __shared__ __align__(16) float sdEt[SV * LDX];     // dE^T
+    __shared__ __align__(16) float sdSt[SV * LDS_];    // dS'^T
+    __shared__ float sg[C], sb[C];
+
+    float4v ds[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int m = wave + 4 * u;
+        ds[u] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (m < NST && dST) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ds[u][j] = dST[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
+        }
+        if (m < NST) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
+        }
+    }
+
+    for (int c = nch - 1; c >= 0; --c) {
+        const long bhn = static_cast<long>(bh) * nch + c;
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int m = wave + 4 * u;
+            if (m < NST) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ws_dS[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[u][j];
+            }
+        }
+        for (int i = tid; i < C * DK / 4; i += 256) {
+            const int t = i / (DK / 4), c4 = i - t * (DK / 4);
+            const float4v xq = load_row4<kBf16>(q, b, c * C + t, T, H, h, DK, 4 * c4);
+            const float4v xk = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sQT[(4 * c4 + e) * LDX + t] = xq[e];
+                sKT[(4 * c4 + e) * LDX + t] = xk[e];
+            }
+        }
+        for (int i = tid; i < C * C / 4; i += 256) {
+            const int t = i / (C / 4), c4 = i - t * (C / 4);
+            *reinterpret_cast<float4v*>(&sT[t * LDX + 4 * c4]) =
+                *reinterpret_cast<const float4v*>(&ws_T[bhn * C * C + t * C + 4 * c4]);
+            *reinterpret_cast<float4v*>(&sP[t * LDX + 4 * c4]) =
+                *reinterpret_cast<const float4v*>(&ws_P[bhn * C * C + t * C + 4 * c4]);
+        }
+        {
+            const int t = tid >> 2, c4 = tid & 3, tg = c * C + t;
+            const int tc = tg < T ? tg : T - 1;
+            float4v x = *reinterpret_cast<const float4v*>(&dy[((static_cast<long>(b) * T + tc) * H + h) * DV + col0 + 4 * c4]);
+            if (tg >= T) x = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sdYt[(4 * c4 + e) * LDX + t] = x[e];
+        }
+        if (tid < C) {
+            const int tg = c * C + tid;
+            sg[tid] = ws_g[bhn * C + tid];
+            sb[tid] = tg < T ? beta[(static_cast<long>(b) * T + tg) * H + h] : 0.f;
+        }
+        __syncthreads();
+
+        // dE = scale P^T dY + diag(lam) K dS'  (P^T upper triangular)
+        {
+            float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+            a1 = mma_at(&sP[16 * wave], LDX, sdYt, LDX, 16 * wave, C, a1);
+            a2 = mma_at(&sKT[16 * wave], LDX, sdSt, LDS_, 0, DK, a2);
+            const float gn = sg[C - 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * wave + 4 * (l >> 4) + j;
+                sdEt[(l & 15) * LDX + r] = scale * a1[j] + __expf(gn - sg[r]) * a2[j];
+            }
+        }
+        for (int i = tid; i < SV * C; i += 256) {
+            const int cc = i / C, t = i - cc * C;
+            sB1t[cc * LDX + t] = scale * __expf(sg[t]) * sdYt[cc * LDX + t];
+        }
+        __syncthreads();
+        // dR = T^T dE; dV = diag(beta) dR
+        {
+            float4v r = {0.f, 0.f, 0.f, 0.f};
+            r = mma_at(&sT[16 * wave], LDX, sdEt, LDX, 16 * wave, C, r);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * wave + 4 * (l >> 4) + j, tg = c * C + t;
+                ws_dR[(bhn * C + t) * DV + col0 + (l & 15)] = r[j];
+                if (tg < T) dv_out[((static_cast<long>(b) * T + tg) * H + h) * DV + col0 + (l & 15)] = sb[t] * r[j];
+                sB2t[(l & 15) * LDX + t] = -sb[t] * __expf(sg[t]) * r[j];
+            }
+        }
+        __syncthreads();
+        // dS = gamma_n dS' + Q^T (scale gamma dY) + K^T (-beta gamma dR)
+        {
+            const float gam_n = __expf(sg[C - 1]);
+#pragma unroll
+            for (int u = 0; u < SPW; ++u) {
+                const int m = wave + 4 * u;
+                if (m < NST) {
+                    float4v acc = gam_n * ds[u];
+                    acc = Mma<float>::range(&sQT[16 * m * LDX], LDX, sB1t, LDX, 0, C, acc);
+                    acc = Mma<float>::range(&sKT[16 * m * LDX], LDX, sB2t, LDX, 0, C, acc);
+                    ds[u] = acc;
+                }
+            }
+        }
+        __syncthreads();                       // every read of sdSt above is done
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int m = wave + 4 * u;
+            if (m < NST) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
+            }
+        }
+        __syncthreads();
+    }
+    if (dS0) {
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int m = wave + 4 * u;
+            if (m < NST) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dS0[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[u][j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4: per-chunk gradients dq, dk, dbeta, dalpha.  grid (nch, B*H), 512
+// threads.  d_k = d_v = D.
+// ---------------------------------------------------------------------------
+template <int D, bool kBf16>
+__global__ __launch_bounds__(512) void bwd_grads_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ dy,
+    const float* __restrict__ ws_g, const float* __restrict__ ws_P, const float* __restrict__ ws_M,
+    const float* __restrict__ ws_S, const float* __restrict__ ws_dS, const float* __restrict__ ws_E,
+    const float* __restrict__ ws_dR, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H, int nch, float scale) {
+    constexpr int SL = 16, LDL = SL + 4, LDX = C + 4;
+    constexpr int NB = D / 16;                      // column blocks of X1..X3
+    constexpr int NP = 4 * NB;                      // (row block, column block) pairs
+    constexpr int PPW = (NP + 7) / 8;               // pairs per wave
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const long bhn = static_cast<long>(bh) * nch + c;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+
+    // phase-1 slabs and phase-2 P, M share one region
+    constexpr int kSlabFloats = 4 * C * LDL + 2 * D * LDL;
+    constexpr int kPMFloats = 2 * C * LDX;
+    constexpr int kRegion = kSlabFloats > kPMFloats ? kSlabFloats : kPMFloats;
+    __shared__ __align__(16) float sR[kRegion];
+    __shared__ __align__(16) float sQT[D * LDX];
+    __shared__ __align__(16) float sKT[D * LDX];
+    __shared__ __align__(16) float sX4[C * LDX];    // X4, then dP o Gamma
+    __shared__ __align__(16) float sX5[C * LDX];    // X5, then Dm
+    __shared__ float sg[C], sb[C], sa[C];
+    __shared__ float sQX1[C], sKX2[C], sKX3[C], sDRv[C], sColPP[C], sColAA[C], sRowPP[C], sRowAA[C], sRowAM[C];
+    __shared__ float sSdS;
+
+    float* sdY = sR;
+    float* sdR = sR + C * LDL;
+    float* sE = sR + 2 * C * LDL;
+    float* sV = sR + 3 * C * LDL;
+    float* sS = sR + 4 * C * LDL;
+    float* sdS = sS + D * LDL;
+
+    float4v x1[PPW], x2[PPW], x3[PPW], x4[2], x5[2];
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) x1[u] = x2[u] = x3[u] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) x4[u] = x5[u] = float4v{0.f, 0.f, 0.f, 0.f};
+    float drv = 0.f, sds = 0.f;
+
+    for (int v0 = 0; v0 < D; v0 += SL) {
+        if (tid < C * SL / 4) {
+            const int t = tid >> 2, c4 = tid & 3, tg = c * C + t;
+            const int tc = tg < T ? tg : T - 1;
+            const long row = (static_cast<long>(b) * T + tc) * H + h;
+            float4v xdy = *reinterpret_cast<const float4v*>(&dy[row * D + v0 + 4 * c4]);
+            float4v xv = load4<kBf16>(v, row * D + v0 + 4 * c4);
+            if (tg >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
+            const float4v xdr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + t) * D + v0 + 4 * c4]);
+            const float4v xe = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + t) * D + v0 + 4 * c4]);
+            *reinterpret_cast<float4v*>(&sdY[t * LDL + 4 * c4]) = xdy;
+            *reinterpret_cast<float4v*>(&sdR[t * LDL + 4 * c4]) = xdr;
+            *reinterpret_cast<float4v*>(&sE[t * LDL + 4 * c4]) = xe;
+            *reinterpret_cast<float4v*>(&sV[t * LDL + 4 * c4]) = xv;
+            drv += xdr.x * xv.x + xdr.y * xv.y + xdr.z * xv.z + xdr.w * xv.w;
+        }
+        for (int i = tid; i < D * SL / 4; i += 512) {
+            const int r = i >> 2, c4 = i & 3;
+            const float4v xs = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + r) * D + v0 + 4 * c4]);
+            const float4v xd = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + r) * D + v0 + 4 * c4]);
+            *reinterpret_cast<float4v*>(&sS[r * LDL + 4 * c4]) = xs;
+            *reinterpret_cast<float4v*>(&sdS[r * LDL + 4 * c4]) = xd;
+            sds += xs.x * xd.x + xs.y * xd.y + xs.z * xd.z + xs.w * xd.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PPW; ++u) {
+            const int p = wave + 8 * u;
+            if (p < NP) {
+                const int ti = p / NB, tj = p - ti * NB;
+                x1[u] = Mma<float>::range(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x1[u]);
+                x2[u] = Mma<float>::range(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x2[u]);
+                x3[u] = Mma<float>::range(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, SL, x3[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
+            if (tj <= ti) {
+                x4[u] = Mma<float>::range(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x4[u]);
+                x5[u] = Mma<float>::range(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x5[u]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 2 ----
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * ti + 4 * (l >> 4) + j, col = 16 * tj + (l & 15);
+            sX4[row * LDX + col] = x4[u][j];
+            sX5[row * LDX + col] = x5[u][j];
+        }
+    }
+    float* sP = sR;
+    float* sM = sR + C * LDX;
+    for (int i = tid; i < C * C / 4; i += 512) {
+        const int t = i / (C / 4), c4 = i - t * (C / 4);
+        *reinterpret_cast<float4v*>(&sP[t * LDX + 4 * c4]) =
+            *reinterpret_cast<const float4v*>(&ws_P[bhn * C * C + t * C + 4 * c4]);
+        *reinterpret_cast<float4v*>(&sM[t * LDX + 4 * c4]) =
+            *reinterpret_cast<const float4v*>(&ws_M[bhn * C * C + t * C + 4 * c4]);
+    }
+    for (int i = tid; i < C * D / 4; i += 512) {
+        const int t = i / (D / 4), c4 = i - t * (D / 4);
+        const float4v xq = load_row4<kBf16>(q, b, c * C + t, T, H, h, D, 4 * c4);
+        const float4v xk = load_row4<kBf16>(k, b, c * C + t, T, H, h, D, 4 * c4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sQT[(4 * c4 + e) * LDX + t] = xq[e];
+            sKT[(4 * c4 + e) * LDX + t] = xk[e];
+        }
+    }
+    if (tid < C) {
+        const int tg = c * C + tid;
+        const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
+        const float a = alpha[gi], be = beta[gi];
+        sg[tid] = ws_g[bhn * C + tid];
+        sb[tid] = tg < T ? be : 0.f;
+        sa[tid] = tg < T ? a : 1.f;
+        sQX1[tid] = sKX2[tid] = sKX3[tid] = 0.f;
+    }
+    if (tid == 0) sSdS = 0.f;
+    // dR . v per row: 4 lanes per row hold the partial sums
+    {
+        const float s = dpp_sum4(drv);
+        if (tid < C * SL / 4 && (tid & 3) == 0) sDRv[tid >> 2] = s;
+    }
+    __syncthreads();
+    // <dS', S> over the whole block
+    {
+        float s = sds;
+        s = dpp_sum16(s);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (l == 0) atomicAdd(&sSdS, s);
+    }
+    // row scalars from X1..X3: q.X1, k.X2, k.X3
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int p = wave + 8 * u;
+        if (p < NP) {
+            const int ti = p / NB, tj = p - ti * NB, col = 16 * tj + (l & 15);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ti + 4 * (l >> 4) + j;
+                const float a1 = dpp_sum16(sQT[col * LDX + row] * x1[u][j]);
+                const float a2 = dpp_sum16(sKT[col * LDX + row] * x2[u][j]);
+                const float a3 = dpp_sum16(sKT[col * LDX + row] * x3[u][j]);
+                if ((l & 15) == 0) {
+                    atomicAdd(&sQX1[row], a1);
+                    atomicAdd(&sKX2[row], a2);
+                    atomicAdd(&sKX3[row], a3);
+                }
+            }
+        }
+    }
+    // column sums of dP o P and dA o A: lane group of 8 per column
+    {
+        const int i = tid >> 3, part = tid & 7;
+        float pp = 0.f, aa = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int t = 8 * part + m;
+            const float dP = i <= t ? scale * sX4[t * LDX + i] : 0.f;
+            const float dA = i < t ? -sX5[t * LDX + i] : 0.f;
+            pp += dP * sP[t * LDX + i];
+            aa += dA * sb[t] * sM[t * LDX + i];
+        }
+        pp = dpp_sum8(pp);
+        aa = dpp_sum8(aa);
+        if (part == 0) {
+            sColPP[i] = pp;
+            sColAA[i] = aa;
+        }
+    }
+    __syncthreads();
+    // row sums, and X4 -> dP o Gamma, X5 -> Dm in place
+    {
+        const int t = tid >> 3, part = tid & 7;
+        float pp = 0.f, aa = 0.f, am = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int i = 8 * part + m;
+            const float dP = i <= t ? scale * sX4[t * LDX + i] : 0.f;
+            const float dA = i < t ? -sX5[t * LDX + i] : 0.f;
+            const float gam = i <= t ? __expf(sg[t] - sg[i]) : 0.f;
+            const float mv = sM[t * LDX + i];
+            pp += dP * sP[t * LDX + i];
+            aa += dA * sb[t] * mv;
+            am += dA * mv;
+            sX4[t * LDX + i] = dP * gam;
+            sX5[t * LDX + i] = sb[t] * dA * gam;
+        }
+        pp = dpp_sum8(pp);
+        aa = dpp_sum8(aa);
+        am = dpp_sum8(am);
+        if (part == 0) {
+            sRowPP[t] = pp;
+            sRowAA[t] = aa;
+            sRowAM[t] = am;
+        }
+    }
+    __syncthreads();
+    // per-token scalars: dbeta, dg, then dlog(alpha) as a reverse cumsum
+    if (wave == 0) {
+        const int t = l, tg = c * C + t;
+        const float gam = __expf(sg[t]), lam = __expf(sg[C - 1] - sg[t]);
+        const float dgam = scale * sQX1[t] - sb[t] * sKX2[t];
+        const float dlam = sKX3[t];
+        const float db = sDRv[t] - gam * sKX2[t] + sRowAM[t];
+        float dg = gam * dgam + sRowPP[t] - sColPP[t] + sRowAA[t] - sColAA[t] - lam * dlam;
+        float tot = lam * dlam;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+        if (t == C - 1) dg += tot + gam * sSdS;
+        // reverse inclusive scan: dl_s = sum_{t >= s} dg_t
+        float x = dg;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(x, off);
+            if (t + off < 64) x += y;
+        }
+        if (tg < T) {
+            const long gi = (static_cast<long>(b) * T + tg) * H + h;
+            dbeta[gi] = db;
+            const float a = sa[t];
+            dalpha[gi] = __logf(a) >= kLogFloor ? x / a : 0.f;
+        }
+    }
+    // dq and dk tiles
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int p = wave + 8 * u;
+        if (p < NP) {
+            const int ti = p / NB, tj = p - ti * NB, col = 16 * tj + (l & 15);
+            float4v aq, ak;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ti + 4 * (l >> 4) + j;
+                const float gam = __expf(sg[row]), lam = __expf(sg[C - 1] - sg[row]);
+                aq[j] = scale * gam * x1[u][j];
+                ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
+            }
+            aq = Mma<float>::range(&sX4[16 * ti * LDX], LDX, &sKT[16 * tj * LDX], LDX, 0, 16 * (ti + 1), aq);
+            ak = mma_sym(sX5, LDX, 16 * ti, &sKT[16 * tj * LDX], LDX, 0, C, ak);
+            ak = mma_at(&sX4[16 * ti], LDX, &sQT[16 * tj * LDX], LDX, 16 * ti, C, ak);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ti + 4 * (l >> 4) + j, tg = c * C + row;
+                if (tg < T) {
+                    const long o = ((static_cast<long>(b) * T + tg) * H + h) * D + col;
+                    dq[o] = aq[j];
+                    dk[o] = ak[j];
+                }
+            }
+        }
+    }
+}
+
+// T == 0: the initial-state gradient is the final-state gradient (or zero).
+__global__ __launch_bounds__(256) void bwd_copy_state_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                             long n) {
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace bwd
+
+size_t prefill_bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
+    const size_t nch = (static_cast<size_t>(T) + bwd::C - 1) / bwd::C;
+    const size_t bhn = static_cast<size_t>(B) * H * nch;
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    return up(bhn * bwd::C * 4) + 3 * up(bhn * bwd::C * bwd::C * 4) + 2 * up(bhn * dk * dv * 4) +
+           2 * up(bhn * bwd::C * dv * 4);
+}
+
+template <int D, bool kBf16>
+static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
+    const int nch = (a.T + bwd::C - 1) / bwd::C;
+    const size_t bhn = static_cast<size_t>(a.B) * a.H * nch;
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    char* w = static_cast<char*>(a.workspace);
+    float* g = reinterpret_cast<float*>(w);            w += up(bhn * bwd::C * 4);
+    float* Tm = reinterpret_cast<float*>(w);           w += up(bhn * bwd::C * bwd::C * 4);
+    float* P = reinterpret_cast<float*>(w);            w += up(bhn * bwd::C * bwd::C * 4);
+    float* M = reinterpret_cast<float*>(w);            w += up(bhn * bwd::C * bwd::C * 4);
+    float* S = reinterpret_cast<float*>(w);            w += up(bhn * D * D * 4);
+    float* dS = reinterpret_cast<float*>(w);           w += up(bhn * D * D * 4);
+    float* E = reinterpret_cast<float*>(w);            w += up(bhn * bwd::C * D * 4);
+    float* dR = reinterpret_cast<float*>(w);
+    const dim3 gc(nch, a.B * a.H), gs(D / 16, a.B * a.H);
+    hipLaunchKernelGGL((bwd::bwd_prep_kernel<D, kBf16>), gc, dim3(256), 0, a.stream, a.q, a.k, a.alpha, a.beta,
+                       g, Tm, P, M, a.T, a.H, nch);
+    hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.k, a.v, a.beta,
+                       a.initial_state, g, Tm, S, E, a.T, a.H, nch);
+    hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.q, a.k, a.beta,
+                       a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, a.scale);
+    hipLaunchKernelGGL((bwd::bwd_grads_kernel<D, kBf16>), gc, dim3(512), 0, a.stream, a.q, a.k, a.v, a.alpha,
+                       a.beta, a.dy, g, P, M, S, dS, E, dR, a.dq, a.dk, a.dalpha, a.dbeta, a.T, a.H, nch, a.scale);
+    return hipGetLastError();
+}
+
+template <bool kBf16>
+static hipError_t launch_bwd_dt(const PrefillBwdArgs& a) {
+    if (a.dk_ != a.dv_) return hipErrorInvalidValue;
+    switch (a.dk_) {
+        case 16: return launch_bwd_t<16, kBf16>(a);
+        case 32: return launch_bwd_t<32, kBf16>(a);
+        case 64: return launch_bwd_t<64, kBf16>(a);
+        case 128: return launch_bwd_t<128, kBf16>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prefill_bwd(const PrefillBwdArgs& a) {
+    if (a.T == 0) {
+        if (!a.d_initial_state) return hipSuccess;
+        const long n = static_cast<long>(a.B) * a.H * a.dk_ * a.dv_;
+        hipLaunchKernelGGL(bwd::bwd_copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                           a.stream, a.d_final_state, a.d_initial_state, n);
+        return hipGetLastError();
+    }
+    return a.bf16 ? launch_bwd_dt<true>(a) : launch_bwd_dt<false>(a);
+}
+
+}  // namespace gdn

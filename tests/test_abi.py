@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gdn_decode_mtp_commit", "gdn_decode_mtp_verify", "gdn_decode_step",
-                                    "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_fwd",
+                                    "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_bwd",
+                                    "gdn_prefill_bwd_workspace_bytes", "gdn_prefill_fwd",
                                     "gdn_prefill_workspace_bytes", "gdn_status_string"]
 
 
@@ -238,3 +239,44 @@ def test_mtp_commit_rejects(kwargs, status):
 def test_mtp_commit_empty_is_a_no_op():
     assert _commit(N=0, s=None) == OK
     assert _commit(K=0, s=None) == OK
+
+
+def _bwd(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, dy=FAKE, dsT=None, dq=FAKE, dk=FAKE, dv=FAKE,
+         da=FAKE, db=FAKE, ds0=None, B=1, T=8, H=2, d_k=64, d_v=64, dtype=1, ws=FAKE, ws_bytes=1 << 40):
+    lib = gdn.load_library()
+    return lib.gdn_prefill_bwd(q, k, v, a, b, s0, dy, dsT, dq, dk, dv, da, db, ds0, B, T, H, d_k, d_v, dtype,
+                               1.0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), ERR_DTYPE),
+    (dict(B=0), ERR_SHAPE),
+    (dict(T=-1), ERR_SHAPE),
+    (dict(d_k=64, d_v=128), ERR_UNSUPPORTED),
+    (dict(d_k=48, d_v=48), ERR_UNSUPPORTED),
+    (dict(H=70000), ERR_UNSUPPORTED),
+    (dict(dy=None), ERR_NULL),
+    (dict(db=None), ERR_NULL),
+    (dict(ws=None), ERR_WORKSPACE),
+    (dict(ws_bytes=16), ERR_WORKSPACE),
+    (dict(dq=MISALIGNED), ERR_ALIGN),
+    (dict(ds0=MISALIGNED), ERR_ALIGN),
+    (dict(ws=MISALIGNED), ERR_ALIGN),
+])
+def test_bwd_rejects(kwargs, status):
+    assert _bwd(**kwargs) == status
+
+
+def test_bwd_workspace_bytes():
+    lib = gdn.load_library()
+    n = lib.gdn_prefill_bwd_workspace_bytes(1, 100, 2, 64, 64, 1)
+    # two chunks x two heads: g, T, P, M, S, dS', E, dR in float32
+    per = 64 * 4 + 3 * 64 * 64 * 4 + 2 * 64 * 64 * 4 + 2 * 64 * 64 * 4
+    assert n >= 4 * per
+    assert n < 4 * per + 8 * 256
+    assert lib.gdn_prefill_bwd_workspace_bytes(1, 0, 2, 64, 64, 1) == 0
+    assert lib.gdn_prefill_bwd_workspace_bytes(1, 100, 2, 64, 32, 1) == 0
+
+
+def test_bwd_empty_sequence_without_state_gradient_is_a_no_op():
+    assert _bwd(T=0, q=None, dy=None, dq=None, ws=None, ws_bytes=0) == OK
