@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=32K + decode state GB/s, as % of MI355X roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def log(msg):
@@ -48,6 +49,20 @@ def prefill_flops(B, T, H, dk, dv, C=64):
     three state products K S, Q S and K^T E; the diagonal-block inverse is
     left out)."""
     return B * T * H * (2 * 2 * C * dk + 2 * 2 * C * dv + 3 * 2 * dk * dv)
+
+
+def bwd_bytes(B, T, H, dk, dv, in_bytes=2):
+    """Algorithmic HBM bytes of one backward call: q, k, v, alpha, beta and dy
+    read once, dq, dk, dv (fp32), dalpha and dbeta written once."""
+    return B * T * H * ((2 * dk + dv) * in_bytes + 8 + 4 * dv + 4 * (2 * dk + dv) + 8)
+
+
+def bwd_flops(B, T, H, d, C=64):
+    """fp32 MFMA tile work of the four backward passes per token-head: the
+    C x d x d products (K S, K^T E, K dS', Q^T dY, K^T dR and the three X1..X3
+    contractions over d_v) and the C x C x d ones (the two Gram products, T R,
+    P^T dY, T^T dE, X4, X5 and the four C x C by C x d products of dq, dk)."""
+    return B * T * H * 2 * (8 * d * d + 11 * C * d)
 
 
 def norm_bytes(rows, dv, in_bytes=2):
@@ -103,6 +118,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-mtp", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -245,6 +261,49 @@ def main():
                             "all_bytes_GBps": all_bytes / (step_ms * 1e-3) / 1e9,
                             "tokens_per_s": N / (step_ms * 1e-3)}
         del state, steps_in, yd
+        torch.cuda.empty_cache()
+
+    # ---------------- backward of the prefill on the same workload ----------------
+    if not args.no_bwd:
+        log(f"backward: B={B} T={T} H={H} d={dk}")
+        d = config_prefill_inputs(2)
+        q, k, v = (to_dev(d[n], True) for n in ("q", "k", "v"))
+        alpha, beta = to_dev(d["alpha"], False), to_dev(d["beta"], False)
+        del d
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        dy = torch.randn((B, T, H, dv), generator=gen, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        outs = (torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32),
+                torch.empty((B, T, H, dv), **f32), torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32),
+                torch.empty((B, H, dk, dv), **f32))
+        ws = torch.empty(gdn.gdn_prefill_bwd_workspace_bytes(B, T, H, dk, dv, torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+
+        def bwd_call():
+            gdn.gdn_prefill_bwd(q, k, v, alpha, beta, dy, workspace=ws, out=outs, stream=stream)
+        for _ in range(2):
+            bwd_call()
+        torch.cuda.synchronize()
+        n_b = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_b):
+            bwd_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b_ms = e0.elapsed_time(e1) / n_b
+        bb, bf = bwd_bytes(B, T, H, dk, dv), bwd_flops(B, T, H, dk)
+        result["backward"] = {"workload": f"backward of the long prefill, B={B} T={T} H={H} d={dk}, bf16 inputs, "
+                                          "fp32 gradients", "kernels": "bwd_prep, bwd_states, bwd_dstates, bwd_grads",
+                              "avg_call_ms": b_ms, "tokens_per_s": B * T / (b_ms * 1e-3),
+                              "algorithmic_bytes": bb, "GBps": bb / (b_ms * 1e-3) / 1e9,
+                              "hbm_frac": bb / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "fp32_mfma_tflops": bf / (b_ms * 1e-3) / 1e12,
+                              "fp32_mfma_frac": bf / (b_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS}
+        log(f"backward {b_ms:.3f} ms ({bf / (b_ms * 1e-3) / 1e12:.1f} TFLOP/s fp32 MFMA, "
+            f"{bb / (b_ms * 1e-3) / 1e9:.0f} GB/s algorithmic)")
+        del q, k, v, alpha, beta, dy, outs, ws
         torch.cuda.empty_cache()
 
     # ---------------- multi-token decode: verify a 4-token draft block, commit ----------------

@@ -38,26 +38,33 @@ namespace bwd {
 constexpr int C = 64;
 constexpr float kLogFloor = -30.f;   // same floor of log(alpha) as the forward
 
-// acc += A * B for one 16x16 tile, A (16 x K) read transposed from At
-// (At[k][r] = A[r][k], leading dimension lda), B given as Bt (16 x K, row-major).
-__device__ __forceinline__ float4v mma_at(const float* At, int lda, const float* Bt, int ldb, int k0, int k1,
-                                          float4v acc) {
-    const int l = threadIdx.x & 63;
+// acc += A B for one 16x16 tile over k in [k0, k1).  Lane l supplies
+// A[l % 16][k + l / 16] and B[k + l / 16][l % 16] (the fp32 MFMA layout).
+//   kAt = false: A row-major (A[r][k] at A[r * lda + k], A at the tile's first row)
+//   kAt = true:  A stored transposed (A[r][k] at A[k * lda + r], A at the tile's first row index)
+//   kBr = false: B given transposed (B[k][n] at B[n * ldb + k], B at the tile's first column)
+//   kBr = true:  B row-major (B[k][n] at B[k * ldb + n], B at the tile's first column)
+// so a tile stored row-major serves both as an operand and as its transpose.
+template <bool kAt, bool kBr>
+__device__ __forceinline__ float4v mma(const float* A, int lda, const float* B, int ldb, int k0, int k1,
+                                       float4v acc) {
+    const int l = threadIdx.x & 63, r = l & 15, kk = l >> 4;
     for (int k = k0; k < k1; k += 4) {
-        const float a = At[(k + (l >> 4)) * lda + (l & 15)];
-        const float b = Bt[(l & 15) * ldb + k + (l >> 4)];
+        const float a = kAt ? A[(k + kk) * lda + r] : A[r * lda + k + kk];
+        const float b = kBr ? B[(k + kk) * ldb + r] : B[r * ldb + k + kk];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
     return acc;
 }
-// acc += (A + A^T) * B with A read both ways from the same row-major storage.
-__device__ __forceinline__ float4v mma_sym(const float* A, int lda, int r0, const float* Bt, int ldb, int k0,
+// acc += (A + A^T) B, A row-major (square, leading dimension lda), rows r0..r0+15
+// of the sum; B row-major at the tile's first column.
+__device__ __forceinline__ float4v mma_sym(const float* A, int lda, int r0, const float* B, int ldb, int k0,
                                            int k1, float4v acc) {
     const int l = threadIdx.x & 63;
     for (int k = k0; k < k1; k += 4) {
         const int r = r0 + (l & 15), kk = k + (l >> 4);
         const float a = A[r * lda + kk] + A[kk * lda + r];
-        const float b = Bt[(l & 15) * ldb + k + (l >> 4)];
+        const float b = B[kk * ldb + (l & 15)];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
     return acc;
@@ -77,26 +84,88 @@ __device__ __forceinline__ float dpp_sum16(float x) {         // sum over a row 
     return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));
 }
 
-// Four consecutive elements (index i, a multiple of 4) of a float32 or bf16 array.
-template <bool kBf16>
-__device__ __forceinline__ float4v load4(const void* p, long i) {
-    if constexpr (kBf16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-        return float4v{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
-                       bf16_to_f32(u.y >> 16)};
-    } else {
-        return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
-    }
+// The sequential walks run one workgroup per (head, 16-column slice).  All
+// slices of a head read the same chunk tiles, so they are placed on the same
+// XCD (consecutive workgroup ids go to the 8 XCDs in turn) to share its L2:
+// block L -> XCD L % 8, and XCD x walks the heads x, x + 8, ...  gridDim.x is
+// kSlices * 8 * ceil(BH / 8); ids past the last head return at once.
+template <int kSlices>
+__device__ __forceinline__ bool slice_of_block(int BH, int& slice, int& bh) {
+    const int L = blockIdx.x, xcd = L & 7, r = L >> 3;
+    slice = r % kSlices;
+    bh = (r / kSlices) * 8 + xcd;
+    return bh < BH;
 }
 
-// Row tg of the chunk as 4 values at column c4*4 (zero past the sequence end;
-// the load itself is clamped so that it is always in bounds).
+// Four consecutive input elements as loaded (bf16: 8 bytes, fp32: 16 bytes).
+template <bool kBf16> struct Raw4Of { typedef float4v type; };
+template <> struct Raw4Of<true> { typedef uint2 type; };
+template <bool kBf16> using Raw4 = typename Raw4Of<kBf16>::type;
+
 template <bool kBf16>
-__device__ __forceinline__ float4v load_row4(const void* p, int b, int tg, int T, int H, int h, int D, int col) {
-    const int tc = tg < T ? tg : T - 1;
-    const float4v x = load4<kBf16>(p, ((static_cast<long>(b) * T + tc) * H + h) * D + col);
-    return tg < T ? x : float4v{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ Raw4<kBf16> raw_load(const void* p, long i) {
+    if constexpr (kBf16) return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    else return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
 }
+template <bool kBf16>
+__device__ __forceinline__ float4v raw_cvt(Raw4<kBf16> u) {
+    if constexpr (kBf16)
+        return float4v{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                       bf16_to_f32(u.y >> 16)};
+    else return u;
+}
+template <bool kBf16>
+__device__ __forceinline__ float4v load4(const void* p, long i) { return raw_cvt<kBf16>(raw_load<kBf16>(p, i)); }
+
+// The C x D rows of chunk c of a [B, T, H, D] input (head h), held in
+// registers between an early load and a later store into a row-major LDS
+// tile.  Every load is unconditional (clamped rows), so that a prefetch of
+// the next chunk never makes the compiler wait inside the current one.
+template <int D, int NT, bool kBf16>
+struct RowTile {
+    static constexpr int kItems = C * D / 4;
+    static constexpr int kPer = (kItems + NT - 1) / NT;
+    Raw4<kBf16> r[kPer];
+    __device__ __forceinline__ void load(const void* p, int b, int c, int T, int H, int h) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            int i = threadIdx.x + NT * m;
+            i = i < kItems ? i : kItems - 1;
+            const int t = i / (D / 4), c4 = i - t * (D / 4);
+            const int tg = c * C + t, tc = tg < T ? tg : T - 1;
+            r[m] = raw_load<kBf16>(p, ((static_cast<long>(b) * T + tc) * H + h) * D + 4 * c4);
+        }
+    }
+    __device__ __forceinline__ void store(float* s, int ld, int c, int T) const {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int i = threadIdx.x + NT * m;
+            if (i < kItems) {
+                const int t = i / (D / 4), c4 = i - t * (D / 4);
+                const float4v x = c * C + t < T ? raw_cvt<kBf16>(r[m]) : float4v{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<float4v*>(&s[t * ld + 4 * c4]) = x;
+            }
+        }
+    }
+};
+
+// A C x C float32 chunk matrix of the workspace, register-staged the same way.
+template <int NT>
+struct MatTile {
+    static constexpr int kPer = C * C / 4 / NT;
+    float4v r[kPer];
+    __device__ __forceinline__ void load(const float* g) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) r[m] = reinterpret_cast<const float4v*>(g)[threadIdx.x + NT * m];
+    }
+    __device__ __forceinline__ void store(float* s, int ld) const {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int i = threadIdx.x + NT * m, t = i / (C / 4), c4 = i - t * (C / 4);
+            *reinterpret_cast<float4v*>(&s[t * ld + 4 * c4]) = r[m];
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Pass 1: gates, T, P and M of one chunk.  grid (nch, B*H), 256 threads.
@@ -108,20 +177,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
                                                        float* __restrict__ ws_T, float* __restrict__ ws_P,
                                                        float* __restrict__ ws_M, int T, int H, int nch) {
     constexpr int LDK = DK + 4, LDA = C + 4;
+    constexpr int kQA = C * LDK > C * LDA ? C * LDK : C * LDA;
     const int c = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const long bhn = static_cast<long>(bh) * nch + c;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
 
-    __shared__ __align__(16) float sQ[C * LDK];
     __shared__ __align__(16) float sK[C * LDK];
-    __shared__ __align__(16) float sA[C * LDA];
+    __shared__ __align__(16) float sQA[kQA];          // Q, then A = diag(beta) M
     __shared__ float sg[C], sb[C];
 
-    for (int i = tid; i < C * DK / 4; i += 256) {
-        const int t = i / (DK / 4), c4 = i - t * (DK / 4);
-        *reinterpret_cast<float4v*>(&sQ[t * LDK + 4 * c4]) = load_row4<kBf16>(q, b, c * C + t, T, H, h, DK, 4 * c4);
-        *reinterpret_cast<float4v*>(&sK[t * LDK + 4 * c4]) = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
+    {
+        RowTile<DK, 256, kBf16> tq, tk;
+        tq.load(q, b, c, T, H, h);
+        tk.load(k, b, c, T, H, h);
+        tq.store(sQA, LDK, c, T);
+        tk.store(sK, LDK, c, T);
     }
     if (wave == 0) {
         const int tg = c * C + l;
@@ -139,27 +210,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
     }
     __syncthreads();
 
-    // Gram tiles: 16 of K K^T and 16 of Q K^T, the upper ones are zero
+    // Gram tiles: 16 of K K^T and 16 of Q K^T; the ones above the diagonal are zero
+    float4v kk[4], qk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int p = wave * 4 + u, ti = p >> 2, tj = p & 3;
+        kk[u] = qk[u] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) {
+            kk[u] = mma<false, false>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, kk[u]);
+            qk[u] = mma<false, false>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, qk[u]);
+        }
+    }
+    __syncthreads();                                   // Q is no longer read: its space takes A
     float* gP = ws_P + bhn * C * C;
     float* gM = ws_M + bhn * C * C;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int p = wave * 4 + u, ti = p >> 2, tj = p & 3;
-        float4v kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
-        if (tj <= ti) {
-            kk = Mma<float>::range(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, kk);
-            qk = Mma<float>::range(&sQ[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, qk);
-        }
         const int col = 16 * tj + (l & 15);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * ti + 4 * (l >> 4) + j;
             const float gam = row >= col ? __expf(sg[row] - sg[col]) : 0.f;
-            const float m = row > col ? gam * kk[j] : 0.f;
-            const float pv = row >= col ? gam * qk[j] : 0.f;
+            const float m = row > col ? gam * kk[u][j] : 0.f;
+            const float pv = row >= col ? gam * qk[u][j] : 0.f;
             gM[row * C + col] = m;
             gP[row * C + col] = pv;
-            sA[row * LDA + col] = sb[row] * m;
+            sQA[row * LDA + col] = sb[row] * m;
         }
     }
     __syncthreads();
@@ -177,7 +254,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 #pragma unroll
         for (int m = 0; m < (t + 3) / 4; ++m) {
             const int i = 4 * m + part;
-            if (i < t) s += sA[t * LDA + i] * tcol[m];
+            if (i < t) s += sQA[t * LDA + i] * tcol[m];
         }
         s = dpp_sum4(s);
         const float v = (t == j ? 1.f : 0.f) - s;
@@ -191,7 +268,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk-start states and E, walking the chunks forward.
 // grid (DV / 16, B*H), 256 threads; the 16-column slice of S lives in the
-// accumulators of the waves that own its row blocks.
+// accumulators of the waves that own its row blocks.  The next chunk's
+// inputs are loaded into registers while the current chunk is computed.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool kBf16>
 __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict__ k, const void* __restrict__ v,
@@ -199,22 +277,50 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
                                                          const float* __restrict__ S0,
                                                          const float* __restrict__ ws_g,
                                                          const float* __restrict__ ws_T, float* __restrict__ ws_S,
-                                                         float* __restrict__ ws_E, int T, int H, int nch) {
-    constexpr int SV = 16, LDKT = C + 4, LDT = C + 4, LDS_ = DK + 4, LDR = C + 4;
+                                                         float* __restrict__ ws_E, int T, int H, int nch, int BH) {
+    constexpr int SV = 16, LDK = DK + 4, LDT = C + 4, LDS_ = DK + 4, LDR = C + 4;
     constexpr int NST = DK / 16;                       // state row blocks
     constexpr int SPW = (NST + 3) / 4;                 // state row blocks per wave
-    const int slice = blockIdx.x, bh = blockIdx.y;
+    int slice, bh;
+    if (!slice_of_block<DV / 16>(BH, slice, bh)) return;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
     const int col0 = slice * SV;
 
-    __shared__ __align__(16) float sKT[DK * LDKT];     // K^T of the chunk
+    __shared__ __align__(16) float sK[C * LDK];
     __shared__ __align__(16) float sT[C * LDT];
     __shared__ __align__(16) float sSt[SV * LDS_];     // S^T (the slice)
     __shared__ __align__(16) float sRt[SV * LDR];      // R^T
     __shared__ __align__(16) float sEt[SV * LDR];      // (lam E)^T
-    __shared__ float sV[C][SV];
+    __shared__ float sV[C][SV + 1];
     __shared__ float sg[C], sb[C];
+
+    RowTile<DK, 256, kBf16> pk;
+    MatTile<256> pt;
+    Raw4<kBf16> pv;
+    float pg = 0.f, pb = 0.f;
+    const int vt = tid >> 2, vc = tid & 3;
+    auto fetch = [&](int cc) {
+        const long bhn = static_cast<long>(bh) * nch + cc;
+        pk.load(k, b, cc, T, H, h);
+        pt.load(ws_T + bhn * C * C);
+        const int tg = cc * C + vt, tc = tg < T ? tg : T - 1;
+        pv = raw_load<kBf16>(v, ((static_cast<long>(b) * T + tc) * H + h) * DV + col0 + 4 * vc);
+        const int tl = tid & 63, tgl = cc * C + tl;
+        pg = ws_g[bhn * C + tl];
+        pb = beta[(static_cast<long>(b) * T + (tgl < T ? tgl : T - 1)) * H + h];
+    };
+    auto publish = [&](int cc) {
+        pk.store(sK, LDK, cc, T);
+        pt.store(sT, LDT);
+        const float4v x = cc * C + vt < T ? raw_cvt<kBf16>(pv) : float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sV[vt][4 * vc + e] = x[e];
+        if (tid < C) {
+            sg[tid] = pg;
+            sb[tid] = cc * C + tid < T ? pb : 0.f;
+        }
+    };
 
     float4v st[SPW];
 #pragma unroll
@@ -231,9 +337,13 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
             for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = st[u][j];
         }
     }
+    fetch(0);
+    publish(0);
+    __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
         const long bhn = static_cast<long>(bh) * nch + c;
+        fetch(c + 1 < nch ? c + 1 : c);
         // chunk-start state out
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
@@ -244,34 +354,10 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
                     ws_S[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = st[u][j];
             }
         }
-        for (int i = tid; i < C * DK / 4; i += 256) {
-            const int t = i / (DK / 4), c4 = i - t * (DK / 4);
-            const float4v x = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sKT[(4 * c4 + e) * LDKT + t] = x[e];
-        }
-        for (int i = tid; i < C * C / 4; i += 256) {
-            const int t = i / (C / 4), c4 = i - t * (C / 4);
-            *reinterpret_cast<float4v*>(&sT[t * LDT + 4 * c4]) =
-                *reinterpret_cast<const float4v*>(&ws_T[bhn * C * C + t * C + 4 * c4]);
-        }
-        {
-            const int t = tid >> 2, c4 = tid & 3;
-            const float4v x = load_row4<kBf16>(v, b, c * C + t, T, H, h, DV, col0 + 4 * c4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sV[t][4 * c4 + e] = x[e];
-        }
-        if (tid < C) {
-            const int tg = c * C + tid;
-            sg[tid] = ws_g[bhn * C + tid];
-            sb[tid] = tg < T ? beta[(static_cast<long>(b) * T + tg) * H + h] : 0.f;
-        }
-        __syncthreads();
-
         // R = diag(beta) (V - diag(gamma) K S), one row block per wave
         {
             float4v ks = {0.f, 0.f, 0.f, 0.f};
-            ks = mma_at(&sKT[16 * wave], LDKT, sSt, LDS_, 0, DK, ks);
+            ks = mma<false, false>(&sK[16 * wave * LDK], LDK, sSt, LDS_, 0, DK, ks);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * wave + 4 * (l >> 4) + j;
@@ -282,7 +368,7 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
         // E = T R (T lower triangular), written out; (lam E)^T kept for the update
         {
             float4v e = {0.f, 0.f, 0.f, 0.f};
-            e = Mma<float>::range(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, 16 * (wave + 1), e);
+            e = mma<false, false>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, 16 * (wave + 1), e);
             const float gn = sg[C - 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -300,13 +386,15 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
                 const int m = wave + 4 * u;
                 if (m < NST) {
                     float4v acc = gam_n * st[u];
-                    acc = Mma<float>::range(&sKT[16 * m * LDKT], LDKT, sEt, LDR, 0, C, acc);
+                    acc = mma<true, false>(&sK[16 * m], LDK, sEt, LDR, 0, C, acc);
                     st[u] = acc;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = acc[j];
                 }
             }
         }
+        __syncthreads();
+        publish(c + 1 < nch ? c + 1 : c);
         __syncthreads();
     }
 }
@@ -320,16 +408,17 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
     const float* __restrict__ dy, const float* __restrict__ dST, const float* __restrict__ ws_g,
     const float* __restrict__ ws_T, const float* __restrict__ ws_P, float* __restrict__ ws_dS,
     float* __restrict__ ws_dR, float* __restrict__ dv_out, float* __restrict__ dS0, int T, int H, int nch,
-    float scale) {
-    constexpr int SV = 16, LDX = C + 4, LDS_ = DK + 4;
+    int BH, float scale) {
+    constexpr int SV = 16, LDK = DK + 4, LDX = C + 4, LDS_ = DK + 4;
     constexpr int NST = DK / 16, SPW = (NST + 3) / 4;
-    const int slice = blockIdx.x, bh = blockIdx.y;
+    int slice, bh;
+    if (!slice_of_block<DV / 16>(BH, slice, bh)) return;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
     const int col0 = slice * SV;
 
-    __shared__ __align__(16) float sQT[DK * LDX];
-    __shared__ __align__(16) float sKT[DK * LDX];
+    __shared__ __align__(16) float sQ[C * LDK];
+    __shared__ __align__(16) float sK[C * LDK];
     __shared__ __align__(16) float sT[C * LDX];
     __shared__ __align__(16) float sP[C * LDX];
     __shared__ __align__(16) float sdYt[SV * LDX];     // dY^T
@@ -338,6 +427,37 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
     __shared__ __align__(16) float sdEt[SV * LDX];     // dE^T
     __shared__ __align__(16) float sdSt[SV * LDS_];    // dS'^T
     __shared__ float sg[C], sb[C];
+
+    RowTile<DK, 256, kBf16> pq, pk;
+    MatTile<256> pt, pp;
+    float4v pdy;
+    float pg = 0.f, pb = 0.f;
+    const int yt = tid >> 2, yc = tid & 3;
+    auto fetch = [&](int cc) {
+        const long bhn = static_cast<long>(bh) * nch + cc;
+        pq.load(q, b, cc, T, H, h);
+        pk.load(k, b, cc, T, H, h);
+        pt.load(ws_T + bhn * C * C);
+        pp.load(ws_P + bhn * C * C);
+        const int tg = cc * C + yt, tc = tg < T ? tg : T - 1;
+        pdy = *reinterpret_cast<const float4v*>(&dy[((static_cast<long>(b) * T + tc) * H + h) * DV + col0 + 4 * yc]);
+        const int tl = tid & 63, tgl = cc * C + tl;
+        pg = ws_g[bhn * C + tl];
+        pb = beta[(static_cast<long>(b) * T + (tgl < T ? tgl : T - 1)) * H + h];
+    };
+    auto publish = [&](int cc) {
+        pq.store(sQ, LDK, cc, T);
+        pk.store(sK, LDK, cc, T);
+        pt.store(sT, LDX);
+        pp.store(sP, LDX);
+        const float4v x = cc * C + yt < T ? pdy : float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdYt[(4 * yc + e) * LDX + yt] = x[e];
+        if (tid < C) {
+            sg[tid] = pg;
+            sb[tid] = cc * C + tid < T ? pb : 0.f;
+        }
+    };
 
     float4v ds[SPW];
 #pragma unroll
@@ -354,9 +474,13 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
             for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
         }
     }
+    fetch(nch - 1);
+    publish(nch - 1);
+    __syncthreads();
 
     for (int c = nch - 1; c >= 0; --c) {
         const long bhn = static_cast<long>(bh) * nch + c;
+        fetch(c > 0 ? c - 1 : 0);
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int m = wave + 4 * u;
@@ -366,43 +490,11 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
                     ws_dS[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[u][j];
             }
         }
-        for (int i = tid; i < C * DK / 4; i += 256) {
-            const int t = i / (DK / 4), c4 = i - t * (DK / 4);
-            const float4v xq = load_row4<kBf16>(q, b, c * C + t, T, H, h, DK, 4 * c4);
-            const float4v xk = load_row4<kBf16>(k, b, c * C + t, T, H, h, DK, 4 * c4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sQT[(4 * c4 + e) * LDX + t] = xq[e];
-                sKT[(4 * c4 + e) * LDX + t] = xk[e];
-            }
-        }
-        for (int i = tid; i < C * C / 4; i += 256) {
-            const int t = i / (C / 4), c4 = i - t * (C / 4);
-            *reinterpret_cast<float4v*>(&sT[t * LDX + 4 * c4]) =
-                *reinterpret_cast<const float4v*>(&ws_T[bhn * C * C + t * C + 4 * c4]);
-            *reinterpret_cast<float4v*>(&sP[t * LDX + 4 * c4]) =
-                *reinterpret_cast<const float4v*>(&ws_P[bhn * C * C + t * C + 4 * c4]);
-        }
-        {
-            const int t = tid >> 2, c4 = tid & 3, tg = c * C + t;
-            const int tc = tg < T ? tg : T - 1;
-            float4v x = *reinterpret_cast<const float4v*>(&dy[((static_cast<long>(b) * T + tc) * H + h) * DV + col0 + 4 * c4]);
-            if (tg >= T) x = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sdYt[(4 * c4 + e) * LDX + t] = x[e];
-        }
-        if (tid < C) {
-            const int tg = c * C + tid;
-            sg[tid] = ws_g[bhn * C + tid];
-            sb[tid] = tg < T ? beta[(static_cast<long>(b) * T + tg) * H + h] : 0.f;
-        }
-        __syncthreads();
-
         // dE = scale P^T dY + diag(lam) K dS'  (P^T upper triangular)
         {
             float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-            a1 = mma_at(&sP[16 * wave], LDX, sdYt, LDX, 16 * wave, C, a1);
-            a2 = mma_at(&sKT[16 * wave], LDX, sdSt, LDS_, 0, DK, a2);
+            a1 = mma<true, false>(&sP[16 * wave], LDX, sdYt, LDX, 16 * wave, C, a1);
+            a2 = mma<false, false>(&sK[16 * wave * LDK], LDK, sdSt, LDS_, 0, DK, a2);
             const float gn = sg[C - 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -418,7 +510,7 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
         // dR = T^T dE; dV = diag(beta) dR
         {
             float4v r = {0.f, 0.f, 0.f, 0.f};
-            r = mma_at(&sT[16 * wave], LDX, sdEt, LDX, 16 * wave, C, r);
+            r = mma<true, false>(&sT[16 * wave], LDX, sdEt, LDX, 16 * wave, C, r);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * wave + 4 * (l >> 4) + j, tg = c * C + t;
@@ -436,13 +528,13 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
                 const int m = wave + 4 * u;
                 if (m < NST) {
                     float4v acc = gam_n * ds[u];
-                    acc = Mma<float>::range(&sQT[16 * m * LDX], LDX, sB1t, LDX, 0, C, acc);
-                    acc = Mma<float>::range(&sKT[16 * m * LDX], LDX, sB2t, LDX, 0, C, acc);
+                    acc = mma<true, false>(&sQ[16 * m], LDK, sB1t, LDX, 0, C, acc);
+                    acc = mma<true, false>(&sK[16 * m], LDK, sB2t, LDX, 0, C, acc);
                     ds[u] = acc;
                 }
             }
         }
-        __syncthreads();                       // every read of sdSt above is done
+        __syncthreads();                       // every read of this chunk's tiles is done
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int m = wave + 4 * u;
@@ -451,6 +543,7 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
                 for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
             }
         }
+        publish(c > 0 ? c - 1 : 0);
         __syncthreads();
     }
     if (dS0) {
@@ -478,7 +571,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     const float* __restrict__ ws_S, const float* __restrict__ ws_dS, const float* __restrict__ ws_E,
     const float* __restrict__ ws_dR, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int H, int nch, float scale) {
-    constexpr int SL = 16, LDL = SL + 4, LDX = C + 4;
+    constexpr int SL = 16, LDL = SL + 4, LDX = C + 4, LDK = D + 4;
     constexpr int NB = D / 16;                      // column blocks of X1..X3
     constexpr int NP = 4 * NB;                      // (row block, column block) pairs
     constexpr int PPW = (NP + 7) / 8;               // pairs per wave
@@ -492,8 +585,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     constexpr int kPMFloats = 2 * C * LDX;
     constexpr int kRegion = kSlabFloats > kPMFloats ? kSlabFloats : kPMFloats;
     __shared__ __align__(16) float sR[kRegion];
-    __shared__ __align__(16) float sQT[D * LDX];
-    __shared__ __align__(16) float sKT[D * LDX];
+    __shared__ __align__(16) float sQ[C * LDK];
+    __shared__ __align__(16) float sK[C * LDK];
     __shared__ __align__(16) float sX4[C * LDX];    // X4, then dP o Gamma
     __shared__ __align__(16) float sX5[C * LDX];    // X5, then Dm
     __shared__ float sg[C], sb[C], sa[C];
@@ -544,17 +637,17 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             const int p = wave + 8 * u;
             if (p < NP) {
                 const int ti = p / NB, tj = p - ti * NB;
-                x1[u] = Mma<float>::range(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x1[u]);
-                x2[u] = Mma<float>::range(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x2[u]);
-                x3[u] = Mma<float>::range(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, SL, x3[u]);
+                x1[u] = mma<false, false>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x1[u]);
+                x2[u] = mma<false, false>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x2[u]);
+                x3[u] = mma<false, false>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, SL, x3[u]);
             }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
             if (tj <= ti) {
-                x4[u] = Mma<float>::range(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x4[u]);
-                x5[u] = Mma<float>::range(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x5[u]);
+                x4[u] = mma<false, false>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x4[u]);
+                x5[u] = mma<false, false>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x5[u]);
             }
         }
         __syncthreads();
@@ -580,15 +673,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         *reinterpret_cast<float4v*>(&sM[t * LDX + 4 * c4]) =
             *reinterpret_cast<const float4v*>(&ws_M[bhn * C * C + t * C + 4 * c4]);
     }
-    for (int i = tid; i < C * D / 4; i += 512) {
-        const int t = i / (D / 4), c4 = i - t * (D / 4);
-        const float4v xq = load_row4<kBf16>(q, b, c * C + t, T, H, h, D, 4 * c4);
-        const float4v xk = load_row4<kBf16>(k, b, c * C + t, T, H, h, D, 4 * c4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sQT[(4 * c4 + e) * LDX + t] = xq[e];
-            sKT[(4 * c4 + e) * LDX + t] = xk[e];
-        }
+    {
+        RowTile<D, 512, kBf16> tq, tk;
+        tq.load(q, b, c, T, H, h);
+        tk.load(k, b, c, T, H, h);
+        tq.store(sQ, LDK, c, T);
+        tk.store(sK, LDK, c, T);
     }
     if (tid < C) {
         const int tg = c * C + tid;
@@ -623,9 +713,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j;
-                const float a1 = dpp_sum16(sQT[col * LDX + row] * x1[u][j]);
-                const float a2 = dpp_sum16(sKT[col * LDX + row] * x2[u][j]);
-                const float a3 = dpp_sum16(sKT[col * LDX + row] * x3[u][j]);
+                const float a1 = dpp_sum16(sQ[row * LDK + col] * x1[u][j]);
+                const float a2 = dpp_sum16(sK[row * LDK + col] * x2[u][j]);
+                const float a3 = dpp_sum16(sK[row * LDK + col] * x3[u][j]);
                 if ((l & 15) == 0) {
                     atomicAdd(&sQX1[row], a1);
                     atomicAdd(&sKX2[row], a2);
@@ -721,9 +811,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 aq[j] = scale * gam * x1[u][j];
                 ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
             }
-            aq = Mma<float>::range(&sX4[16 * ti * LDX], LDX, &sKT[16 * tj * LDX], LDX, 0, 16 * (ti + 1), aq);
-            ak = mma_sym(sX5, LDX, 16 * ti, &sKT[16 * tj * LDX], LDX, 0, C, ak);
-            ak = mma_at(&sX4[16 * ti], LDX, &sQT[16 * tj * LDX], LDX, 16 * ti, C, ak);
+            aq = mma<false, true>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, 16 * (ti + 1), aq);
+            ak = mma_sym(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, C, ak);
+            ak = mma<true, true>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 16 * ti, C, ak);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j, tg = c * C + row;
@@ -768,13 +858,15 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
     float* dS = reinterpret_cast<float*>(w);           w += up(bhn * D * D * 4);
     float* E = reinterpret_cast<float*>(w);            w += up(bhn * bwd::C * D * 4);
     float* dR = reinterpret_cast<float*>(w);
-    const dim3 gc(nch, a.B * a.H), gs(D / 16, a.B * a.H);
+    const int BH = a.B * a.H;
+    const dim3 gc(nch, BH), gs((D / 16) * 8 * ((BH + 7) / 8), 1);
     hipLaunchKernelGGL((bwd::bwd_prep_kernel<D, kBf16>), gc, dim3(256), 0, a.stream, a.q, a.k, a.alpha, a.beta,
                        g, Tm, P, M, a.T, a.H, nch);
     hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.k, a.v, a.beta,
-                       a.initial_state, g, Tm, S, E, a.T, a.H, nch);
+                       a.initial_state, g, Tm, S, E, a.T, a.H, nch, BH);
     hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.q, a.k, a.beta,
-                       a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, a.scale);
+                       a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, BH,
+                       a.scale);
     hipLaunchKernelGGL((bwd::bwd_grads_kernel<D, kBf16>), gc, dim3(512), 0, a.stream, a.q, a.k, a.v, a.alpha,
                        a.beta, a.dy, g, P, M, S, dS, E, dR, a.dq, a.dk, a.dalpha, a.dbeta, a.T, a.H, nch, a.scale);
     return hipGetLastError();
