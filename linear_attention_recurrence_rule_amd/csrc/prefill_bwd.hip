@@ -56,6 +56,41 @@ __device__ __forceinline__ float4v mma(const float* A, int lda, const float* B, 
     }
     return acc;
 }
+// The same product over a compile-time length N = k1 - k0 with a split-K lane
+// layout: lane group l / 16 owns the contiguous run [k0 + (l/16) N/4, ... + N/4)
+// and step s takes element s of every run (the four partial sums of one MFMA
+// cover different k, and their total is the same contraction).  All operand
+// values are read from LDS before the first MFMA, so the dependent MFMA chain
+// never waits on LDS latency; row-major runs are read as float4.
+template <bool kAt, bool kBr, int N>
+__device__ __forceinline__ float4v mma_n(const float* A, int lda, const float* B, int ldb, int k0, float4v acc) {
+    constexpr int S = N / 4;
+    static_assert(S % 4 == 0, "contraction length must be a multiple of 16");
+    const int l = threadIdx.x & 63, r = l & 15, kb = k0 + (l >> 4) * S;
+    float a[S], b[S];
+#pragma unroll
+    for (int s = 0; s < S; s += 4) {
+        if constexpr (kAt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[s + e] = A[(kb + s + e) * lda + r];
+        } else {
+            const float4v x = *reinterpret_cast<const float4v*>(&A[r * lda + kb + s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[s + e] = x[e];
+        }
+        if constexpr (kBr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[s + e] = B[(kb + s + e) * ldb + r];
+        } else {
+            const float4v x = *reinterpret_cast<const float4v*>(&B[r * ldb + kb + s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[s + e] = x[e];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
 // acc += (A + A^T) B, A row-major (square, leading dimension lda), rows r0..r0+15
 // of the sum; B row-major at the tile's first column.
 __device__ __forceinline__ float4v mma_sym(const float* A, int lda, int r0, const float* B, int ldb, int k0,
@@ -357,7 +392,7 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
         // R = diag(beta) (V - diag(gamma) K S), one row block per wave
         {
             float4v ks = {0.f, 0.f, 0.f, 0.f};
-            ks = mma<false, false>(&sK[16 * wave * LDK], LDK, sSt, LDS_, 0, DK, ks);
+            ks = mma_n<false, false, DK>(&sK[16 * wave * LDK], LDK, sSt, LDS_, 0, ks);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * wave + 4 * (l >> 4) + j;
@@ -368,7 +403,7 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
         // E = T R (T lower triangular), written out; (lam E)^T kept for the update
         {
             float4v e = {0.f, 0.f, 0.f, 0.f};
-            e = mma<false, false>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, 16 * (wave + 1), e);
+            e = mma_n<false, false, C>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, e);   // T is zero above the diagonal
             const float gn = sg[C - 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -386,7 +421,7 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
                 const int m = wave + 4 * u;
                 if (m < NST) {
                     float4v acc = gam_n * st[u];
-                    acc = mma<true, false>(&sK[16 * m], LDK, sEt, LDR, 0, C, acc);
+                    acc = mma_n<true, false, C>(&sK[16 * m], LDK, sEt, LDR, 0, acc);
                     st[u] = acc;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = acc[j];
@@ -493,8 +528,8 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
         // dE = scale P^T dY + diag(lam) K dS'  (P^T upper triangular)
         {
             float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-            a1 = mma<true, false>(&sP[16 * wave], LDX, sdYt, LDX, 16 * wave, C, a1);
-            a2 = mma<false, false>(&sK[16 * wave * LDK], LDK, sdSt, LDS_, 0, DK, a2);
+            a1 = mma_n<true, false, C>(&sP[16 * wave], LDX, sdYt, LDX, 0, a1);   // P^T is zero below the diagonal
+            a2 = mma_n<false, false, DK>(&sK[16 * wave * LDK], LDK, sdSt, LDS_, 0, a2);
             const float gn = sg[C - 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -510,7 +545,7 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
         // dR = T^T dE; dV = diag(beta) dR
         {
             float4v r = {0.f, 0.f, 0.f, 0.f};
-            r = mma<true, false>(&sT[16 * wave], LDX, sdEt, LDX, 16 * wave, C, r);
+            r = mma_n<true, false, C>(&sT[16 * wave], LDX, sdEt, LDX, 0, r);   // T^T is zero below the diagonal
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * wave + 4 * (l >> 4) + j, tg = c * C + t;
@@ -528,8 +563,8 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
                 const int m = wave + 4 * u;
                 if (m < NST) {
                     float4v acc = gam_n * ds[u];
-                    acc = mma<true, false>(&sQ[16 * m], LDK, sB1t, LDX, 0, C, acc);
-                    acc = mma<true, false>(&sK[16 * m], LDK, sB2t, LDX, 0, C, acc);
+                    acc = mma_n<true, false, C>(&sQ[16 * m], LDK, sB1t, LDX, 0, acc);
+                    acc = mma_n<true, false, C>(&sK[16 * m], LDK, sB2t, LDX, 0, acc);
                     ds[u] = acc;
                 }
             }
