@@ -642,47 +642,66 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     for (int u = 0; u < 2; ++u) x4[u] = x5[u] = float4v{0.f, 0.f, 0.f, 0.f};
     float drv = 0.f, sds = 0.f;
 
+    // phase-2 operands are loaded into registers first; each dv slab is
+    // loaded one slab ahead of its use
+    RowTile<D, 512, kBf16> tq, tk;
+    MatTile<512> tp, tm;
+    tq.load(q, b, c, T, H, h);
+    tk.load(k, b, c, T, H, h);
+    tp.load(ws_P + bhn * C * C);
+    tm.load(ws_M + bhn * C * C);
+    const int rt = (tid & 255) >> 2, rc = tid & 3;                 // row item: row rt, columns 4 rc..
+    const int si = tid % (D * SL / 4), sr = si >> 2, sc = si & 3;  // state item: row sr, columns 4 sc..
+    const int tg0 = c * C + rt, tc0 = tg0 < T ? tg0 : T - 1;
+    const long row0 = (static_cast<long>(b) * T + tc0) * H + h;
+    float4v fdy, fdr, fe, fs, fds;
+    Raw4<kBf16> fv;
+    auto fetch = [&](int v0) {
+        fdy = *reinterpret_cast<const float4v*>(&dy[row0 * D + v0 + 4 * rc]);
+        fv = raw_load<kBf16>(v, row0 * D + v0 + 4 * rc);
+        fdr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + rt) * D + v0 + 4 * rc]);
+        fe = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + rt) * D + v0 + 4 * rc]);
+        fs = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + sr) * D + v0 + 4 * sc]);
+        fds = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + sr) * D + v0 + 4 * sc]);
+    };
+    fetch(0);
     for (int v0 = 0; v0 < D; v0 += SL) {
         if (tid < C * SL / 4) {
-            const int t = tid >> 2, c4 = tid & 3, tg = c * C + t;
-            const int tc = tg < T ? tg : T - 1;
-            const long row = (static_cast<long>(b) * T + tc) * H + h;
-            float4v xdy = *reinterpret_cast<const float4v*>(&dy[row * D + v0 + 4 * c4]);
-            float4v xv = load4<kBf16>(v, row * D + v0 + 4 * c4);
-            if (tg >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
-            const float4v xdr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + t) * D + v0 + 4 * c4]);
-            const float4v xe = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + t) * D + v0 + 4 * c4]);
-            *reinterpret_cast<float4v*>(&sdY[t * LDL + 4 * c4]) = xdy;
-            *reinterpret_cast<float4v*>(&sdR[t * LDL + 4 * c4]) = xdr;
-            *reinterpret_cast<float4v*>(&sE[t * LDL + 4 * c4]) = xe;
-            *reinterpret_cast<float4v*>(&sV[t * LDL + 4 * c4]) = xv;
-            drv += xdr.x * xv.x + xdr.y * xv.y + xdr.z * xv.z + xdr.w * xv.w;
+            float4v xdy = fdy, xv = raw_cvt<kBf16>(fv);
+            if (tg0 >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<float4v*>(&sdY[rt * LDL + 4 * rc]) = xdy;
+            *reinterpret_cast<float4v*>(&sdR[rt * LDL + 4 * rc]) = fdr;
+            *reinterpret_cast<float4v*>(&sE[rt * LDL + 4 * rc]) = fe;
+            *reinterpret_cast<float4v*>(&sV[rt * LDL + 4 * rc]) = xv;
+            drv += fdr.x * xv.x + fdr.y * xv.y + fdr.z * xv.z + fdr.w * xv.w;
         }
-        for (int i = tid; i < D * SL / 4; i += 512) {
-            const int r = i >> 2, c4 = i & 3;
-            const float4v xs = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + r) * D + v0 + 4 * c4]);
-            const float4v xd = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + r) * D + v0 + 4 * c4]);
-            *reinterpret_cast<float4v*>(&sS[r * LDL + 4 * c4]) = xs;
-            *reinterpret_cast<float4v*>(&sdS[r * LDL + 4 * c4]) = xd;
-            sds += xs.x * xd.x + xs.y * xd.y + xs.z * xd.z + xs.w * xd.w;
+        if (tid < D * SL / 4) {
+            *reinterpret_cast<float4v*>(&sS[sr * LDL + 4 * sc]) = fs;
+            *reinterpret_cast<float4v*>(&sdS[sr * LDL + 4 * sc]) = fds;
+            sds += fs.x * fds.x + fs.y * fds.y + fs.z * fds.z + fs.w * fds.w;
+        }
+        if (v0 == 0) {
+            tq.store(sQ, LDK, c, T);
+            tk.store(sK, LDK, c, T);
         }
         __syncthreads();
+        fetch(v0 + SL < D ? v0 + SL : v0);
 #pragma unroll
         for (int u = 0; u < PPW; ++u) {
             const int p = wave + 8 * u;
             if (p < NP) {
                 const int ti = p / NB, tj = p - ti * NB;
-                x1[u] = mma<false, false>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x1[u]);
-                x2[u] = mma<false, false>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, SL, x2[u]);
-                x3[u] = mma<false, false>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, SL, x3[u]);
+                x1[u] = mma_n<false, false, SL>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x1[u]);
+                x2[u] = mma_n<false, false, SL>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x2[u]);
+                x3[u] = mma_n<false, false, SL>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, x3[u]);
             }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
             if (tj <= ti) {
-                x4[u] = mma<false, false>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x4[u]);
-                x5[u] = mma<false, false>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, SL, x5[u]);
+                x4[u] = mma_n<false, false, SL>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x4[u]);
+                x5[u] = mma_n<false, false, SL>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x5[u]);
             }
         }
         __syncthreads();
@@ -701,20 +720,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     }
     float* sP = sR;
     float* sM = sR + C * LDX;
-    for (int i = tid; i < C * C / 4; i += 512) {
-        const int t = i / (C / 4), c4 = i - t * (C / 4);
-        *reinterpret_cast<float4v*>(&sP[t * LDX + 4 * c4]) =
-            *reinterpret_cast<const float4v*>(&ws_P[bhn * C * C + t * C + 4 * c4]);
-        *reinterpret_cast<float4v*>(&sM[t * LDX + 4 * c4]) =
-            *reinterpret_cast<const float4v*>(&ws_M[bhn * C * C + t * C + 4 * c4]);
-    }
-    {
-        RowTile<D, 512, kBf16> tq, tk;
-        tq.load(q, b, c, T, H, h);
-        tk.load(k, b, c, T, H, h);
-        tq.store(sQ, LDK, c, T);
-        tk.store(sK, LDK, c, T);
-    }
+    tp.store(sP, LDX);
+    tm.store(sM, LDX);
     if (tid < C) {
         const int tg = c * C + tid;
         const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
@@ -846,9 +853,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 aq[j] = scale * gam * x1[u][j];
                 ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
             }
-            aq = mma<false, true>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, 16 * (ti + 1), aq);
+            aq = mma_n<false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
             ak = mma_sym(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, C, ak);
-            ak = mma<true, true>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 16 * ti, C, ak);
+            ak = mma_n<true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j, tg = c * C + row;
