@@ -15,6 +15,8 @@ parameterisation block of the same Module A; multi-token (speculative)
 decode is the same recurrence over a block of draft tokens, with a commit step
 that advances the live state by the accepted prefix only; the backward is the
 chain rule through the same recurrence, written out step by step in reverse.
+The QSA indexer (key pooling, partial rotary embedding, block-causal ReLU
+scores, top-K block selection) follows Module B of the same slinene page.
 """
 
 from .gdn_ref import (  # noqa: F401
@@ -26,3 +28,4 @@ from .gdn_ref import (  # noqa: F401
 from .frontend_ref import gdn_frontend, short_conv, silu, l2norm  # noqa: F401
 from .mtp_ref import mtp_verify, mtp_commit  # noqa: F401
 from .bwd_ref import gated_delta_backward  # noqa: F401
+from .qsa_ref import rmsnorm, partial_rope, qsa_prep, qsa_scores, qsa_select, qsa_token_set  # noqa: F401

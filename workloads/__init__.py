@@ -14,4 +14,6 @@ from .synth import (  # noqa: F401
     decode_step_inputs,
     frontend_inputs,
     mtp_draft_inputs,
+    qsa_inputs,
+    qsa_select_inputs,
 )

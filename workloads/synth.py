@@ -194,3 +194,25 @@ def mtp_draft_inputs(rnd, K=4, index=3, N=None, H=None):
     N, H = N or c["N"], H or c["H"]
     return _draw_segment(np.random.default_rng([c["seed"], MTP_STREAM, rnd]), N, K, H, c["dk"], c["dv"],
                          c["A"], c["b"], c["dtype"], False)
+
+
+QSA_STREAM = 2**31 - 3       # second seed word of the indexer streams
+
+
+def qsa_inputs(B, n, H=4, D=128, dtype="bf16", seed=0):
+    """Projected indexer streams: q_proj [B, n, H, D] and k_proj [B, n, D],
+    N(0, 1) (rounded to bf16 unless dtype is f32), from
+    default_rng([seed, QSA_STREAM, 0])."""
+    rng = np.random.default_rng([seed, QSA_STREAM, 0])
+    return dict(q_proj=_cast(rng.standard_normal((B, n, H, D)), dtype),
+                k_proj=_cast(rng.standard_normal((B, n, D)), dtype))
+
+
+def qsa_select_inputs(B, n, r=4, H=4, D=128, dtype="bf16", seed=0):
+    """Prepared indexer operands for the scoring / selection step: q [B, n, H, D]
+    and pooled keys kbar [B, n // r, D].  After RMSNorm and the rotation their
+    entries have unit mean square, so N(0, 1) draws (rounded to bf16 unless
+    dtype is f32) stand in for them; from default_rng([seed, QSA_STREAM, 1])."""
+    rng = np.random.default_rng([seed, QSA_STREAM, 1])
+    return dict(q=_cast(rng.standard_normal((B, n, H, D)), dtype),
+                kbar=_cast(rng.standard_normal((B, n // r, D)), dtype))
