@@ -247,6 +247,51 @@ gdn_status gdn_decode_mtp_commit(const void* k, const float* alpha, const float*
                                  int N, int K, int H, int d_k, int d_v,
                                  gdn_dtype qkv_dtype, void* hip_stream);
 
+/*
+ * QSA indexer, part 1 (slinene page, Module B: the compressed MQA indexer):
+ * the indexer operands from the projected streams, per sequence of n tokens
+ * with block size r:
+ *     q[i][h]  = PRoPE(RMSNorm(q_proj[i][h]), i)
+ *     kbar[b]  = PRoPE(RMSNorm(mean(k_proj[b r .. b r + r - 1])), b r),  b < n / r
+ * (keys are pooled before the rotation).  RMSNorm(x) = x / sqrt(mean(x^2) + eps)
+ * times the weight (NULL = 1).  PRoPE turns the first rope_dims entries in
+ * rotate-half pairs (j, j + rope_dims / 2) by pos * rope_base^(-2 j / rope_dims).
+ *
+ *   q_proj    [B, n, H, D]  io_dtype        k_proj   [B, n, D] io_dtype
+ *   q_weight, k_weight  [D] float32 or NULL
+ *   q_out     [B, n, H, D]  io_dtype out    kbar_out [B, n / r, D] io_dtype out
+ *   D in {32, 64, 128}; 0 <= rope_dims <= D, even; r >= 1; eps >= 0.
+ */
+gdn_status gdn_qsa_prep(const void* q_proj, const void* k_proj,
+                        const float* q_weight, const float* k_weight,
+                        void* q_out, void* kbar_out,
+                        int B, int n, int H, int D, int r, int rope_dims,
+                        float rope_base, float eps, gdn_dtype io_dtype, void* hip_stream);
+
+/*
+ * QSA indexer, part 2 (slinene page, Module B: block-causal scoring and
+ * top-K block selection): for query i the candidates are the complete blocks
+ * b < (i + 1) / r (b r + r - 1 <= i), scored
+ *     I[i][b] = sum_h ReLU(<q[i][h], kbar[b]>)
+ * and the K_B = ceil(K / r) best are selected (all of them when there are
+ * fewer; equal scores are broken towards the later block).  The tail tokens of
+ * the current incomplete block are always attended and are not listed.
+ *
+ *   q            [B, n, H, D]  dtype (the output of gdn_qsa_prep)
+ *   kbar         [B, n / r, D] dtype
+ *   block_idx    [B, n, K_B]   int32 out: selected blocks in ascending order,
+ *                padded with -1
+ *   workspace    caller-owned, >= gdn_qsa_select_workspace_bytes(...) bytes:
+ *                the fp32 block scores, B n ceil(n / r / 64) 64 4 bytes
+ *   D in {32, 64, 128}; r >= 1; K >= 1.
+ */
+gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx,
+                          int B, int n, int H, int D, int r, int K,
+                          gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes gdn_qsa_select needs (0 for invalid arguments). */
+size_t gdn_qsa_select_workspace_bytes(int B, int n, int H, int D, int r, int K, gdn_dtype dtype);
+
 /* Static, never-NULL description of a status code. */
 const char* gdn_status_string(gdn_status status);
 

@@ -18,7 +18,8 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
     "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
     "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit",
-    "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_status_string",
+    "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
+    "gdn_qsa_select_workspace_bytes", "gdn_status_string",
 ]
 
 GDN_F32 = 0
@@ -73,6 +74,12 @@ def load_library():
     lib.gdn_prefill_bwd.restype = ctypes.c_int
     lib.gdn_prefill_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gdn_prefill_bwd_workspace_bytes.restype = sz
+    lib.gdn_qsa_prep.argtypes = [vp, vp, fp, fp, vp, vp, i, i, i, i, i, i, f, f, i, vp]
+    lib.gdn_qsa_prep.restype = ctypes.c_int
+    lib.gdn_qsa_select.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.gdn_qsa_select.restype = ctypes.c_int
+    lib.gdn_qsa_select_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.gdn_qsa_select_workspace_bytes.restype = sz
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -357,3 +364,58 @@ def gdn_prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, d_final_state=
     if st:
         raise GdnError(st, "gdn_prefill_bwd")
     return dq, dk_, dv_, da, db, dS0
+
+
+def gdn_qsa_prep(q_proj, k_proj, r=4, rope_dims=64, rope_base=10000.0, eps=1e-6, q_weight=None, k_weight=None,
+                 out=None, stream=None):
+    """QSA indexer operands.  q_proj [B, n, H, D], k_proj [B, n, D] (bf16 or fp32, one
+    dtype); q_weight, k_weight [D] fp32 or None.  Returns (q [B, n, H, D],
+    kbar [B, n // r, D]) in the input dtype; ``out`` may hold both."""
+    lib = load_library()
+    _require_gpu(q_proj, "q_proj")
+    B, n, H, D = q_proj.shape
+    dev, dt = q_proj.device, q_proj.dtype
+    _check(k_proj, "k_proj", (B, n, D), dt, dev)
+    _check(q_weight, "q_weight", (D,), torch.float32, dev)
+    _check(k_weight, "k_weight", (D,), torch.float32, dev)
+    if out is None:
+        out = (torch.empty((B, n, H, D), dtype=dt, device=dev), torch.empty((B, n // r, D), dtype=dt, device=dev))
+    q, kbar = out
+    _check(q, "q", (B, n, H, D), dt, dev)
+    _check(kbar, "kbar", (B, n // r, D), dt, dev)
+    st = lib.gdn_qsa_prep(_ptr(q_proj), _ptr(k_proj), _ptr(q_weight), _ptr(k_weight), _ptr(q), _ptr(kbar),
+                          B, n, H, D, r, rope_dims, float(rope_base), float(eps), _dtype_code(q_proj),
+                          _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_qsa_prep")
+    return q, kbar
+
+
+def gdn_qsa_select_workspace_bytes(B, n, H, D, r, K, dtype):
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(load_library().gdn_qsa_select_workspace_bytes(B, n, H, D, r, K, code))
+
+
+def gdn_qsa_select(q, kbar, r=4, K=2048, block_idx=None, workspace=None, stream=None):
+    """Top-ceil(K / r) complete key blocks per query.  q [B, n, H, D], kbar
+    [B, n // r, D] (bf16 or fp32).  Returns block_idx [B, n, ceil(K / r)] int32,
+    ascending, -1 padded."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    B, n, H, D = q.shape
+    dev = q.device
+    KB = -(-K // r)
+    _check(kbar, "kbar", (B, n // r, D), q.dtype, dev)
+    if block_idx is None:
+        block_idx = torch.empty((B, n, KB), dtype=torch.int32, device=dev)
+    _check(block_idx, "block_idx", (B, n, KB), torch.int32, dev)
+    code = _dtype_code(q)
+    need = int(lib.gdn_qsa_select_workspace_bytes(B, n, H, D, r, K, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_qsa_select(_ptr(q), _ptr(kbar), _ptr(block_idx), B, n, H, D, r, K, code, _ptr(workspace),
+                            ws_bytes, _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_qsa_select")
+    return block_idx

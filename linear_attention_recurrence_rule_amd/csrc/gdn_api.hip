@@ -221,6 +221,62 @@ gdn_status gdn_decode_mtp_commit(const void* k, const float* alpha, const float*
     return from_hip(gdn::launch_mtp(a));
 }
 
+namespace {
+
+bool qsa_dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
+
+gdn_status qsa_select_check(int B, int n, int H, int D, int r, int K, gdn_dtype dtype) {
+    if (!dtype_ok(dtype)) return GDN_ERR_DTYPE;
+    if (B <= 0 || n < 0 || H <= 0 || r < 1 || K < 1) return GDN_ERR_SHAPE;
+    if (!qsa_dim_ok(D) || B > 65535) return GDN_ERR_UNSUPPORTED;
+    const long long nb = n / r;
+    if (!fits(B, n, H, D) || !fits(B, n, (nb + 63) / 64 * 64, 4) || !fits(B, n, (K + r - 1) / r, 4))
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status gdn_qsa_prep(const void* q_proj, const void* k_proj, const float* q_weight, const float* k_weight,
+                        void* q_out, void* kbar_out, int B, int n, int H, int D, int r, int rope_dims,
+                        float rope_base, float eps, gdn_dtype io_dtype, void* hip_stream) {
+    if (!dtype_ok(io_dtype)) return GDN_ERR_DTYPE;
+    if (B <= 0 || n < 0 || H <= 0 || r < 1 || rope_dims < 0 || (rope_dims & 1) || !(eps >= 0.f) ||
+        !(rope_base > 0.f))
+        return GDN_ERR_SHAPE;
+    if (!qsa_dim_ok(D) || rope_dims > D) return GDN_ERR_UNSUPPORTED;
+    if (!fits(B, n, H, D) || (static_cast<long long>(B) * n * (H + 1) + 3) / 4 > INT_MAX) return GDN_ERR_UNSUPPORTED;
+    if (n == 0) return GDN_OK;
+    if (!q_proj || !k_proj || !q_out || !kbar_out) return GDN_ERR_NULL;
+    for (const void* p : {q_proj, k_proj, static_cast<const void*>(q_weight), static_cast<const void*>(k_weight),
+                          static_cast<const void*>(q_out), static_cast<const void*>(kbar_out)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::QsaPrepArgs a{q_proj, k_proj, q_weight, k_weight, q_out, kbar_out, B, n, H, D, r, rope_dims, rope_base,
+                       eps, io_dtype == GDN_BF16, static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_qsa_prep(a));
+}
+
+size_t gdn_qsa_select_workspace_bytes(int B, int n, int H, int D, int r, int K, gdn_dtype dtype) {
+    if (qsa_select_check(B, n, H, D, r, K, dtype) != GDN_OK) return 0;
+    return gdn::qsa_select_workspace_bytes(B, n, r);
+}
+
+gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx, int B, int n, int H, int D, int r, int K,
+                          gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = qsa_select_check(B, n, H, D, r, K, dtype);
+    if (st != GDN_OK) return st;
+    if (n == 0) return GDN_OK;
+    if (!q || !block_idx || (n / r > 0 && !kbar)) return GDN_ERR_NULL;
+    for (const void* p : {q, kbar, static_cast<const void*>(block_idx)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = gdn::qsa_select_workspace_bytes(B, n, r);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return GDN_ERR_ALIGN;
+    gdn::QsaSelectArgs a{q, kbar, block_idx, B, n, H, D, r, (K + r - 1) / r, dtype == GDN_BF16, workspace,
+                         static_cast<hipStream_t>(hip_stream)};
+    return from_hip(gdn::launch_qsa_select(a));
+}
+
 const char* gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "ok";

@@ -113,6 +113,29 @@ struct PrefillBwdArgs {
     hipStream_t stream;
 };
 
+struct QsaPrepArgs {
+    const void* q_proj;         // [B, n, H, D]
+    const void* k_proj;         // [B, n, D]
+    const float* q_weight;      // [D] or null (1)
+    const float* k_weight;      // [D] or null (1)
+    void* q_out;                // [B, n, H, D]
+    void* kbar_out;             // [B, n / r, D]
+    int B, n, H, D, r, rope_dims;
+    float rope_base, eps;
+    bool bf16;
+    hipStream_t stream;
+};
+
+struct QsaSelectArgs {
+    const void* q;              // [B, n, H, D]
+    const void* kbar;           // [B, n / r, D]
+    int* idx;                   // [B, n, KB]
+    int B, n, H, D, r, KB;
+    bool bf16;
+    void* workspace;            // qsa_select_workspace_bytes: the block scores
+    hipStream_t stream;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
@@ -122,5 +145,8 @@ hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_mtp(const MtpArgs& a);
 hipError_t launch_prefill_bwd(const PrefillBwdArgs& a);
 size_t prefill_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_qsa_prep(const QsaPrepArgs& a);
+hipError_t launch_qsa_select(const QsaSelectArgs& a);
+size_t qsa_select_workspace_bytes(int B, int n, int r);
 
 }  // namespace gdn

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["gdn_decode_mtp_commit", "gdn_decode_mtp_verify", "gdn_decode_step",
                                     "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_bwd",
                                     "gdn_prefill_bwd_workspace_bytes", "gdn_prefill_fwd",
-                                    "gdn_prefill_workspace_bytes", "gdn_status_string"]
+                                    "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
+                                    "gdn_qsa_select_workspace_bytes", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -280,3 +281,66 @@ def test_bwd_workspace_bytes():
 
 def test_bwd_empty_sequence_without_state_gradient_is_a_no_op():
     assert _bwd(T=0, q=None, dy=None, dq=None, ws=None, ws_bytes=0) == OK
+
+
+def _qprep(qp=FAKE, kp=FAKE, qw=None, kw=None, qo=FAKE, ko=FAKE, B=1, n=64, H=4, D=128, r=4, R=64,
+           base=10000.0, eps=1e-6, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_qsa_prep(qp, kp, qw, kw, qo, ko, B, n, H, D, r, R, base, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=5), ERR_DTYPE),
+    (dict(B=0), ERR_SHAPE),
+    (dict(n=-1), ERR_SHAPE),
+    (dict(r=0), ERR_SHAPE),
+    (dict(R=3), ERR_SHAPE),
+    (dict(eps=-1.0), ERR_SHAPE),
+    (dict(base=0.0), ERR_SHAPE),
+    (dict(D=96), ERR_UNSUPPORTED),
+    (dict(D=32, R=64), ERR_UNSUPPORTED),
+    (dict(kp=None), ERR_NULL),
+    (dict(ko=None), ERR_NULL),
+    (dict(qw=MISALIGNED), ERR_ALIGN),
+    (dict(qo=MISALIGNED), ERR_ALIGN),
+])
+def test_qsa_prep_rejects(kwargs, status):
+    assert _qprep(**kwargs) == status
+
+
+def test_qsa_prep_empty_is_a_no_op():
+    assert _qprep(n=0, qp=None, kp=None) == OK
+
+
+def _qsel(q=FAKE, kb=FAKE, idx=FAKE, B=1, n=64, H=4, D=128, r=4, K=16, dtype=1, ws=FAKE, ws_bytes=1 << 40):
+    lib = gdn.load_library()
+    return lib.gdn_qsa_select(q, kb, idx, B, n, H, D, r, K, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), ERR_DTYPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(K=0), ERR_SHAPE),
+    (dict(r=0), ERR_SHAPE),
+    (dict(D=48), ERR_UNSUPPORTED),
+    (dict(q=None), ERR_NULL),
+    (dict(idx=None), ERR_NULL),
+    (dict(kb=None), ERR_NULL),
+    (dict(ws=None), ERR_WORKSPACE),
+    (dict(ws_bytes=4), ERR_WORKSPACE),
+    (dict(idx=MISALIGNED), ERR_ALIGN),
+    (dict(ws=MISALIGNED), ERR_ALIGN),
+])
+def test_qsa_select_rejects(kwargs, status):
+    assert _qsel(**kwargs) == status
+
+
+def test_qsa_select_workspace_bytes():
+    lib = gdn.load_library()
+    # n = 100 tokens, r = 4: 25 blocks, rows padded to 64 scores
+    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 128, 4, 2048, 1) == 2 * 100 * 64 * 4
+    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 100, 4, 2048, 1) == 0
+
+
+def test_qsa_select_empty_is_a_no_op():
+    assert _qsel(n=0, q=None, idx=None, ws=None, ws_bytes=0) == OK
