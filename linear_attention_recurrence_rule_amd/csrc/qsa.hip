@@ -197,7 +197,118 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// select: grid (n, B), 256 threads.
+// scores, four query heads: the rows of the query tile are taken in their
+// memory order (query, head), so the four rows a lane holds in each 16x16
+// MFMA output tile are the four heads of one query and the ReLU-sum over
+// heads stays inside the lane.  A workgroup keeps 32 queries (128 rows) in
+// LDS and streams the visible 64-block key tiles through two LDS buffers,
+// loading the next tile into registers while the current one is used.
+// grid (ceil(n / 32), B), 256 threads; the longest query tiles go first.
+// ---------------------------------------------------------------------------
+template <int D, bool kBf16>
+__global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict__ q, const void* __restrict__ kbar,
+                                                         float* __restrict__ scores, int n, int r, int nb, long ldS) {
+    constexpr int TQ = 32, TR = 4 * TQ, TB = 64;
+    constexpr int ES = kBf16 ? 2 : 4;
+    constexpr int LD = D + (kBf16 ? 8 : 4);
+    constexpr int kVec = 16 / ES;                    // elements per 16-byte load
+    constexpr int kKPer = TB * D / kVec / 256;       // 16-byte key loads per thread and tile
+    const int ntq = (n + TQ - 1) / TQ;
+    const int qt = ntq - 1 - static_cast<int>(blockIdx.x), b = blockIdx.y;
+    const int i0 = qt * TQ;
+    const int ilast = min(i0 + TQ, n) - 1;
+    const int mvis = (ilast + 1) / r;                // blocks visible to the tile's last query
+    if (mvis == 0) return;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+
+    __shared__ __align__(16) unsigned char sQ[TR * LD * ES];
+    __shared__ __align__(16) unsigned char sK[2][TB * LD * ES];
+
+    const unsigned char* qb = static_cast<const unsigned char*>(q);
+    const unsigned char* kb = static_cast<const unsigned char*>(kbar);
+    for (int idx = tid; idx < TR * D / kVec; idx += 256) {
+        const int rr = idx / (D / kVec), cc = idx - rr * (D / kVec);
+        const int i = i0 + rr / 4;
+        float4v v = {0.f, 0.f, 0.f, 0.f};
+        if (i < n) v = *reinterpret_cast<const float4v*>(qb + ((static_cast<long>(b) * n + i0) * 4 * D + rr * D + cc * kVec) * ES);
+        *reinterpret_cast<float4v*>(sQ + (rr * LD + cc * kVec) * ES) = v;
+    }
+    float4v pre[kKPer];
+    auto fetch = [&](int bt) {
+#pragma unroll
+        for (int u = 0; u < kKPer; ++u) {
+            const int idx = tid + 256 * u, rr = idx / (D / kVec), cc = idx - rr * (D / kVec);
+            const int blk = min(bt * TB + rr, nb - 1);
+            pre[u] = *reinterpret_cast<const float4v*>(kb + ((static_cast<long>(b) * nb + blk) * D + cc * kVec) * ES);
+        }
+    };
+    auto publish = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kKPer; ++u) {
+            const int idx = tid + 256 * u, rr = idx / (D / kVec), cc = idx - rr * (D / kVec);
+            *reinterpret_cast<float4v*>(sK[buf] + (rr * LD + cc * kVec) * ES) = pre[u];
+        }
+    };
+    const int nbt = (mvis + TB - 1) / TB;
+    fetch(0);
+    publish(0);
+    __syncthreads();
+    for (int bt = 0; bt < nbt; ++bt) {
+        const int buf = bt & 1;
+        fetch(bt + 1 < nbt ? bt + 1 : bt);
+        const int b0 = bt * TB;
+        float4v acc[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBf16) {
+            const __bf16* A = reinterpret_cast<const __bf16*>(sQ) + (32 * wave + (l & 15)) * LD + 8 * (l >> 4);
+            const __bf16* Bt = reinterpret_cast<const __bf16*>(sK[buf]) + (l & 15) * LD + 8 * (l >> 4);
+#pragma unroll
+            for (int k = 0; k < D; k += 32) {
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(A + k);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(A + 16 * LD + k);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bt + 16 * nt * LD + k);
+                    acc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bv, acc[0][nt], 0, 0, 0);
+                    acc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[1][nt], 0, 0, 0);
+                }
+            }
+        } else {
+            const float* A = reinterpret_cast<const float*>(sQ) + (32 * wave + (l & 15)) * LD + (l >> 4) * (D / 4);
+            const float* Bt = reinterpret_cast<const float*>(sK[buf]) + (l & 15) * LD + (l >> 4) * (D / 4);
+#pragma unroll 8
+            for (int k = 0; k < D / 4; ++k) {
+                const float a0 = A[k], a1 = A[16 * LD + k];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const float bv = Bt[16 * nt * LD + k];
+                    acc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0][nt], 0, 0, 0);
+                    acc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][nt], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int i = i0 + 8 * wave + 4 * mt + (l >> 4);
+            const int vis = (i + 1) / r;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int blk = b0 + 16 * nt + (l & 15);
+                const float sc = fmaxf(acc[mt][nt][0], 0.f) + fmaxf(acc[mt][nt][1], 0.f) +
+                                 fmaxf(acc[mt][nt][2], 0.f) + fmaxf(acc[mt][nt][3], 0.f);
+                if (i < n && blk < vis) scores[(static_cast<long>(b) * n + i) * ldS + blk] = sc;
+            }
+        }
+        publish(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// select: grid (ceil(n / 4), B), 256 threads, one wave per query.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned order_key(float f) {   // order-preserving bits of a float
     const unsigned u = __float_as_uint(f);
@@ -497,7 +608,10 @@ static hipError_t launch_qsa_select_t(const QsaSelectArgs& a) {
     const int nb = a.n / a.r;
     const long ld = (nb + 63) / 64 * 64;
     float* scores = static_cast<float*>(a.workspace);
-    if (nb > 0)
+    if (nb > 0 && a.H == 4)
+        hipLaunchKernelGGL((qsa::qsa_score4_kernel<D, kBf16>), dim3((a.n + 31) / 32, a.B), dim3(256), 0, a.stream, a.q,
+                           a.kbar, scores, a.n, a.r, nb, ld);
+    else if (nb > 0)
         hipLaunchKernelGGL((qsa::qsa_score_kernel<D, kBf16>), dim3((a.n + 63) / 64, (nb + 63) / 64, a.B), dim3(256), 0,
                            a.stream, a.q, a.kbar, scores, a.n, a.H, a.r, nb, ld);
     hipLaunchKernelGGL(qsa::qsa_select_kernel, dim3((a.n + 3) / 4, a.B), dim3(256), 0, a.stream, scores, a.idx, a.n,
