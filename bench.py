@@ -119,6 +119,7 @@ def main():
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-qsa", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -407,6 +408,52 @@ def main():
                               "tokens_per_s": B * T / (fe_ms * 1e-3)}
         log(f"front end {fe_ms * 1e3:.1f} us, {fe_bytes / (fe_ms * 1e-3) / 1e9:.0f} GB/s")
         del fe, outs
+        torch.cuda.empty_cache()
+
+    # ---------------- QSA indexer: 64K tokens, 4 query heads, r = 4, K = 2048 ----------------
+    if not args.no_qsa:
+        nq, Hq, Dq, rq, Kq = 65536, 4, 128, 4, 2048
+        log(f"qsa indexer: n={nq} H={Hq} D={Dq} r={rq} K={Kq}")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(13)
+        qp = torch.randn((1, nq, Hq, Dq), generator=gen, device=dev).to(torch.bfloat16)
+        kp = torch.randn((1, nq, Dq), generator=gen, device=dev).to(torch.bfloat16)
+        qo = torch.empty_like(qp)
+        ko = torch.empty((1, nq // rq, Dq), dtype=torch.bfloat16, device=dev)
+        KBq = -(-Kq // rq)
+        idx = torch.empty((1, nq, KBq), dtype=torch.int32, device=dev)
+        wsq = torch.empty(gdn.gdn_qsa_select_workspace_bytes(1, nq, Hq, Dq, rq, Kq, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+
+        def prep():
+            gdn.gdn_qsa_prep(qp, kp, r=rq, out=(qo, ko), stream=stream)
+
+        def select():
+            gdn.gdn_qsa_select(qo, ko, r=rq, K=Kq, block_idx=idx, workspace=wsq, stream=stream)
+
+        def time_it(fn, reps=10):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        p_ms, s_ms = time_it(prep), time_it(select)
+        cand = sum((i + 1) // rq for i in range(nq))          # scored (query, block) pairs
+        flops = cand * Hq * Dq * 2
+        prep_bytes = (nq * Hq * Dq + nq * Dq) * 2 + (nq * Hq * Dq + (nq // rq) * Dq) * 2
+        result["qsa"] = {"workload": f"QSA indexer, n={nq} tokens, {Hq} query heads, D={Dq}, r={rq}, K={Kq}, bf16",
+                         "prep_ms": p_ms, "prep_GBps": prep_bytes / (p_ms * 1e-3) / 1e9,
+                         "select_ms": s_ms, "scored_pairs": cand,
+                         "score_tflops_over_select": flops / (s_ms * 1e-3) / 1e12,
+                         "queries_per_s": nq / ((p_ms + s_ms) * 1e-3)}
+        log(f"qsa prep {p_ms * 1e3:.1f} us, select {s_ms:.3f} ms ({flops / (s_ms * 1e-3) / 1e12:.1f} TFLOP/s "
+            f"of score work over the whole select)")
+        del qp, kp, qo, ko, idx, wsq
         torch.cuda.empty_cache()
 
     # ---------------- float64 CPU oracle on a bounded sample ----------------
