@@ -346,21 +346,32 @@ def main():
         def round_(r):
             verify(r)
             commit(r)
-        v_ms, c_ms, r_ms = timed(verify), timed(commit), timed(round_)
+
+        e_prev = torch.zeros_like(em)
+
+        def fused(r):
+            # commit block r - 1 (all accepted) and verify block r in one pass
+            q_, k_, v_, a_, b_ = blocks[r % len(blocks)]
+            _, pk_, _, pa_, pb_ = blocks[(r - 1) % len(blocks)]
+            gdn.gdn_decode_mtp_commit_verify(q_, k_, v_, a_, b_, state, pk_, pa_, pb_, e_prev, all_acc, y=ym,
+                                             e=e_prev, stream=stream)
+        v_ms, c_ms, r_ms, f_ms = timed(verify), timed(commit), timed(round_), timed(fused)
         sb = N * H3 * d3 * d3 * 4
         tok_io = N * H3 * K * (3 * d3 * 2 + 8)
         v_bytes = sb + tok_io + 2 * N * H3 * K * d3 * 4                  # state, q/k/v/gates, y and e
         c_bytes = 2 * sb + N * H3 * K * (d3 * 2 + 8 + d3 * 4)              # state in/out, k, gates, e
         result["mtp"] = {"workload": f"multi-token decode, {N} sequences x {H3} heads, d={d3}, {K}-token drafts, "
                                      "all accepted", "verify_us": v_ms * 1e3, "commit_us": c_ms * 1e3,
-                         "round_us": r_ms * 1e3,
+                         "round_us": r_ms * 1e3, "fused_round_us": f_ms * 1e3,
+                         "fused_round_GBps": (2 * sb + tok_io + 2 * N * H3 * K * d3 * 4) / (f_ms * 1e-3) / 1e9,
                          "verify_GBps": v_bytes / (v_ms * 1e-3) / 1e9,
                          "verify_frac": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                          "commit_GBps": c_bytes / (c_ms * 1e-3) / 1e9,
                          "commit_frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "tokens_per_s": N * K / (r_ms * 1e-3)}
+                         "tokens_per_s": N * K / (f_ms * 1e-3)}
         log(f"mtp verify {v_ms * 1e3:.1f} us ({v_bytes / (v_ms * 1e-3) / 1e9:.0f} GB/s), "
-            f"commit {c_ms * 1e3:.1f} us ({c_bytes / (c_ms * 1e-3) / 1e9:.0f} GB/s), round {r_ms * 1e3:.1f} us")
+            f"commit {c_ms * 1e3:.1f} us ({c_bytes / (c_ms * 1e-3) / 1e9:.0f} GB/s), round {r_ms * 1e3:.1f} us, "
+            f"fused round {f_ms * 1e3:.1f} us")
         del state, blocks, ym, em
         torch.cuda.empty_cache()
 

@@ -165,6 +165,31 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
                             gdn_dtype io_dtype, float norm_eps, void* hip_stream);
 
 /*
+ * Multi-token decode, both parts in one pass over the state: commit the
+ * accepted prefix of the previous verified block (exactly as
+ * gdn_decode_mtp_commit with prev_k, prev_alpha, prev_beta, prev_e,
+ * prev_accepted and K_prev), then verify the new block from the committed
+ * state (exactly as gdn_decode_mtp_verify, without prefix states).  The state
+ * is read once and written once (not at all for sequences with nothing
+ * accepted), so a draft round costs one state round trip instead of three.
+ *
+ *   q, k, v, alpha, beta   the new block, [N, K, H, ...] as for verify
+ *   state                  [N, H, d_k, d_v] float32, updated in place by the commit
+ *   y, e                   the new block's outputs and misses (e may be NULL);
+ *                          e may be the same buffer as prev_e
+ *   prev_*                 the previous block, [N, K_prev, H, ...], and its
+ *                          accepted counts [N] int32 (clamped to 0..K_prev)
+ *   K, K_prev in 1..8.
+ */
+gdn_status gdn_decode_mtp_commit_verify(const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta,
+                                        float* state, float* y, float* e,
+                                        const void* prev_k, const float* prev_alpha, const float* prev_beta,
+                                        const float* prev_e, const int* prev_accepted,
+                                        int N, int K, int K_prev, int H, int d_k, int d_v,
+                                        gdn_dtype qkv_dtype, float scale, void* hip_stream);
+
+/*
  * Backward of gdn_prefill_fwd (the chain rule through the delta form of the
  * slinene page, Module A; the pages mention a backward kernel only as part
  * of the FlashQLA library).  For the loss L = sum <dy, y> + <d_final_state,

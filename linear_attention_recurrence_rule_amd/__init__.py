@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
     "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
-    "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit",
+    "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit", "gdn_decode_mtp_commit_verify",
     "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
     "gdn_qsa_select_workspace_bytes", "gdn_status_string",
 ]
@@ -69,6 +69,9 @@ def load_library():
     lib.gdn_decode_mtp_verify.restype = ctypes.c_int
     lib.gdn_decode_mtp_commit.argtypes = [vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, vp]
     lib.gdn_decode_mtp_commit.restype = ctypes.c_int
+    lib.gdn_decode_mtp_commit_verify.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, fp, vp,
+                                                 i, i, i, i, i, i, i, f, vp]
+    lib.gdn_decode_mtp_commit_verify.restype = ctypes.c_int
     lib.gdn_prefill_bwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                     i, i, i, i, i, i, f, vp, sz, vp]
     lib.gdn_prefill_bwd.restype = ctypes.c_int
@@ -419,3 +422,42 @@ def gdn_qsa_select(q, kbar, r=4, K=2048, block_idx=None, workspace=None, stream=
     if st:
         raise GdnError(st, "gdn_qsa_select")
     return block_idx
+
+
+def gdn_decode_mtp_commit_verify(q, k, v, alpha, beta, state, prev_k, prev_alpha, prev_beta, prev_e,
+                                 prev_accepted, y=None, e=None, scale=1.0, return_e=True, stream=None):
+    """Commit the previous block's accepted drafts onto ``state`` (in place) and
+    verify the new block from the committed state, in one pass over the state.
+    New block: q, k [N, K, H, d_k]; v [N, K, H, d_v]; alpha, beta [N, K, H].
+    Previous block: prev_k [N, K_prev, H, d_k]; prev_alpha, prev_beta
+    [N, K_prev, H]; prev_e [N, K_prev, H, d_v]; prev_accepted [N] int32.
+    Returns (y, e) of the new block."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    Kp = prev_k.shape[1]
+    dev = q.device
+    _check(k, "k", (N, K, H, dk), q.dtype, dev)
+    _check(v, "v", (N, K, H, dv), q.dtype, dev)
+    _check(alpha, "alpha", (N, K, H), torch.float32, dev)
+    _check(beta, "beta", (N, K, H), torch.float32, dev)
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    _check(prev_k, "prev_k", (N, Kp, H, dk), q.dtype, dev)
+    _check(prev_alpha, "prev_alpha", (N, Kp, H), torch.float32, dev)
+    _check(prev_beta, "prev_beta", (N, Kp, H), torch.float32, dev)
+    _check(prev_e, "prev_e", (N, Kp, H, dv), torch.float32, dev)
+    _check(prev_accepted, "prev_accepted", (N,), torch.int32, dev)
+    if y is None:
+        y = torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    _check(y, "y", (N, K, H, dv), torch.float32, dev)
+    if e is None and return_e:
+        e = torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    _check(e, "e", (N, K, H, dv), torch.float32, dev)
+    st = lib.gdn_decode_mtp_commit_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(y),
+                                          _ptr(e), _ptr(prev_k), _ptr(prev_alpha), _ptr(prev_beta), _ptr(prev_e),
+                                          _ptr(prev_accepted), N, K, Kp, H, dk, dv, _dtype_code(q), float(scale),
+                                          _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_decode_mtp_commit_verify")
+    return y, e

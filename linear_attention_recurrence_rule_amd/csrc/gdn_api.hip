@@ -277,6 +277,35 @@ gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx, int B
     return from_hip(gdn::launch_qsa_select(a));
 }
 
+gdn_status gdn_decode_mtp_commit_verify(const void* q, const void* k, const void* v, const float* alpha,
+                                        const float* beta, float* state, float* y, float* e, const void* prev_k,
+                                        const float* prev_alpha, const float* prev_beta, const float* prev_e,
+                                        const int* prev_accepted, int N, int K, int K_prev, int H, int d_k, int d_v,
+                                        gdn_dtype qkv_dtype, float scale, void* hip_stream) {
+    gdn_status st = mtp_check(N, K, H, d_k, d_v, qkv_dtype);
+    if (st == GDN_OK) st = mtp_check(N, K_prev, H, d_k, d_v, qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (K < 1 || K_prev < 1) return GDN_ERR_SHAPE;
+    if (N == 0) return GDN_OK;
+    if (!q || !k || !v || !alpha || !beta || !state || !y || !prev_k || !prev_alpha || !prev_beta || !prev_e ||
+        !prev_accepted)
+        return GDN_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
+                          static_cast<const void*>(state), static_cast<const void*>(y), static_cast<const void*>(e),
+                          prev_k, static_cast<const void*>(prev_alpha), static_cast<const void*>(prev_beta),
+                          static_cast<const void*>(prev_e), static_cast<const void*>(prev_accepted)})
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    gdn::MtpArgs a{false, q, k, v, alpha, beta, state, y, e, nullptr, nullptr, N, K, H, d_k, d_v,
+                   qkv_dtype == GDN_BF16, scale, static_cast<hipStream_t>(hip_stream)};
+    a.pend_k = prev_k;
+    a.pend_alpha = prev_alpha;
+    a.pend_beta = prev_beta;
+    a.pend_e = prev_e;
+    a.pend_accepted = prev_accepted;
+    a.Kp = K_prev;
+    return from_hip(gdn::launch_mtp(a));
+}
+
 const char* gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "ok";

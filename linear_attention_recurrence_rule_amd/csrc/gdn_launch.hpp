@@ -89,6 +89,13 @@ struct MtpArgs {
     bool bf16;
     float scale;
     hipStream_t stream;
+    // verify after committing a previous block (all null for a plain verify)
+    const void* pend_k = nullptr;        // [N, Kp, H, d_k]
+    const float* pend_alpha = nullptr;   // [N, Kp, H]
+    const float* pend_beta = nullptr;
+    const float* pend_e = nullptr;       // [N, Kp, H, d_v]
+    const int* pend_accepted = nullptr;  // [N]
+    int Kp = 0;
 };
 
 struct PrefillBwdArgs {

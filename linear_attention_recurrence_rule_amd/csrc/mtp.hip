@@ -60,12 +60,25 @@ __device__ __forceinline__ float row16_sum(float x) {
 // padding: zero q, k, v, alpha = 1, beta = 0, outputs not written).
 // kPrefix: also write every prefix state (keeps the state slice in registers
 // to the end; without it the slice dies after the column sums).
-template <int DK, int DV, int KM, bool kBf16, bool kPrefix>
+// kCommit: first commit the accepted prefix of the previous block (pk, pa,
+// pb, pe, pacc; Kp tokens) onto the state slice in registers and write it
+// back, then verify the new block from the committed state: one read and at
+// most one write of the state for a whole draft round.
+struct PendingBlock {
+    const void* k;          // [N, Kp, H, d_k]
+    const float* alpha;     // [N, Kp, H]
+    const float* beta;
+    const float* e;         // [N, Kp, H, d_v]
+    const int* accepted;    // [N]
+    int Kp;
+};
+
+template <int DK, int DV, int KM, bool kBf16, bool kPrefix, bool kCommit = false>
 __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ state,
+    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
     float* __restrict__ y, float* __restrict__ e_out, float* __restrict__ prefix, int K, int H,
-    float scale) {
+    float scale, PendingBlock pend) {
     using Sh = MtpShape<DK, DV>;
     constexpr int KQ = 2 * KM;                 // k_0..k_{KM-1}, q_0..q_{KM-1}
     constexpr int kIn = (KQ * DK + Sh::kThreads - 1) / Sh::kThreads;
@@ -111,13 +124,45 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
     const float ain = tid < K ? a_ld : 1.f;
     const float bin = tid < K ? b_ld : 0.f;
 
+    // the previous block's accepted writes (kCommit): u_t = beta_t e_t times
+    // the decay still to come within the accepted prefix, and its keys
+    constexpr int kPin = (KM * DK + Sh::kThreads - 1) / Sh::kThreads;
+    int jacc = 0;
+    float Gp = 1.f;
+    float4v pu[KM];
+    float xpk[kPin];
+    if constexpr (kCommit) {
+        jacc = pend.accepted[n];
+        jacc = jacc < 0 ? 0 : (jacc > pend.Kp ? pend.Kp : jacc);
+#pragma unroll
+        for (int t = KM - 1; t >= 0; --t) {
+            pu[t] = float4v{0.f, 0.f, 0.f, 0.f};
+            if (t < jacc) {
+                const long gp = static_cast<long>(n * pend.Kp + t) * H + h;
+                const float4v et = *reinterpret_cast<const float4v*>(pend.e + gp * DV + 4 * cg);
+                pu[t] = (Gp * pend.beta[gp]) * et;
+                Gp *= pend.alpha[gp];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kPin; ++m) {
+            const int i = tid + m * Sh::kThreads;
+            const int ic = i < KM * DK ? i : KM * DK - 1;
+            const int t = ic / DK, r = ic - t * DK;
+            const int tc = t < jacc ? t : 0;
+            const float x = load_in<kBf16>(pend.k, (static_cast<long>(n * pend.Kp + tc) * H + h) * DK + r);
+            xpk[m] = t < jacc ? x : 0.f;
+        }
+    }
+
     // the state slice of this thread: a read-once stream
-    const float4v* S = reinterpret_cast<const float4v*>(state + static_cast<long>(nh) * DK * DV);
+    float4v* S = reinterpret_cast<float4v*>(state + static_cast<long>(nh) * DK * DV);
     float4v s[Sh::kRpt];
 #pragma unroll
     for (int j = 0; j < Sh::kRpt; ++j)
         s[j] = __builtin_nontemporal_load(&S[(rg + j * Sh::kRowGroups) * Sh::kColGroups + cg]);
 
+    __shared__ __align__(16) float skp[kCommit ? DK : 1][KM];       // previous block's keys (kCommit)
     __shared__ __align__(16) float skq[DK][KQ];                    // row r: k_t[r] then q_t[r]
     __shared__ float4v sv[KM][Sh::kColGroups];
     __shared__ float4v red[Sh::kWaves][KQ][Sh::kColGroups];
@@ -140,7 +185,29 @@ __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kerne
         sa[tid] = ain;
         sb[tid] = bin;
     }
+    if constexpr (kCommit) {
+#pragma unroll
+        for (int m = 0; m < kPin; ++m) {
+            const int i = tid + m * Sh::kThreads;
+            const int t = i / DK, r = i - t * DK;
+            if (i < KM * DK) skp[r][t] = xpk[m];
+        }
+    }
     __syncthreads();
+    if constexpr (kCommit) {
+        // commit: S <- G_j S + sum_{t<j} k_t u_t^T, written back when anything was accepted
+        if (jacc > 0) {
+#pragma unroll
+            for (int j = 0; j < Sh::kRpt; ++j) {
+                const int r = rg + j * Sh::kRowGroups;
+                float4v o = Gp * s[j];
+#pragma unroll
+                for (int t = 0; t < KM; ++t) o = fma4(skp[r][t], pu[t], o);
+                s[j] = o;
+                __builtin_nontemporal_store(o, &S[r * Sh::kColGroups + cg]);
+            }
+        }
+    }
 
     // K x K dot products of the block, 16 lanes each: pair (a, b) gives
     // k_a.k_b when a < b and k_b.q_a when a >= b
@@ -309,18 +376,23 @@ static hipError_t launch_mtp_t(const MtpArgs& a) {
     if (a.commit)
         hipLaunchKernelGGL((mtp_commit_kernel<DK, DV, KM, kBf16>), grid, block, 0, a.stream, a.k, a.alpha,
                            a.beta, a.e, a.accepted, a.state, a.K, a.H);
+    else if (a.pend_accepted)
+        hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16, false, true>), grid, block, 0, a.stream, a.q, a.k,
+                           a.v, a.alpha, a.beta, a.state, a.y, a.e, nullptr, a.K, a.H, a.scale,
+                           PendingBlock{a.pend_k, a.pend_alpha, a.pend_beta, a.pend_e, a.pend_accepted, a.Kp});
     else if (a.prefix)
         hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16, true>), grid, block, 0, a.stream, a.q, a.k,
-                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale);
+                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale, PendingBlock{});
     else
         hipLaunchKernelGGL((mtp_verify_kernel<DK, DV, KM, kBf16, false>), grid, block, 0, a.stream, a.q, a.k,
-                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale);
+                           a.v, a.alpha, a.beta, a.state, a.y, a.e, a.prefix, a.K, a.H, a.scale, PendingBlock{});
     return hipGetLastError();
 }
 
 template <int DK, int DV, bool kBf16>
 static hipError_t launch_mtp_k(const MtpArgs& a) {
-    return a.K <= 4 ? launch_mtp_t<DK, DV, 4, kBf16>(a) : launch_mtp_t<DK, DV, 8, kBf16>(a);
+    const int km = a.pend_accepted && a.Kp > a.K ? a.Kp : a.K;
+    return km <= 4 ? launch_mtp_t<DK, DV, 4, kBf16>(a) : launch_mtp_t<DK, DV, 8, kBf16>(a);
 }
 
 template <bool kBf16>

@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gdn_decode_mtp_commit", "gdn_decode_mtp_verify", "gdn_decode_step",
+    assert declared_functions() == ["gdn_decode_mtp_commit", "gdn_decode_mtp_commit_verify",
+                                    "gdn_decode_mtp_verify", "gdn_decode_step",
                                     "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_bwd",
                                     "gdn_prefill_bwd_workspace_bytes", "gdn_prefill_fwd",
                                     "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
@@ -344,3 +345,31 @@ def test_qsa_select_workspace_bytes():
 
 def test_qsa_select_empty_is_a_no_op():
     assert _qsel(n=0, q=None, idx=None, ws=None, ws_bytes=0) == OK
+
+
+def _cv(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, y=FAKE, e=None, pk=FAKE, pa=FAKE, pb=FAKE, pe=FAKE,
+        pacc=FAKE, N=4, K=4, Kp=4, H=2, dk=128, dv=128, dtype=1):
+    lib = gdn.load_library()
+    return lib.gdn_decode_mtp_commit_verify(q, k, v, a, b, s, y, e, pk, pa, pb, pe, pacc, N, K, Kp, H, dk, dv,
+                                            dtype, 1.0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=3), ERR_DTYPE),
+    (dict(K=0), ERR_SHAPE),
+    (dict(Kp=0), ERR_SHAPE),
+    (dict(N=-1), ERR_SHAPE),
+    (dict(Kp=9), ERR_UNSUPPORTED),
+    (dict(dk=24), ERR_UNSUPPORTED),
+    (dict(pe=None), ERR_NULL),
+    (dict(pacc=None), ERR_NULL),
+    (dict(s=None), ERR_NULL),
+    (dict(pk=MISALIGNED), ERR_ALIGN),
+    (dict(e=MISALIGNED), ERR_ALIGN),
+])
+def test_mtp_commit_verify_rejects(kwargs, status):
+    assert _cv(**kwargs) == status
+
+
+def test_mtp_commit_verify_empty_is_a_no_op():
+    assert _cv(N=0, q=None, s=None) == OK

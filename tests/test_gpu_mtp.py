@@ -150,3 +150,63 @@ def test_decode_workload_full_shape():
                 check(f"prefix states seq {n}", host(pref[n:n + 1]), p_ref, MTP_TOL)
             del pref
         S = S_new
+
+
+@pytest.mark.parametrize("K,Kp", [(4, 4), (5, 3), (1, 8)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_commit_verify_equals_commit_then_verify(K, Kp, dtype):
+    """The fused call: commit the previous block's accepted prefix, then verify
+    the new block, against the oracle's commit followed by its verify."""
+    say(f"mtp commit+verify K={K} Kp={Kp} {dtype}")
+    N, H, d_ = 6, 3, 128
+    prev, S0 = _block(N, Kp, H, d_, d_, dtype, seed=40 + K)
+    new, _ = _block(N, K, H, d_, d_, dtype, seed=50 + Kp)
+    _, pe_ref, _ = mtp_verify(prev["q"], prev["k"], prev["v"], prev["alpha"], prev["beta"], S0)
+    acc = np.array([0, Kp, 1, Kp // 2, 7, -2], dtype=np.int32)
+    state = dev(S0)
+    y, e = gdn.gdn_decode_mtp_commit_verify(*_gpu_block(new, dtype), state, dev(prev["k"], dtype),
+                                            dev(prev["alpha"]), dev(prev["beta"]), dev(pe_ref),
+                                            torch.from_numpy(acc).cuda(), scale=0.9)
+    S1 = mtp_commit(prev["k"], prev["alpha"], prev["beta"], pe_ref, np.clip(acc, 0, Kp), S0)
+    y_ref, e_ref, _ = mtp_verify(new["q"], new["k"], new["v"], new["alpha"], new["beta"], S1, scale=0.9)
+    check("committed state", host(state), S1, MTP_TOL)
+    check("y", host(y), y_ref, MTP_TOL)
+    check("e", host(e), e_ref, MTP_TOL)
+    np.testing.assert_array_equal(host(state)[0], S0[0].astype(np.float64))    # nothing accepted: untouched
+
+
+def test_fused_rounds_follow_the_accepted_tokens():
+    """Rounds of the fused call (each commits the previous round's accepted
+    drafts), with a final plain commit: outputs of accepted drafts and the final
+    state equal one recurrence over the accepted tokens only."""
+    say("mtp fused rounds")
+    N, K, H, d_ = 4, 4, 3, 64
+    rng = np.random.default_rng(77)
+    S0 = (0.2 * rng.standard_normal((N, H, d_, d_))).astype(np.float32)
+    state = dev(S0)
+    kept = [{x: [] for x in ("q", "k", "v", "alpha", "beta", "y")} for _ in range(N)]
+    prev = None
+    for rnd in range(5):
+        d = prefill_inputs(N, K, H, d_, d_, "bf16", -1.0, 0.5, seed=[77, rnd])
+        blk = _gpu_block(d, "bf16")
+        if prev is None:
+            y, e, _ = gdn.gdn_decode_mtp_verify(*blk, state)
+        else:
+            pk, pa, pb, pe, pacc = prev
+            y, e = gdn.gdn_decode_mtp_commit_verify(*blk, state, pk, pa, pb, pe, pacc)
+        acc = rng.integers(0, K + 1, size=N).astype(np.int32)
+        prev = (blk[1], blk[3], blk[4], e, torch.from_numpy(acc).cuda())
+        yh = host(y)
+        for n in range(N):
+            for x in ("q", "k", "v", "alpha", "beta"):
+                kept[n][x].append(d[x][n, :acc[n]])
+            kept[n]["y"].append(yh[n, :acc[n]])
+    pk, pa, pb, pe, pacc = prev
+    gdn.gdn_decode_mtp_commit(pk, pa, pb, pe, pacc, state)
+    S_gpu = host(state)
+    for n in range(N):
+        cat = {x: np.concatenate(kept[n][x], axis=0)[None] for x in kept[n]}
+        y_ref, S_ref = gated_delta_recurrence(cat["q"], cat["k"], cat["v"], cat["alpha"], cat["beta"], S0[n:n + 1])
+        if cat["q"].shape[1]:
+            check(f"seq {n} accepted y", cat["y"], y_ref, MTP_TOL)
+        check(f"seq {n} state", S_gpu[n:n + 1], S_ref, MTP_TOL)
