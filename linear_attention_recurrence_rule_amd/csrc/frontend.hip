@@ -120,6 +120,20 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         }
     }
 
+    // the gate logits of the run, one token per lane (several when the row
+    // group has fewer lanes than the run has tokens), loaded up front
+    constexpr int kGPer = kGates ? (kRun + LPR - 1) / LPR : 1;
+    float al[kGPer], bl[kGPer];
+    if constexpr (kGates) {
+#pragma unroll
+        for (int u = 0; u < kGPer; ++u) {
+            const int t = min(t0 + sub + u * LPR, t1 - 1);
+            const long g = (static_cast<long>(b) * T + t) * H + h;
+            al[u] = a_logit[g];
+            bl[u] = b_logit[g];
+        }
+    }
+
     // kStep tokens per step, independent of each other given the inputs, so
     // their reductions overlap; the next step's rows are loaded meanwhile.
     // Offsets inside the run are 32-bit (a run spans kRun rows).
@@ -157,13 +171,6 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 #pragma unroll
         for (int u = 0; u < kStep; ++u)
             if (r0 + u <= last) store4<kBf16>(out, run_base + (r0 + u) * rs, s[u]);
-        if constexpr (kGates) {
-            if (sub < kStep && r0 + sub <= last) {
-                const long g = (static_cast<long>(b) * T + t0 + r0 + sub) * H + h;
-                beta[g] = sigmoid(b_logit[g]);
-                alpha[g] = __expf(-__expf(A[h]) * softplus(a_logit[g] + b_alpha[h]));
-            }
-        }
         // the window moves to the last W-1 rows of this step
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
@@ -177,6 +184,18 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
     for (int r0 = 0; r0 <= last; r0 += 2 * kStep) {
         step(ra, rb, r0);
         if (r0 + kStep <= last) step(rb, ra, r0 + kStep);
+    }
+    if constexpr (kGates) {
+        const float ea = __expf(A[h]), ba = b_alpha[h];
+#pragma unroll
+        for (int u = 0; u < kGPer; ++u) {
+            const int t = t0 + sub + u * LPR;
+            if (t < t1) {
+                const long g = (static_cast<long>(b) * T + t) * H + h;
+                beta[g] = sigmoid(bl[u]);
+                alpha[g] = __expf(-ea * softplus(al[u] + ba));
+            }
+        }
     }
 }
 
