@@ -307,7 +307,8 @@ gdn_status gdn_qsa_prep(const void* q_proj, const void* k_proj,
  *   block_idx    [B, n, K_B]   int32 out: selected blocks in ascending order,
  *                padded with -1
  *   workspace    caller-owned, >= gdn_qsa_select_workspace_bytes(...) bytes:
- *                the fp32 block scores, B n ceil(n / r / 64) 64 4 bytes
+ *                the fp32 block scores, B n ceil(n / r / 64) 64 4 bytes,
+ *                then the per-query maxima, B n 4 bytes rounded up to 256
  *   D in {32, 64, 128}; r >= 1; K >= 1.
  */
 gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx,

@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const void* __restrict__
 // ---------------------------------------------------------------------------
 template <int D, bool kBf16>
 __global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict__ q, const void* __restrict__ kbar,
-                                                         float* __restrict__ scores, int n, int r, int nb, long ldS) {
+                                                         float* __restrict__ scores, float* __restrict__ rowmax, int n,
+                                                         int r, int nb, long ldS) {
     constexpr int TQ = 32, TR = 4 * TQ, TB = 64;
     constexpr int ES = kBf16 ? 2 : 4;
     constexpr int LD = D + (kBf16 ? 8 : 4);
@@ -223,6 +224,7 @@ __global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict_
 
     __shared__ __align__(16) unsigned char sQ[TR * LD * ES];
     __shared__ __align__(16) unsigned char sK[2][TB * LD * ES];
+    __shared__ __align__(16) float sOut[4][8][TB + 4];          // each wave's 8 rows of the tile's scores
 
     const unsigned char* qb = static_cast<const unsigned char*>(q);
     const unsigned char* kb = static_cast<const unsigned char*>(kbar);
@@ -250,6 +252,7 @@ __global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict_
         }
     };
     const int nbt = (mvis + TB - 1) / TB;
+    float rmax[2] = {0.f, 0.f};
     fetch(0);
     publish(0);
     __syncthreads();
@@ -290,6 +293,10 @@ __global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict_
                 }
             }
         }
+        // the tile's scores go out as whole 256-byte row pieces through a
+        // wave-private LDS staging area, with streaming stores; entries past a
+        // row's visible blocks are written too (within the row's padded
+        // storage) and never read
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int i = i0 + 8 * wave + 4 * mt + (l >> 4);
@@ -299,11 +306,37 @@ __global__ __launch_bounds__(256) void qsa_score4_kernel(const void* __restrict_
                 const int blk = b0 + 16 * nt + (l & 15);
                 const float sc = fmaxf(acc[mt][nt][0], 0.f) + fmaxf(acc[mt][nt][1], 0.f) +
                                  fmaxf(acc[mt][nt][2], 0.f) + fmaxf(acc[mt][nt][3], 0.f);
-                if (i < n && blk < vis) scores[(static_cast<long>(b) * n + i) * ldS + blk] = sc;
+                if (blk < vis) rmax[mt] = fmaxf(rmax[mt], sc);
+                sOut[wave][4 * mt + (l >> 4)][16 * nt + (l & 15)] = sc;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int f = l + 64 * p, row = f >> 4, c4 = f & 15;
+            const int i = i0 + 8 * wave + row;
+            if (i < n)
+                __builtin_nontemporal_store(*reinterpret_cast<const float4v*>(&sOut[wave][row][4 * c4]),
+                                            reinterpret_cast<float4v*>(&scores[(static_cast<long>(b) * n + i) * ldS + b0 + 4 * c4]));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         publish(buf ^ 1);
         __syncthreads();
+    }
+    // per-row maximum of the visible scores (16 lanes share a row)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        float x = rmax[mt];
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));
+        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false)));
+        const int i = i0 + 8 * wave + 4 * mt + (l >> 4);
+        if ((l & 15) == 0 && i < n) rowmax[static_cast<long>(b) * n + i] = x;
     }
 }
 
@@ -477,7 +510,8 @@ __device__ void radix_cut_wave(const float* row, int m, int KB, unsigned* hist, 
 // bin's candidates (a handful for continuous scores) are ranked against each
 // other by (score, index) to find the cut; more than 64 of them fall back to
 // the exact radix select.  The selected blocks then go out in ascending order.
-__global__ __launch_bounds__(256) void qsa_select_kernel(const float* __restrict__ scores, int* __restrict__ idx,
+__global__ __launch_bounds__(256) void qsa_select_kernel(const float* __restrict__ scores,
+                                                         const float* __restrict__ rowmax, int* __restrict__ idx,
                                                          int n, int r, int KB, long ldS) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i = blockIdx.x * 4 + w, b = blockIdx.y;
@@ -495,9 +529,13 @@ __global__ __launch_bounds__(256) void qsa_select_kernel(const float* __restrict
     unsigned* hist = shist[w];
 
     float mx = 0.f;
-    for_each_score(row, m, [&](int, float v) { mx = fmaxf(mx, v); });
+    if (rowmax) {
+        mx = rowmax[static_cast<long>(b) * n + i];   // from the scoring pass
+    } else {
+        for_each_score(row, m, [&](int, float v) { mx = fmaxf(mx, v); });
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
     for (int j = lane; j < kBins; j += 64) hist[j] = 0;
     wave_sync();
 
@@ -584,10 +622,11 @@ __global__ __launch_bounds__(256) void qsa_select_kernel(const float* __restrict
 
 }  // namespace qsa
 
+// Workspace: the fp32 scores, rows padded to 64 blocks, then the per-row maxima.
 size_t qsa_select_workspace_bytes(int B, int n, int r) {
     const long nb = n / r;
     const long ld = (nb + 63) / 64 * 64;
-    return static_cast<size_t>(B) * n * ld * 4;
+    return static_cast<size_t>(B) * n * ld * 4 + ((static_cast<size_t>(B) * n * 4 + 255) & ~static_cast<size_t>(255));
 }
 
 template <bool kBf16>
@@ -608,14 +647,16 @@ static hipError_t launch_qsa_select_t(const QsaSelectArgs& a) {
     const int nb = a.n / a.r;
     const long ld = (nb + 63) / 64 * 64;
     float* scores = static_cast<float*>(a.workspace);
-    if (nb > 0 && a.H == 4)
+    float* rowmax = scores + static_cast<long>(a.B) * a.n * ld;
+    const bool four = a.H == 4;
+    if (nb > 0 && four)
         hipLaunchKernelGGL((qsa::qsa_score4_kernel<D, kBf16>), dim3((a.n + 31) / 32, a.B), dim3(256), 0, a.stream, a.q,
-                           a.kbar, scores, a.n, a.r, nb, ld);
+                           a.kbar, scores, rowmax, a.n, a.r, nb, ld);
     else if (nb > 0)
         hipLaunchKernelGGL((qsa::qsa_score_kernel<D, kBf16>), dim3((a.n + 63) / 64, (nb + 63) / 64, a.B), dim3(256), 0,
                            a.stream, a.q, a.kbar, scores, a.n, a.H, a.r, nb, ld);
-    hipLaunchKernelGGL(qsa::qsa_select_kernel, dim3((a.n + 3) / 4, a.B), dim3(256), 0, a.stream, scores, a.idx, a.n,
-                       a.r, a.KB, ld);
+    hipLaunchKernelGGL(qsa::qsa_select_kernel, dim3((a.n + 3) / 4, a.B), dim3(256), 0, a.stream, scores,
+                       four ? rowmax : nullptr, a.idx, a.n, a.r, a.KB, ld);
     return hipGetLastError();
 }
 

@@ -338,8 +338,9 @@ def test_qsa_select_rejects(kwargs, status):
 
 def test_qsa_select_workspace_bytes():
     lib = gdn.load_library()
-    # n = 100 tokens, r = 4: 25 blocks, rows padded to 64 scores
-    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 128, 4, 2048, 1) == 2 * 100 * 64 * 4
+    # n = 100 tokens, r = 4: 25 blocks, rows padded to 64 scores,
+    # plus the per-row maxima, padded to 256 bytes
+    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 128, 4, 2048, 1) == 2 * 100 * 64 * 4 + 1024
     assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 100, 4, 2048, 1) == 0
 
 
