@@ -306,9 +306,13 @@ gdn_status gdn_qsa_prep(const void* q_proj, const void* k_proj,
  *   kbar         [B, n / r, D] dtype
  *   block_idx    [B, n, K_B]   int32 out: selected blocks in ascending order,
  *                padded with -1
- *   workspace    caller-owned, >= gdn_qsa_select_workspace_bytes(...) bytes:
- *                the fp32 block scores, B n ceil(n / r / 64) 64 4 bytes,
- *                then the per-query maxima, B n 4 bytes rounded up to 256
+ *   workspace    caller-owned, >= gdn_qsa_select_workspace_bytes(...) bytes,
+ *                16-byte aligned.  H = 4 keeps no scores: per query 16
+ *                candidate sub-lists of K_B / 16 + 96 (bits, block) pairs
+ *                plus a little bookkeeping (B n 16 (K_B / 16 + 96) 8 bytes in
+ *                all), and 256 scratch rows of ceil(n / r / 64) 64 floats.
+ *                Other H store the fp32 block scores,
+ *                B n ceil(n / r / 64) 64 4 bytes.
  *   D in {32, 64, 128}; r >= 1; K >= 1.
  */
 gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx,

@@ -230,7 +230,8 @@ gdn_status qsa_select_check(int B, int n, int H, int D, int r, int K, gdn_dtype 
     if (B <= 0 || n < 0 || H <= 0 || r < 1 || K < 1) return GDN_ERR_SHAPE;
     if (!qsa_dim_ok(D) || B > 65535) return GDN_ERR_UNSUPPORTED;
     const long long nb = n / r;
-    if (!fits(B, n, H, D) || !fits(B, n, (nb + 63) / 64 * 64, 4) || !fits(B, n, (K + r - 1) / r, 4))
+    if (!fits(B, n, H, D) || !fits(B, n, (nb + 63) / 64 * 64, 4) || !fits(B, n, (K + r - 1) / r, 4) ||
+        static_cast<long long>(B) * n > INT_MAX)
         return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
@@ -258,7 +259,7 @@ gdn_status gdn_qsa_prep(const void* q_proj, const void* k_proj, const float* q_w
 
 size_t gdn_qsa_select_workspace_bytes(int B, int n, int H, int D, int r, int K, gdn_dtype dtype) {
     if (qsa_select_check(B, n, H, D, r, K, dtype) != GDN_OK) return 0;
-    return gdn::qsa_select_workspace_bytes(B, n, r);
+    return gdn::qsa_select_workspace_bytes(B, n, H, r, (K + r - 1) / r);
 }
 
 gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx, int B, int n, int H, int D, int r, int K,
@@ -269,7 +270,7 @@ gdn_status gdn_qsa_select(const void* q, const void* kbar, int* block_idx, int B
     if (!q || !block_idx || (n / r > 0 && !kbar)) return GDN_ERR_NULL;
     for (const void* p : {q, kbar, static_cast<const void*>(block_idx)})
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-    const size_t need = gdn::qsa_select_workspace_bytes(B, n, r);
+    const size_t need = gdn::qsa_select_workspace_bytes(B, n, H, r, (K + r - 1) / r);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return GDN_ERR_ALIGN;
     gdn::QsaSelectArgs a{q, kbar, block_idx, B, n, H, D, r, (K + r - 1) / r, dtype == GDN_BF16, workspace,

@@ -139,7 +139,7 @@ struct QsaSelectArgs {
     int* idx;                   // [B, n, KB]
     int B, n, H, D, r, KB;
     bool bf16;
-    void* workspace;            // qsa_select_workspace_bytes: the block scores
+    void* workspace;            // qsa_select_workspace_bytes bytes
     hipStream_t stream;
 };
 
@@ -154,6 +154,8 @@ hipError_t launch_prefill_bwd(const PrefillBwdArgs& a);
 size_t prefill_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
 hipError_t launch_qsa_prep(const QsaPrepArgs& a);
 hipError_t launch_qsa_select(const QsaSelectArgs& a);
-size_t qsa_select_workspace_bytes(int B, int n, int r);
+hipError_t launch_qsa_select4(const QsaSelectArgs& a);
+size_t qsa_select_workspace_bytes(int B, int n, int H, int r, int KB);
+size_t qsa_select4_workspace_bytes(int B, int n, int r, int KB);
 
 }  // namespace gdn

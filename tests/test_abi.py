@@ -338,9 +338,18 @@ def test_qsa_select_rejects(kwargs, status):
 
 def test_qsa_select_workspace_bytes():
     lib = gdn.load_library()
-    # n = 100 tokens, r = 4: 25 blocks, rows padded to 64 scores,
-    # plus the per-row maxima, padded to 256 bytes
-    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 128, 4, 2048, 1) == 2 * 100 * 64 * 4 + 1024
+    up = lambda x: (x + 255) // 256 * 256
+    # four query heads, n = 100 tokens, r = 4 (25 blocks), K = 2048 (K_B = 512),
+    # 200 query rows: key maxima + queue count, per-row band (8 B), 16 sub-list
+    # lengths (4 B each), the queue (4 B), 16 sub-lists of
+    # 512 / 16 + 1024 / 16 + 32 (bits, block) pairs (8 B) per row, and 512
+    # scratch rows of 64 floats
+    rows = 2 * 100
+    four = (up(2 * 4) + 256 + up(rows * 8) + up(rows * 16 * 4) + up(rows * 4) + up(rows * 16 * 128 * 8)
+            + up(256 * 64 * 4))
+    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 128, 4, 2048, 1) == four
+    # other head counts store the fp32 scores, rows padded to 64 blocks
+    assert lib.gdn_qsa_select_workspace_bytes(2, 100, 2, 128, 4, 2048, 1) == 2 * 100 * 64 * 4
     assert lib.gdn_qsa_select_workspace_bytes(2, 100, 4, 100, 4, 2048, 1) == 0
 
 
