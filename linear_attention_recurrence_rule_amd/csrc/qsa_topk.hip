@@ -42,7 +42,7 @@ namespace qsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kTQ = 32, kTB = 64;    // queries and blocks per tile
+constexpr int kTB = 64;              // key blocks per tile
 constexpr int kHB = 256;             // histogram bins per query
 
 // sum over the four heads of ReLU(score); ReLU as a signed-integer max with 0
@@ -96,24 +96,25 @@ __global__ __launch_bounds__(256) void qsa_kmax_kernel(const void* __restrict__ 
 // are the four heads of one query and the ReLU-sum over heads stays in the
 // lane (lane l holds query 8 w + 4 mt + l / 16, block column l % 16).
 // ---------------------------------------------------------------------------
-template <int D, bool kBf16>
+template <int D, bool kBf16, int MT>
 struct QFrag;
-template <int D>
-struct QFrag<D, true> {
-    bf16x8 a[2][D / 32];   // lane (r + 16 g): row r of the 16-row group, elements 32 kk + 8 g .. + 8
+template <int D, int MT>
+struct QFrag<D, true, MT> {
+    bf16x8 a[MT][D / 32];  // lane (r + 16 g): row r of 16-row group mt, elements 32 kk + 8 g .. + 8
 };
-template <int D>
-struct QFrag<D, false> {
-    float a[2][D / 4];     // lane (r + 16 g): row r, elements g D / 4 + k (split-K fp32 layout)
+template <int D, int MT>
+struct QFrag<D, false, MT> {
+    float a[MT][D / 4];    // lane (r + 16 g): row r, elements g D / 4 + k (split-K fp32 layout)
 };
 
-template <int D, bool kBf16>
-__device__ __forceinline__ void load_qfrag(QFrag<D, kBf16>& f, const void* q, int b, int n, int i0, int wave,
-                                           int l, float (&sq)[2]) {
+// A wave holds MT groups of 16 tile rows, 4 MT queries.
+template <int D, bool kBf16, int MT>
+__device__ __forceinline__ void load_qfrag(QFrag<D, kBf16, MT>& f, const void* q, int b, int n, int i0, int wave,
+                                           int l, float (&sq)[MT]) {
     const int r = l & 15, g = l >> 4;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int R = 32 * wave + 16 * mt + r;          // tile row: query R / 4, head R % 4
+    for (int mt = 0; mt < MT; ++mt) {
+        const int R = 16 * MT * wave + 16 * mt + r;     // tile row: query R / 4, head R % 4
         const bool ok = i0 + R / 4 < n;
         const long base = ((static_cast<long>(b) * n + i0) * 4 + R) * D;
         float s = 0.f;
@@ -141,17 +142,29 @@ __device__ __forceinline__ void load_qfrag(QFrag<D, kBf16>& f, const void* q, in
     }
 }
 
-// Scores of one 32-query x 64-block tile for this wave's 8 queries:
-// acc[mt][nt][h] = <q_i^h, kbar_blk>, i = i0 + 8 w + 4 mt + l / 16,
+// Scores of one 64-block key tile for this wave's 4 MT queries:
+// acc[mt][nt][h] = <q_i^h, kbar_blk>, i = i0 + 4 MT w + 4 mt + l / 16,
 // blk = b0 + 16 nt + l % 16.  sK: 64 key rows of LD elements.
-template <int D, bool kBf16, int LD>
-__device__ __forceinline__ void tile_scores(const QFrag<D, kBf16>& f, const unsigned char* sK, int l,
-                                            float4v (&acc)[2][4]) {
+template <int D, bool kBf16, int LD, int MT>
+__device__ __forceinline__ void tile_scores(const QFrag<D, kBf16, MT>& f, const unsigned char* sK, int l,
+                                            float4v (&acc)[MT][4]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kBf16) {
+    if constexpr (kBf16 && MT > 2) {
+        // four or more groups reuse each B fragment enough to hide its read
+        const __bf16* Bt = reinterpret_cast<const __bf16*>(sK) + (l & 15) * LD + 8 * (l >> 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bt + 16 * nt * LD + 32 * kk);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mt][kk], bv, acc[mt][nt], 0, 0, 0);
+            }
+    } else if constexpr (kBf16) {
         // every B fragment of the tile is read before the first MFMA, so the
         // LDS latency is paid once per tile
         const __bf16* Bt = reinterpret_cast<const __bf16*>(sK) + (l & 15) * LD + 8 * (l >> 4);
@@ -162,13 +175,12 @@ __device__ __forceinline__ void tile_scores(const QFrag<D, kBf16>& f, const unsi
             for (int nt = 0; nt < 4; ++nt) bv[kk][nt] = *reinterpret_cast<const bf16x8*>(Bt + 16 * nt * LD + 32 * kk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
+        for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                acc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[0][kk], bv[kk][nt], acc[0][nt], 0, 0, 0);
-                acc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[1][kk], bv[kk][nt], acc[1][nt], 0, 0, 0);
-            }
-        }
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mt][kk], bv[kk][nt], acc[mt][nt], 0, 0, 0);
     } else {
         const float* Bt = reinterpret_cast<const float*>(sK) + (l & 15) * LD + (l >> 4) * (D / 4);
 #pragma unroll 8
@@ -176,8 +188,9 @@ __device__ __forceinline__ void tile_scores(const QFrag<D, kBf16>& f, const unsi
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const float bv = Bt[16 * nt * LD + k];
-                acc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[0][k], bv, acc[0][nt], 0, 0, 0);
-                acc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[1][k], bv, acc[1][nt], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[mt][k], bv, acc[mt][nt], 0, 0, 0);
             }
         }
     }
@@ -225,8 +238,10 @@ constexpr int kMapWords = 512;       // merge: output bitmap chunk (32768 blocks
 __device__ __forceinline__ int sampled_tile(int j) { return 8 * j + ((5 * j) & 7); }
 
 // ---------------------------------------------------------------------------
-// Both scoring passes, grid (ceil(n / 32), B), 256 threads (4 waves x 8
-// queries); the longest query tiles go first.  The key tiles stream through
+// Both scoring passes, 256 threads: the histogram pass with 4 waves x 8
+// queries, grid (ceil(n / 32), B); the emit pass with 4 waves x 16 queries,
+// grid (ceil(n / 64), B), so that each B fragment read from LDS feeds four
+// MFMAs.  The longest query tiles go first.  The key tiles stream through
 // two LDS buffers with register prefetch.
 //   kEmit = false: histogram pass.  For each query with m > K_B it keeps the
 //     band [tlo, thi) of score bit patterns that should hold its K_B-th
@@ -248,27 +263,29 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     constexpr int LD = D + (kBf16 ? 8 : 4);
     constexpr int kVec = 16 / ES;                    // elements per 16-byte load
     constexpr int kKPer = kTB * D / kVec / 256;      // 16-byte key loads per thread and tile
-    const int ntq = (n + kTQ - 1) / kTQ;
+    constexpr int MT = kEmit ? 4 : 2;                // 16-row groups (4 queries each) per wave
+    constexpr int TQ = 16 * MT;                      // queries per workgroup
+    const int ntq = (n + TQ - 1) / TQ;
     const int qt = ntq - 1 - static_cast<int>(blockIdx.x), b = blockIdx.y;
-    const int i0 = qt * kTQ;
-    const int ilast = min(i0 + kTQ, n) - 1;
+    const int i0 = qt * TQ;
+    const int ilast = min(i0 + TQ, n) - 1;
     const int mvis = (ilast + 1) / r;                // blocks visible to the tile's last query
     if (mvis <= KB) return;                          // every query of the tile keeps all its blocks
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, g = l >> 4;
 
     __shared__ __align__(16) unsigned char sK[2][kTB * LD * ES];
-    __shared__ unsigned sH[kEmit ? 1 : kTQ][kHB];
+    __shared__ unsigned sH[kEmit ? 1 : TQ][kHB];
 
-    QFrag<D, kBf16> f;
-    float sq[2];
-    load_qfrag<D, kBf16>(f, q, b, n, i0, wave, l, sq);
+    QFrag<D, kBf16, MT> f;
+    float sq[MT];
+    load_qfrag<D, kBf16, MT>(f, q, b, n, i0, wave, l, sq);
 
-    // this lane's two queries (mt = 0, 1)
-    int qi[2], vis[2];
-    bool act[2];
+    // this lane's MT queries
+    int qi[MT], vis[MT];
+    bool act[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        qi[mt] = i0 + 8 * wave + 4 * mt + g;
+    for (int mt = 0; mt < MT; ++mt) {
+        qi[mt] = i0 + 4 * MT * wave + 4 * mt + g;
         vis[mt] = qi[mt] < n ? (qi[mt] + 1) / r : 0;
         act[mt] = vis[mt] > KB;
     }
@@ -277,13 +294,19 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     const int nsteps = sampled ? (nbt + 7) / 8 : nbt;
     auto tile_of = [&](int j) { return sampled ? sampled_tile(j) : j; };
 
-    int lo[2] = {0, 0};
-    unsigned tlo[2] = {0u, 0u}, thi[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};
+    int lo[MT];
+    unsigned tlo[MT], thi[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        lo[mt] = 0;
+        tlo[mt] = 0u;
+        thi[mt] = 0xFFFFFFFFu;
+    }
     if constexpr (!kEmit) {
         // bound: sum_h |q^h| max_j |kbar_j|; lanes r = 4 u + h of group mt hold (query u, head h)
         const float km = kmax[b];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             float s = sq[mt];
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
@@ -291,10 +314,10 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
             const float ub = __shfl(qn, 4 * g) * km; // this lane's query in the output layout
             lo[mt] = static_cast<int>(((__float_as_uint(ub) >> 23) & 255u) + 1u) * 16 - (kHB - 2);
         }
-        for (int j = l; j < 8 * kHB; j += 64) sH[8 * wave + j / kHB][j % kHB] = 0u;
+        for (int j = l; j < 4 * MT * kHB; j += 64) sH[4 * MT * wave + j / kHB][j % kHB] = 0u;
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             if (act[mt]) {
                 const uint2 t = info[static_cast<long>(b) * n + qi[mt]];
                 tlo[mt] = t.x;
@@ -302,8 +325,10 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
             }
         }
     }
-    unsigned zc[2] = {0u, 0u};                      // histogram pass: zeros seen by this lane
-    int nl[2] = {0, 0};                              // emit pass: this lane's sub-list lengths
+    unsigned zc[MT];                                 // histogram pass: zeros seen by this lane
+    int nl[MT];                                      // emit pass: this lane's sub-list lengths
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) zc[mt] = nl[mt] = 0;
 
     const unsigned char* kb = static_cast<const unsigned char*>(kbar);
     // key tiles: two register sets, loaded two steps ahead of their use
@@ -328,10 +353,10 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     auto step = [&](int j, int buf) {
         const int bt = tile_of(j);                   // may pass nbt in the last sampled group
         const int b0 = bt * kTB;
-        float4v acc[2][4];
-        tile_scores<D, kBf16, LD>(f, sK[buf], l, acc);
+        float4v acc[MT][4];
+        tile_scores<D, kBf16, LD, MT>(f, sK[buf], l, acc);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int blk = b0 + 16 * nt + (l & 15);
@@ -340,7 +365,7 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
                 if constexpr (!kEmit) {
                     if (valid) {
                         if (u == 0u) ++zc[mt];
-                        else atomicAdd(&sH[8 * wave + 4 * mt + g][ubin(u, lo[mt])], 1u);
+                        else atomicAdd(&sH[4 * MT * wave + 4 * mt + g][ubin(u, lo[mt])], 1u);
                     }
                 } else {
                     // lane sub-list (query, l % 16): blocks of that residue mod 16
@@ -372,17 +397,17 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     if constexpr (!kEmit) {
         // zeros: one plain store per query (bin 0 gets no atomics)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             const unsigned z = row16_sum_u(zc[mt]);
-            if ((l & 15) == 0) sH[8 * wave + 4 * mt + g][0] = z;
+            if ((l & 15) == 0) sH[4 * MT * wave + 4 * mt + g][0] = z;
         }
         wave_sync();
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int i = i0 + 8 * wave + rr;
+        for (int rr = 0; rr < 4 * MT; ++rr) {
+            const int i = i0 + 4 * MT * wave + rr;
             const int m = i < n ? (i + 1) / r : 0;
             if (m > KB) {                            // wave-uniform
-                const unsigned* h = sH[8 * wave + rr];
+                const unsigned* h = sH[4 * MT * wave + rr];
                 const int lor = __shfl(lo[rr >> 2], 16 * (rr & 3));
                 unsigned c4 = 0;
 #pragma unroll
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     } else {
         // per query: the 16 sub-list lengths (uncapped)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
             if (act[mt]) cnt[(static_cast<long>(b) * n + qi[mt]) * 16 + (l & 15)] = nl[mt];
     }
 }
@@ -619,11 +644,11 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
         const int b = static_cast<int>(row / n), i = static_cast<int>(row % n);
         const int m = (i + 1) / r;
         float* sr = m <= kExactLds ? srow : scratch + static_cast<long>(blockIdx.x) * ld;
-        QFrag<D, kBf16> f;
-        float sqd[2];
-        load_qfrag<D, kBf16>(f, q, b, n, i, 0, lane, sqd);   // A rows 0..3: (i, head 0..3)
+        QFrag<D, kBf16, 1> f;
+        float sqd[1];
+        load_qfrag<D, kBf16, 1>(f, q, b, n, i, 0, lane, sqd);   // A rows 0..3: (i, head 0..3)
         float mx = 0.f;
-        constexpr int kG = kBf16 ? 8 : 2;            // 16-block groups per batch
+        constexpr int kG = kBf16 ? 4 : 2;            // 16-block groups per batch
         for (int g0 = 16 * kG * w; g0 < m; g0 += 16 * kG * kExactWaves) {
             float4v acc[kG];
 #pragma unroll
@@ -726,14 +751,14 @@ static hipError_t launch_select4_t(const QsaSelectArgs& a) {
     uint2* list = reinterpret_cast<uint2*>(ws + t.list);
     float* scratch = reinterpret_cast<float*>(ws + t.scratch);
     const long ld = nbw > 0 ? static_cast<long>(nbw) * 64 : 64;
-    const dim3 gt((a.n + kTQ - 1) / kTQ, a.B), gq((a.n + 3) / 4, a.B);
+    const dim3 gh((a.n + 31) / 32, a.B), ge((a.n + 63) / 64, a.B), gq((a.n + 3) / 4, a.B);
     hipLaunchKernelGGL(qsa_zero_kernel, dim3(1), dim3(256), 0, a.stream, kmax, a.B, qcount);
     if (nb > a.KB) {                                 // otherwise every query keeps all its blocks
         hipLaunchKernelGGL((qsa_kmax_kernel<D, kBf16>), dim3((nb + 255) / 256, a.B), dim3(256), 0, a.stream, a.kbar,
                            kmax, nb);
-        hipLaunchKernelGGL((qsa_pass4_kernel<D, kBf16, false>), gt, dim3(256), 0, a.stream, a.q, a.kbar, kmax, info,
+        hipLaunchKernelGGL((qsa_pass4_kernel<D, kBf16, false>), gh, dim3(256), 0, a.stream, a.q, a.kbar, kmax, info,
                            cnt, list, a.n, a.r, nb, a.KB, cap);
-        hipLaunchKernelGGL((qsa_pass4_kernel<D, kBf16, true>), gt, dim3(256), 0, a.stream, a.q, a.kbar, kmax, info,
+        hipLaunchKernelGGL((qsa_pass4_kernel<D, kBf16, true>), ge, dim3(256), 0, a.stream, a.q, a.kbar, kmax, info,
                            cnt, list, a.n, a.r, nb, a.KB, cap);
     }
     hipLaunchKernelGGL(qsa_merge_kernel, gq, dim3(256), 0, a.stream, info, cnt, list, a.idx, queue, qcount, a.n,
