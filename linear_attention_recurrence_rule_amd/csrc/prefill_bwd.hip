@@ -302,39 +302,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Pass 2: chunk-start states and E, walking the chunks forward.
-// grid (DV / 16, B*H), 256 threads; the 16-column slice of S lives in the
-// accumulators of the waves that own its row blocks.  The next chunk's
-// inputs are loaded into registers while the current chunk is computed.
+// grid (DV / 16 slices x 8 x ceil(B*H / 8)), 512 threads (8 waves); state
+// row block m of the slice lives in wave m's accumulators.  Per chunk:
+//   1. K S for row block w % 4, its d_k columns split between waves w and
+//      w + 4 as two partial sums, added in LDS into R = diag(beta) (V -
+//      diag(gamma) K S).
+//   2. E = T R (waves 0..3, one row block each), written out, (lam E)^T kept.
+//   3. S' = gamma_n S + K^T (lam E), one state block per wave.
+// The next chunk's inputs are loaded into registers while the current chunk
+// is computed.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool kBf16>
-__global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict__ k, const void* __restrict__ v,
+__global__ __launch_bounds__(512) void bwd_states_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                          const float* __restrict__ beta,
                                                          const float* __restrict__ S0,
                                                          const float* __restrict__ ws_g,
                                                          const float* __restrict__ ws_T, float* __restrict__ ws_S,
                                                          float* __restrict__ ws_E, int T, int H, int nch, int BH) {
     constexpr int SV = 16, LDK = DK + 4, LDT = C + 4, LDS_ = DK + 4, LDR = C + 4;
-    constexpr int NST = DK / 16;                       // state row blocks
-    constexpr int SPW = (NST + 3) / 4;                 // state row blocks per wave
+    constexpr int NST = DK / 16;                       // state row blocks, one per wave
+    constexpr int NT = 512;
+    constexpr int KH = DK >= 32 ? DK / 2 : DK;         // d_k columns of K S in the first partial sum
     int slice, bh;
     if (!slice_of_block<DV / 16>(BH, slice, bh)) return;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int rb = wave & 3, half = wave >> 2;
     const int col0 = slice * SV;
+    const bool owns = wave < NST;
 
     __shared__ __align__(16) float sK[C * LDK];
     __shared__ __align__(16) float sT[C * LDT];
     __shared__ __align__(16) float sSt[SV * LDS_];     // S^T (the slice)
+    __shared__ __align__(16) float sKSp[2][SV * LDR];  // the two partial sums of (K S)^T
     __shared__ __align__(16) float sRt[SV * LDR];      // R^T
     __shared__ __align__(16) float sEt[SV * LDR];      // (lam E)^T
     __shared__ float sV[C][SV + 1];
     __shared__ float sg[C], sb[C];
 
-    RowTile<DK, 256, kBf16> pk;
-    MatTile<256> pt;
+    RowTile<DK, NT, kBf16> pk;
+    MatTile<NT> pt;
     Raw4<kBf16> pv;
     float pg = 0.f, pb = 0.f;
-    const int vt = tid >> 2, vc = tid & 3;
+    const int vt = (tid >> 2) & 63, vc = tid & 3;
     auto fetch = [&](int cc) {
         const long bhn = static_cast<long>(bh) * nch + cc;
         pk.load(k, b, cc, T, H, h);
@@ -348,29 +358,26 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
     auto publish = [&](int cc) {
         pk.store(sK, LDK, cc, T);
         pt.store(sT, LDT);
-        const float4v x = cc * C + vt < T ? raw_cvt<kBf16>(pv) : float4v{0.f, 0.f, 0.f, 0.f};
+        if (tid < 256) {
+            const float4v x = cc * C + vt < T ? raw_cvt<kBf16>(pv) : float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sV[vt][4 * vc + e] = x[e];
+            for (int e = 0; e < 4; ++e) sV[vt][4 * vc + e] = x[e];
+        }
         if (tid < C) {
             sg[tid] = pg;
             sb[tid] = cc * C + tid < T ? pb : 0.f;
         }
     };
 
-    float4v st[SPW];
-#pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-        const int m = wave + 4 * u;
-        st[u] = float4v{0.f, 0.f, 0.f, 0.f};
-        if (m < NST && S0) {
+    float4v st = {0.f, 0.f, 0.f, 0.f};
+    if (owns) {
+        if (S0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                st[u][j] = S0[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
+                st[j] = S0[(static_cast<long>(bh) * DK + 16 * wave + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
         }
-        if (m < NST) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = st[u][j];
-        }
+        for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * wave + 4 * (l >> 4) + j] = st[j];
     }
     fetch(0);
     publish(0);
@@ -380,28 +387,28 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
         const long bhn = static_cast<long>(bh) * nch + c;
         fetch(c + 1 < nch ? c + 1 : c);
         // chunk-start state out
+        if (owns) {
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) {
-            const int m = wave + 4 * u;
-            if (m < NST) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ws_S[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = st[u][j];
-            }
+            for (int j = 0; j < 4; ++j)
+                ws_S[(bhn * DK + 16 * wave + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = st[j];
         }
-        // R = diag(beta) (V - diag(gamma) K S), one row block per wave
-        {
+        // 1. K S for row block rb, d_k columns [0, KH) or [KH, DK)
+        if (half == 0 || KH < DK) {
             float4v ks = {0.f, 0.f, 0.f, 0.f};
-            ks = mma_n<false, false, DK>(&sK[16 * wave * LDK], LDK, sSt, LDS_, 0, ks);
+            if (half == 0) ks = mma_n<false, false, KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, 0, ks);
+            else if constexpr (KH < DK) ks = mma_n<false, false, DK - KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, KH, ks);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * wave + 4 * (l >> 4) + j;
-                sRt[(l & 15) * LDR + r] = sb[r] * (sV[r][l & 15] - __expf(sg[r]) * ks[j]);
-            }
+            for (int j = 0; j < 4; ++j) sKSp[half][(l & 15) * LDR + 16 * rb + 4 * (l >> 4) + j] = ks[j];
         }
         __syncthreads();
-        // E = T R (T lower triangular), written out; (lam E)^T kept for the update
-        {
+        for (int i = tid; i < SV * C; i += NT) {
+            const int cc = i / C, r = i - cc * C;
+            const float ks = KH < DK ? sKSp[0][cc * LDR + r] + sKSp[1][cc * LDR + r] : sKSp[0][cc * LDR + r];
+            sRt[cc * LDR + r] = sb[r] * (sV[r][cc] - __expf(sg[r]) * ks);
+        }
+        __syncthreads();
+        // 2. E = T R (T lower triangular), written out; (lam E)^T kept for the update
+        if (wave < 4) {
             float4v e = {0.f, 0.f, 0.f, 0.f};
             e = mma_n<false, false, C>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, e);   // T is zero above the diagonal
             const float gn = sg[C - 1];
@@ -413,20 +420,12 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
             }
         }
         __syncthreads();
-        // S' = gamma_n S + K^T (lam E)
-        {
+        // 3. S' = gamma_n S + K^T (lam E)
+        if (owns) {
             const float gam_n = __expf(sg[C - 1]);
+            st = mma_n<true, false, C>(&sK[16 * wave], LDK, sEt, LDR, 0, gam_n * st);
 #pragma unroll
-            for (int u = 0; u < SPW; ++u) {
-                const int m = wave + 4 * u;
-                if (m < NST) {
-                    float4v acc = gam_n * st[u];
-                    acc = mma_n<true, false, C>(&sK[16 * m], LDK, sEt, LDR, 0, acc);
-                    st[u] = acc;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = acc[j];
-                }
-            }
+            for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * wave + 4 * (l >> 4) + j] = st[j];
         }
         __syncthreads();
         publish(c + 1 < nch ? c + 1 : c);
@@ -435,22 +434,35 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(const void* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3: state gradients, walking the chunks backward.  grid (DV / 16, B*H).
+// Pass 3: state gradients, walking the chunks backward.  grid as pass 2,
+// 512 threads (8 waves).  State row block m of the slice lives in wave m's
+// accumulators.  Per chunk:
+//   1. dE = scale P^T dY + diag(lam) K dS': row block w % 4; wave w / 4 = 0
+//      takes P^T dY and the first ka columns of K dS', wave w / 4 = 1 the
+//      rest, as two partial sums added in LDS.  scale gamma dY is formed.
+//   2. dR = T^T dE (waves 0..3, one row block each; dV = beta dR) while every
+//      wave m < DK / 16 starts its block of dS with gamma_n dS' + Q^T (scale
+//      gamma dY).
+//   3. dS += K^T (-beta gamma dR).
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool kBf16>
-__global__ __launch_bounds__(256) void bwd_dstates_kernel(
+__global__ __launch_bounds__(512) void bwd_dstates_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ beta,
     const float* __restrict__ dy, const float* __restrict__ dST, const float* __restrict__ ws_g,
     const float* __restrict__ ws_T, const float* __restrict__ ws_P, float* __restrict__ ws_dS,
     float* __restrict__ ws_dR, float* __restrict__ dv_out, float* __restrict__ dS0, int T, int H, int nch,
     int BH, float scale) {
     constexpr int SV = 16, LDK = DK + 4, LDX = C + 4, LDS_ = DK + 4;
-    constexpr int NST = DK / 16, SPW = (NST + 3) / 4;
+    constexpr int NST = DK / 16;                       // state row blocks, one per wave
+    constexpr int NT = 512;
+    constexpr int KA = DK == 128 ? 32 : 0;             // columns of K dS' taken with P^T dY
     int slice, bh;
     if (!slice_of_block<DV / 16>(BH, slice, bh)) return;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int rb = wave & 3, half = wave >> 2;
     const int col0 = slice * SV;
+    const bool owns = wave < NST;
 
     __shared__ __align__(16) float sQ[C * LDK];
     __shared__ __align__(16) float sK[C * LDK];
@@ -459,15 +471,16 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
     __shared__ __align__(16) float sdYt[SV * LDX];     // dY^T
     __shared__ __align__(16) float sB1t[SV * LDX];     // (scale gamma dY)^T
     __shared__ __align__(16) float sB2t[SV * LDX];     // (-beta gamma dR)^T
+    __shared__ __align__(16) float sdEp[2][SV * LDX];  // the two partial sums of dE^T
     __shared__ __align__(16) float sdEt[SV * LDX];     // dE^T
     __shared__ __align__(16) float sdSt[SV * LDS_];    // dS'^T
     __shared__ float sg[C], sb[C];
 
-    RowTile<DK, 256, kBf16> pq, pk;
-    MatTile<256> pt, pp;
-    float4v pdy;
+    RowTile<DK, NT, kBf16> pq, pk;
+    MatTile<NT> pt, pp;
+    float4v pdy = {0.f, 0.f, 0.f, 0.f};
     float pg = 0.f, pb = 0.f;
-    const int yt = tid >> 2, yc = tid & 3;
+    const int yt = (tid >> 2) & 63, yc = tid & 3;
     auto fetch = [&](int cc) {
         const long bhn = static_cast<long>(bh) * nch + cc;
         pq.load(q, b, cc, T, H, h);
@@ -485,29 +498,26 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
         pk.store(sK, LDK, cc, T);
         pt.store(sT, LDX);
         pp.store(sP, LDX);
-        const float4v x = cc * C + yt < T ? pdy : float4v{0.f, 0.f, 0.f, 0.f};
+        if (tid < 256) {
+            const float4v x = cc * C + yt < T ? pdy : float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sdYt[(4 * yc + e) * LDX + yt] = x[e];
+            for (int e = 0; e < 4; ++e) sdYt[(4 * yc + e) * LDX + yt] = x[e];
+        }
         if (tid < C) {
             sg[tid] = pg;
             sb[tid] = cc * C + tid < T ? pb : 0.f;
         }
     };
 
-    float4v ds[SPW];
-#pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-        const int m = wave + 4 * u;
-        ds[u] = float4v{0.f, 0.f, 0.f, 0.f};
-        if (m < NST && dST) {
+    float4v ds = {0.f, 0.f, 0.f, 0.f};
+    if (owns) {
+        if (dST) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                ds[u][j] = dST[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
+                ds[j] = dST[(static_cast<long>(bh) * DK + 16 * wave + 4 * (l >> 4) + j) * DV + col0 + (l & 15)];
         }
-        if (m < NST) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
-        }
+        for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * wave + 4 * (l >> 4) + j] = ds[j];
     }
     fetch(nch - 1);
     publish(nch - 1);
@@ -516,34 +526,40 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
     for (int c = nch - 1; c >= 0; --c) {
         const long bhn = static_cast<long>(bh) * nch + c;
         fetch(c > 0 ? c - 1 : 0);
+        if (owns) {
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) {
-            const int m = wave + 4 * u;
-            if (m < NST) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ws_dS[(bhn * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[u][j];
-            }
+            for (int j = 0; j < 4; ++j)
+                ws_dS[(bhn * DK + 16 * wave + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[j];
         }
-        // dE = scale P^T dY + diag(lam) K dS'  (P^T upper triangular)
+        // 1. the two partial sums of dE for row block rb
         {
-            float4v a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-            a1 = mma_n<true, false, C>(&sP[16 * wave], LDX, sdYt, LDX, 0, a1);   // P^T is zero below the diagonal
-            a2 = mma_n<false, false, DK>(&sK[16 * wave * LDK], LDK, sdSt, LDS_, 0, a2);
             const float gn = sg[C - 1];
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+            float4v kd = {0.f, 0.f, 0.f, 0.f};
+            if (half == 0) {
+                acc = mma_n<true, false, C>(&sP[16 * rb], LDX, sdYt, LDX, 0, acc);   // P^T is zero below the diagonal
+                if constexpr (KA > 0) kd = mma_n<false, false, KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, 0, kd);
+            } else {
+                kd = mma_n<false, false, DK - KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, KA, kd);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * wave + 4 * (l >> 4) + j;
-                sdEt[(l & 15) * LDX + r] = scale * a1[j] + __expf(gn - sg[r]) * a2[j];
+                const int r = 16 * rb + 4 * (l >> 4) + j;
+                sdEp[half][(l & 15) * LDX + r] = scale * acc[j] + __expf(gn - sg[r]) * kd[j];
             }
         }
-        for (int i = tid; i < SV * C; i += 256) {
+        for (int i = tid; i < SV * C; i += NT) {
             const int cc = i / C, t = i - cc * C;
             sB1t[cc * LDX + t] = scale * __expf(sg[t]) * sdYt[cc * LDX + t];
         }
         __syncthreads();
-        // dR = T^T dE; dV = diag(beta) dR
-        {
+        for (int i = tid; i < SV * C; i += NT) {
+            const int cc = i / C, t = i - cc * C;
+            sdEt[cc * LDX + t] = sdEp[0][cc * LDX + t] + sdEp[1][cc * LDX + t];
+        }
+        __syncthreads();
+        // 2. dR = T^T dE, dV = diag(beta) dR (waves 0..3); dS starts with gamma_n dS' + Q^T (scale gamma dY)
+        if (wave < 4) {
             float4v r = {0.f, 0.f, 0.f, 0.f};
             r = mma_n<true, false, C>(&sT[16 * wave], LDX, sdEt, LDX, 0, r);   // T^T is zero below the diagonal
 #pragma unroll
@@ -554,43 +570,23 @@ __global__ __launch_bounds__(256) void bwd_dstates_kernel(
                 sB2t[(l & 15) * LDX + t] = -sb[t] * __expf(sg[t]) * r[j];
             }
         }
+        const float gam_n = __expf(sg[C - 1]);
+        if (owns) ds = mma_n<true, false, C>(&sQ[16 * wave], LDK, sB1t, LDX, 0, gam_n * ds);
         __syncthreads();
-        // dS = gamma_n dS' + Q^T (scale gamma dY) + K^T (-beta gamma dR)
-        {
-            const float gam_n = __expf(sg[C - 1]);
-#pragma unroll
-            for (int u = 0; u < SPW; ++u) {
-                const int m = wave + 4 * u;
-                if (m < NST) {
-                    float4v acc = gam_n * ds[u];
-                    acc = mma_n<true, false, C>(&sQ[16 * m], LDK, sB1t, LDX, 0, acc);
-                    acc = mma_n<true, false, C>(&sK[16 * m], LDK, sB2t, LDX, 0, acc);
-                    ds[u] = acc;
-                }
-            }
-        }
+        // 3. dS += K^T (-beta gamma dR)
+        if (owns) ds = mma_n<true, false, C>(&sK[16 * wave], LDK, sB2t, LDX, 0, ds);
         __syncthreads();                       // every read of this chunk's tiles is done
+        if (owns) {
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) {
-            const int m = wave + 4 * u;
-            if (m < NST) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * m + 4 * (l >> 4) + j] = ds[u][j];
-            }
+            for (int j = 0; j < 4; ++j) sdSt[(l & 15) * LDS_ + 16 * wave + 4 * (l >> 4) + j] = ds[j];
         }
         publish(c > 0 ? c - 1 : 0);
         __syncthreads();
     }
-    if (dS0) {
+    if (dS0 && owns) {
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) {
-            const int m = wave + 4 * u;
-            if (m < NST) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dS0[(static_cast<long>(bh) * DK + 16 * m + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[u][j];
-            }
-        }
+        for (int j = 0; j < 4; ++j)
+            dS0[(static_cast<long>(bh) * DK + 16 * wave + 4 * (l >> 4) + j) * DV + col0 + (l & 15)] = ds[j];
     }
 }
 
@@ -904,9 +900,9 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
     const dim3 gc(nch, BH), gs((D / 16) * 8 * ((BH + 7) / 8), 1);
     hipLaunchKernelGGL((bwd::bwd_prep_kernel<D, kBf16>), gc, dim3(256), 0, a.stream, a.q, a.k, a.alpha, a.beta,
                        g, Tm, P, M, a.T, a.H, nch);
-    hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.k, a.v, a.beta,
+    hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.k, a.v, a.beta,
                        a.initial_state, g, Tm, S, E, a.T, a.H, nch, BH);
-    hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(256), 0, a.stream, a.q, a.k, a.beta,
+    hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.q, a.k, a.beta,
                        a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, BH,
                        a.scale);
     hipLaunchKernelGGL((bwd::bwd_grads_kernel<D, kBf16>), gc, dim3(512), 0, a.stream, a.q, a.k, a.v, a.alpha,
