@@ -464,8 +464,9 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
     __shared__ int sBlk[4][kCapB];
     __shared__ unsigned long long sMap[4][kMapWords];
     const unsigned thi = info[row].y;
-    // lane l reads sub-list l % 16, entries l / 16 + 4 t: kBatch entries per lane in flight
-    constexpr int kBatch = 32;
+    // lane l reads sub-list l % 16, entry pairs l / 16 + 4 t (16 bytes each):
+    // 2 kBatch entries per lane in flight
+    constexpr int kBatch = 16;
     const int sl = lane & 15;
     const int len = cnt[row * 16 + sl];
     const bool over = __ballot(len > cap) != 0ull;
@@ -475,16 +476,22 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
     const uint2* lst = list + (row * 16 + sl) * cap;
     const bool one_chunk = m <= 64 * kMapWords;
     // visit(u, blk) for every listed entry, kBatch loads per lane at a time
+    auto load_pairs = [&](int k0, uint2 (&e)[2 * kBatch]) {
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+            const int k = k0 + 2 * ((lane >> 4) + 4 * t);
+            uint4 v = make_uint4(0u, 0xFFFFFFFFu, 0u, 0xFFFFFFFFu);
+            if (k < len) v = *reinterpret_cast<const uint4*>(lst + k);
+            e[2 * t] = make_uint2(v.x, v.y);
+            e[2 * t + 1] = k + 1 < len ? make_uint2(v.z, v.w) : make_uint2(0u, 0xFFFFFFFFu);
+        }
+    };
     auto for_entries = [&](auto visit) {
-        for (int k0 = 0; k0 < maxlen; k0 += 4 * kBatch) {
-            uint2 e[kBatch];
+        for (int k0 = 0; k0 < maxlen; k0 += 8 * kBatch) {
+            uint2 e[2 * kBatch];
+            load_pairs(k0, e);
 #pragma unroll
-            for (int t = 0; t < kBatch; ++t) {
-                const int k = k0 + (lane >> 4) + 4 * t;
-                e[t] = k < len ? lst[k] : make_uint2(0u, 0xFFFFFFFFu);
-            }
-#pragma unroll
-            for (int t = 0; t < kBatch; ++t) visit(e[t].x, static_cast<int>(e[t].y));
+            for (int t = 0; t < 2 * kBatch; ++t) visit(e[t].x, static_cast<int>(e[t].y));
         }
     };
     auto mark = [&](int d, int c0) { atomicOr(&sMap[w][(d - c0) >> 6], 1ull << ((d - c0) & 63)); };
@@ -495,16 +502,12 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
     wave_sync();
     unsigned nc = 0, nd = 0;
     if (!over) {
-        for (int k0 = 0; k0 < maxlen; k0 += 4 * kBatch) {
-            uint2 e[kBatch];
-#pragma unroll
-            for (int t = 0; t < kBatch; ++t) {
-                const int k = k0 + (lane >> 4) + 4 * t;
-                e[t] = k < len ? lst[k] : make_uint2(0u, 0xFFFFFFFFu);
-            }
+        for (int k0 = 0; k0 < maxlen; k0 += 8 * kBatch) {
+            uint2 e[2 * kBatch];
+            load_pairs(k0, e);
             unsigned mine = 0, outr = 0;
 #pragma unroll
-            for (int t = 0; t < kBatch; ++t) {
+            for (int t = 0; t < 2 * kBatch; ++t) {
                 const int d = static_cast<int>(e[t].y);
                 if (d >= 0 && e[t].x < thi) ++mine;
                 if (d >= 0 && e[t].x >= thi) {
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
             }
             unsigned pos = nc + wave_prefix_excl(mine);
 #pragma unroll
-            for (int t = 0; t < kBatch; ++t) {
+            for (int t = 0; t < 2 * kBatch; ++t) {
                 const int d = static_cast<int>(e[t].y);
                 if (d >= 0 && e[t].x < thi) {
                     if (pos < static_cast<unsigned>(kCapB)) {
@@ -580,7 +583,12 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
         else xhi = mid;
     }
     const int X = xlo;
-    // ascending union, one bitmap chunk at a time (one chunk: marked in pass A)
+    // ascending union, one bitmap chunk at a time (one chunk: marked in pass A);
+    // with K_B <= kCapB the output is staged in sBlk (the candidates are in
+    // registers by now) and copied out in order
+    const bool staged = KB <= kCapB;
+    int* sOut = sBlk[w];
+    wave_sync();
     unsigned written = 0;
     for (int c0 = 0; c0 < m; c0 += 64 * kMapWords) {
         const int c1 = min(m, c0 + 64 * kMapWords);
@@ -605,7 +613,10 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
             unsigned pos = written + wave_prefix_excl(cw);
             while (word) {
                 const int bit = __ffsll(static_cast<long long>(word)) - 1;
-                if (pos < static_cast<unsigned>(KB)) out[pos] = c0 + 64 * wi + bit;
+                if (pos < static_cast<unsigned>(KB)) {
+                    if (staged) sOut[pos] = c0 + 64 * wi + bit;
+                    else out[pos] = c0 + 64 * wi + bit;
+                }
                 ++pos;
                 word &= word - 1ull;
             }
@@ -613,6 +624,8 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
         }
         wave_sync();
     }
+    if (staged)
+        for (int j = lane; j < KB; j += 64) out[j] = sOut[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -706,7 +719,7 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
 
 // Sub-list capacity (per query and lane): K_B / 16 + kCapB / 16 or fewer
 // entries on average, with room to spare.
-static int sub_cap(int KB) { return (KB + 15) / 16 + kCapB / 16 + 32; }
+static int sub_cap(int KB) { return ((KB + 15) / 16 + kCapB / 16 + 32 + 1) & ~1; }
 
 // Workspace carving (each piece 256-byte aligned).
 struct TopkLayout {
