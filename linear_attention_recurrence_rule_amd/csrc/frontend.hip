@@ -11,8 +11,9 @@
 // sqrt(sum(x^2) + eps) over the head dimension.
 //
 // One pass per stream (q, k, v), each a pure stream over its input and output
-// (HBM-bound).  A row group of D/4 lanes owns one (sequence, head) and a run
-// of kRun consecutive tokens; each lane owns 4 channels, keeps its filter
+// (HBM-bound).  A row group of lanes owns one (sequence, head) and a run of
+// kRun consecutive tokens; each lane owns 16 bytes of a row (8 bf16 or 4
+// fp32 channels), keeps its filter
 // taps and the last W-1 input rows in registers and slides along the run
 // kStep tokens at a time (their norms reduce together), loading the next
 // step's rows while the current ones are processed.  The L2 norm is a
@@ -30,24 +31,39 @@ namespace frontend {
 constexpr int kRun = 32;   // tokens per row group
 constexpr int kStep = 4;   // tokens processed together (kRun is a multiple)
 
+// Each lane moves 16 bytes of a row: 8 bf16 or 4 fp32 channels.
 template <bool kBf16>
-__device__ __forceinline__ float4v load4(const void* p, long i) {
+struct Lane {
+    static constexpr int N = kBf16 ? 8 : 4;
+    typedef float Vec __attribute__((ext_vector_type(N)));
+};
+
+template <bool kBf16>
+__device__ __forceinline__ typename Lane<kBf16>::Vec loadv(const void* p, long i) {
     if constexpr (kBf16) {
-        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-        return float4v{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
-                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+        const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        typename Lane<kBf16>::Vec v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+        return v;
     } else {
         return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
     }
 }
 
 template <bool kBf16>
-__device__ __forceinline__ void store4(void* p, long i, float4v x) {
+__device__ __forceinline__ void storev(void* p, long i, typename Lane<kBf16>::Vec x) {
     if constexpr (kBf16) {
-        uint2 r;
+        uint4 r;
         r.x = pack_bf16x2(x[0], x[1]);
         r.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = r;
+        r.z = pack_bf16x2(x[4], x[5]);
+        r.w = pack_bf16x2(x[6], x[7]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = r;
     } else {
         *reinterpret_cast<float4v*>(static_cast<float*>(p) + i) = x;
     }
@@ -83,7 +99,9 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
                                                      const float* __restrict__ A, const float* __restrict__ b_alpha,
                                                      float* __restrict__ alpha, float* __restrict__ beta, int B,
                                                      int T, int H, float eps) {
-    constexpr int LPR = D / 4;              // lanes per row
+    using Vec = typename Lane<kBf16>::Vec;
+    constexpr int NC = Lane<kBf16>::N;      // channels per lane
+    constexpr int LPR = D / NC;             // lanes per row
     constexpr int RPB = 256 / LPR;          // row groups per block
     const int tid = threadIdx.x;
     const int sub = tid % LPR;
@@ -96,27 +114,27 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
     if (b >= B) return;                      // whole row groups drop out together
     const int t0 = run * kRun, t1 = min(t0 + kRun, T);
     const long row_stride = static_cast<long>(H) * D;
-    const long base = (static_cast<long>(b) * T * H + h) * D + 4 * sub;   // element (b, t = 0, h, 4 sub)
+    const long base = (static_cast<long>(b) * T * H + h) * D + NC * sub;   // element (b, t = 0, h, NC sub)
 
-    // filter taps of this lane's 4 channels: wt[j][c] = w[h][4 sub + c][j]
-    float4v wt[W];
+    // filter taps of this lane's channels: wt[j][c] = w[h][NC sub + c][j]
+    Vec wt[W];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int j = 0; j < W; ++j) wt[j][c] = w[(static_cast<long>(h) * D + 4 * sub + c) * W + j];
+        for (int j = 0; j < W; ++j) wt[j][c] = w[(static_cast<long>(h) * D + NC * sub + c) * W + j];
 
     // the W-1 rows before t0: from the sequence, the caller's history, or zero
-    float4v win[W > 1 ? W - 1 : 1];
+    Vec win[W > 1 ? W - 1 : 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int t = t0 - (W - 1) + j;
         if (t >= 0) {
-            win[j] = load4<kBf16>(x, base + t * row_stride);
+            win[j] = loadv<kBf16>(x, base + t * row_stride);
         } else if (hist) {
-            const long hb = ((static_cast<long>(b) * (W - 1) + (W - 1 + t)) * H + h) * D + 4 * sub;
-            win[j] = load4<kBf16>(hist, hb);
+            const long hb = ((static_cast<long>(b) * (W - 1) + (W - 1 + t)) * H + h) * D + NC * sub;
+            win[j] = loadv<kBf16>(hist, hb);
         } else {
-            win[j] = float4v{0.f, 0.f, 0.f, 0.f};
+            win[j] = Vec{};
         }
     }
 
@@ -140,29 +158,34 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
     const int last = t1 - 1 - t0;
     const int rs = static_cast<int>(row_stride);
     const long run_base = base + t0 * row_stride;
-    auto load_rows = [&](float4v (&r)[kStep], int r0) {
+    auto load_rows = [&](Vec (&r)[kStep], int r0) {
 #pragma unroll
-        for (int u = 0; u < kStep; ++u) r[u] = load4<kBf16>(x, run_base + min(r0 + u, last) * rs);
+        for (int u = 0; u < kStep; ++u) r[u] = loadv<kBf16>(x, run_base + min(r0 + u, last) * rs);
     };
-    auto step = [&](float4v (&cur)[kStep], float4v (&nxt)[kStep], int r0) {
+    auto step = [&](Vec (&cur)[kStep], Vec (&nxt)[kStep], int r0) {
         if (r0 + kStep <= last) load_rows(nxt, r0 + kStep);
-        float4v s[kStep];
+        Vec s[kStep];
 #pragma unroll
         for (int u = 0; u < kStep; ++u) {
             // conv over rows r0+u-(W-1) .. r0+u: the window holds the W-1 rows
             // before r0, cur the rows r0 .. r0+kStep-1
-            float4v c = wt[W - 1] * cur[u];
+            Vec c = wt[W - 1] * cur[u];
 #pragma unroll
             for (int j = 0; j < W - 1; ++j) {
                 const int src = u - (W - 1) + j;   // row r0 + src
                 c += wt[j] * (src >= 0 ? cur[src >= 0 ? src : 0] : win[(W - 1) + src >= 0 ? (W - 1) + src : 0]);
             }
-            s[u] = float4v{silu(c[0]), silu(c[1]), silu(c[2]), silu(c[3])};
+#pragma unroll
+            for (int e = 0; e < NC; ++e) s[u][e] = silu(c[e]);
         }
         if constexpr (kNorm) {
             float ss[kStep];
 #pragma unroll
-            for (int u = 0; u < kStep; ++u) ss[u] = s[u][0] * s[u][0] + s[u][1] * s[u][1] + s[u][2] * s[u][2] + s[u][3] * s[u][3];
+            for (int u = 0; u < kStep; ++u) {
+                ss[u] = 0.f;
+#pragma unroll
+                for (int e = 0; e < NC; ++e) ss[u] += s[u][e] * s[u][e];
+            }
 #pragma unroll
             for (int u = 0; u < kStep; ++u) ss[u] = row_sum<LPR>(ss[u]);
 #pragma unroll
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         }
 #pragma unroll
         for (int u = 0; u < kStep; ++u)
-            if (r0 + u <= last) store4<kBf16>(out, run_base + (r0 + u) * rs, s[u]);
+            if (r0 + u <= last) storev<kBf16>(out, run_base + (r0 + u) * rs, s[u]);
         // the window moves to the last W-1 rows of this step
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
@@ -179,7 +202,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         }
     };
     // steps in pairs over two register sets, so that no copies are needed
-    float4v ra[kStep], rb[kStep];
+    Vec ra[kStep], rb[kStep];
     load_rows(ra, 0);
     for (int r0 = 0; r0 <= last; r0 += 2 * kStep) {
         step(ra, rb, r0);
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 
 template <int D, int W, bool kNorm, bool kGates, bool kBf16>
 static hipError_t launch_stream(const void* x, const float* w, const void* hist, void* out, const FrontendArgs& a) {
-    constexpr int RPB = 256 / (D / 4);
+    constexpr int RPB = 256 / (D / Lane<kBf16>::N);
     const long tasks = static_cast<long>(a.B) * a.H * ((a.T + kRun - 1) / kRun);
     const long blocks = (tasks + RPB - 1) / RPB;
     hipLaunchKernelGGL((stream_kernel<D, W, kNorm, kGates, kBf16>), dim3(static_cast<unsigned>(blocks)), dim3(256),
