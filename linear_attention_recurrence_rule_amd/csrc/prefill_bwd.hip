@@ -38,30 +38,18 @@ namespace bwd {
 constexpr int C = 64;
 constexpr float kLogFloor = -30.f;   // same floor of log(alpha) as the forward
 
-// acc += A B for one 16x16 tile over k in [k0, k1).  Lane l supplies
-// A[l % 16][k + l / 16] and B[k + l / 16][l % 16] (the fp32 MFMA layout).
+// acc += A B for one 16x16 tile over k in [k0, k0 + N), fp32 MFMA 16x16x4.
 //   kAt = false: A row-major (A[r][k] at A[r * lda + k], A at the tile's first row)
 //   kAt = true:  A stored transposed (A[r][k] at A[k * lda + r], A at the tile's first row index)
 //   kBr = false: B given transposed (B[k][n] at B[n * ldb + k], B at the tile's first column)
 //   kBr = true:  B row-major (B[k][n] at B[k * ldb + n], B at the tile's first column)
 // so a tile stored row-major serves both as an operand and as its transpose.
-template <bool kAt, bool kBr>
-__device__ __forceinline__ float4v mma(const float* A, int lda, const float* B, int ldb, int k0, int k1,
-                                       float4v acc) {
-    const int l = threadIdx.x & 63, r = l & 15, kk = l >> 4;
-    for (int k = k0; k < k1; k += 4) {
-        const float a = kAt ? A[(k + kk) * lda + r] : A[r * lda + k + kk];
-        const float b = kBr ? B[(k + kk) * ldb + r] : B[r * ldb + k + kk];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-    }
-    return acc;
-}
-// The same product over a compile-time length N = k1 - k0 with a split-K lane
-// layout: lane group l / 16 owns the contiguous run [k0 + (l/16) N/4, ... + N/4)
-// and step s takes element s of every run (the four partial sums of one MFMA
-// cover different k, and their total is the same contraction).  All operand
-// values are read from LDS before the first MFMA, so the dependent MFMA chain
-// never waits on LDS latency; row-major runs are read as float4.
+// Split-K lane layout: lane group l / 16 owns the contiguous run
+// [k0 + (l/16) N/4, ... + N/4) and step s takes element s of every run (the
+// four partial sums of one MFMA cover different k, and their total is the
+// same contraction).  All operand values are read from LDS before the first
+// MFMA, so the dependent MFMA chain never waits on LDS latency; row-major
+// runs are read as float4.
 template <bool kAt, bool kBr, int N>
 __device__ __forceinline__ float4v mma_n(const float* A, int lda, const float* B, int ldb, int k0, float4v acc) {
     constexpr int S = N / 4;
@@ -91,17 +79,22 @@ __device__ __forceinline__ float4v mma_n(const float* A, int lda, const float* B
     for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
     return acc;
 }
-// acc += (A + A^T) B, A row-major (square, leading dimension lda), rows r0..r0+15
-// of the sum; B row-major at the tile's first column.
-__device__ __forceinline__ float4v mma_sym(const float* A, int lda, int r0, const float* B, int ldb, int k0,
-                                           int k1, float4v acc) {
-    const int l = threadIdx.x & 63;
-    for (int k = k0; k < k1; k += 4) {
-        const int r = r0 + (l & 15), kk = k + (l >> 4);
-        const float a = A[r * lda + kk] + A[kk * lda + r];
-        const float b = B[kk * ldb + (l & 15)];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+// acc += (A + A^T) B over k in [k0, k0 + N): A row-major and square (leading
+// dimension lda), rows r0 .. r0 + 15 of the sum; B row-major at the tile's
+// first column.  Split-K lane layout of mma_n, operands read first.
+template <int N>
+__device__ __forceinline__ float4v mma_sym_n(const float* A, int lda, int r0, const float* B, int ldb, int k0,
+                                             float4v acc) {
+    constexpr int S = N / 4;
+    const int l = threadIdx.x & 63, r = r0 + (l & 15), kb = k0 + (l >> 4) * S;
+    float a[S], b[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        a[s] = A[r * lda + kb + s] + A[(kb + s) * lda + r];
+        b[s] = B[(kb + s) * ldb + (l & 15)];
     }
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
     return acc;
 }
 
@@ -252,8 +245,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
         const int p = wave * 4 + u, ti = p >> 2, tj = p & 3;
         kk[u] = qk[u] = float4v{0.f, 0.f, 0.f, 0.f};
         if (tj <= ti) {
-            kk[u] = mma<false, false>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, kk[u]);
-            qk[u] = mma<false, false>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, DK, qk[u]);
+            kk[u] = mma_n<false, false, DK>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, kk[u]);
+            qk[u] = mma_n<false, false, DK>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, qk[u]);
         }
     }
     __syncthreads();                                   // Q is no longer read: its space takes A
@@ -850,7 +843,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
             }
             aq = mma_n<false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
-            ak = mma_sym(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, C, ak);
+            ak = mma_sym_n<C>(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, ak);
             ak = mma_n<true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
