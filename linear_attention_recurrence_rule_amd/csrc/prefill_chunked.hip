@@ -120,216 +120,276 @@ __device__ __forceinline__ half8 ld_split_tr(const _Float16* base, int m0, int k
 }
 
 // ===========================================================================
-// prep_kernel: T' = (I + A)^-1 diag(beta) for one (head, chunk).
+// prep_kernel: T' = (I + A)^-1 diag(beta) for one (head, chunk), one wave per
+// chunk.  Every product runs from registers, so the waves never wait for one
+// another:
+//   * the Gram tiles K_J K_I^T come from bf16 MFMAs on k fragments loaded
+//     straight from HBM (each lane: 16 rows x 8 columns per 32-wide step; the
+//     same fragment serves as the A operand of one tile and the B operand of
+//     another);
+//   * each lane then holds 4 consecutive columns of one row of A, which is
+//     exactly the A operand of a 16x16x16 MFMA, so A's sub-diagonal blocks stay
+//     in registers;
+//   * the 16x16 diagonal blocks of T are inverted by forward substitution in
+//     float32 (lane = (block, column)), then one block sub-diagonal per step,
+//         T'_IJ = -T_II * sum_{K=J}^{I-1} A_IK T'_KJ,   T'_JJ = T_JJ diag(beta_J),
+//     (the column scaling by beta commutes with the sum, so T' is built
+//     directly), whose accumulator layout is again the B operand of the next
+//     step.
+// The k fragments of the wave's next chunk are loaded as soon as the Gram
+// tiles no longer need them.  Per-wave LDS only stages the diagonal blocks and
+// the output.
 // ===========================================================================
+constexpr int kPrepWaves = 4;        // waves (chunks in flight) per workgroup
+constexpr int kPrepResidentWGs = 512; // two workgroups per CU
+
 template <int DK>
 struct PrepCfg {
-    static constexpr int LDQ = DK + 8;   // padded rows (fp16)
-    static constexpr int LDC = C + 8;
-    static constexpr int LDA = 16 + 4;   // float rows of a diagonal block, 16-byte aligned
-    static constexpr int LDX = 16 + 8;
-    static constexpr int NB = chunked::NB;
-    static constexpr int NW = 4;
+    static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1;   // MFMA K steps over d_k
+    static constexpr int LDA = 16 + 4;                     // float row stride of a diagonal block
+    static constexpr int ABLK = 16 * LDA + 8;              // float stride between blocks (bank offset)
 };
 
-// K is dead once A is formed, so T (row-major and transposed) reuses its
-// space; the whole set fits four workgroups in a CU's LDS.
-template <int DK>
-struct alignas(16) PrepSmem {
-    using Cfg = PrepCfg<DK>;
-    struct TPair {
-        _Float16 Tm[C * Cfg::LDC];
-        _Float16 TT[C * Cfg::LDC];
-    };
-    union {
-        _Float16 K[C * Cfg::LDQ];
-        TPair tp;
-    };
-    _Float16 A16[C * Cfg::LDC];
-    _Float16 X[Cfg::NW][16 * Cfg::LDX];
-    float Ad[NB][16 * Cfg::LDA];   // the diagonal 16x16 blocks of A in float32
+// One wave's staging area.
+struct alignas(16) PrepWaveSmem {
+    float Ad[NB * (16 * (16 + 4) + 8)];   // diagonal blocks of A, float32 row-major
+    _Float16 Tr[NTB * TBLK];               // T', lower blocks row-major (the output)
+    _Float16 Tc[NB * TBLK];                // diagonal blocks of T', column-major
+    _Float16 Tu[NB * TBLK];                // diagonal blocks of T (unscaled), row-major
     float g[C], beta[C];
 };
 
-// T = (I + A)^-1 for the unit lower-triangular chunk system, from A in
-// sm.A16 (fp16) and its diagonal blocks in sm.Ad (float32).  The 16x16 diagonal blocks are
-// inverted by forward substitution in float32 (one block per wave, one column
-// per lane); then one block sub-diagonal per step,
-//     T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ,
-// whose terms all lie on earlier sub-diagonals.  Writes sm.tp.Tm (row-major)
-// and sm.tp.TT (transposed).  Contains workgroup barriers: call from all 4 waves.
-template <class Cfg, class Smem>
-__device__ __forceinline__ void build_T(Smem& sm, int w, int l) {
-    using M = Mma<_Float16>;
-    constexpr int LDC = Cfg::LDC, LDA = Cfg::LDA, LDX = Cfg::LDX, NW = Cfg::NW;
-    const int lr = l & 15, lq = l >> 4;
-    if (w < NB && l < 16) {
-        const int base = w * 16;
-        float x[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = (t == l) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < t; ++i) acc -= sm.Ad[w][t * LDA + i] * x[i];
-            x[t] = acc;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            sm.tp.Tm[(base + t) * LDC + base + l] = static_cast<_Float16>(x[t]);
-            sm.tp.TT[(base + l) * LDC + base + t] = static_cast<_Float16>(x[t]);
-        }
-    }
-    __syncthreads();
-    static_assert(NW >= NB - 1, "one block of each sub-diagonal per wave");
-#pragma unroll
-    for (int lev = 1; lev < NB; ++lev) {
-        const int J = w;
-        if (J + lev < NB) {
-            const int I = J + lev;
-            const float4v x = M::range(sm.A16 + I * 16 * LDC, LDC, sm.tp.TT + J * 16 * LDC, LDC, J * 16, I * 16,
-                                       float4v{0.f, 0.f, 0.f, 0.f});
-            _Float16* Xw = sm.X[w];
-            *reinterpret_cast<half4*>(&Xw[lr * LDX + 4 * lq]) = to_h4(x);   // X transposed
-            const float4v t = M::range(sm.tp.Tm + I * 16 * LDC + I * 16, LDC, Xw, LDX, 0, 16,
-                                       float4v{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sm.tp.Tm[(I * 16 + 4 * lq + j) * LDC + J * 16 + lr] = static_cast<_Float16>(-t[j]);
-            *reinterpret_cast<half4*>(&sm.tp.TT[(J * 16 + lr) * LDC + I * 16 + 4 * lq]) =
-                to_h4(-t[0], -t[1], -t[2], -t[3]);
-        }
-        __syncthreads();
-    }
+template <int DK>
+struct PrepFrag {
+    static constexpr bool kWide = DK >= 32;
+    using type = typename std::conditional<kWide, uint4, uint2>::type;
+};
+
+__device__ __forceinline__ float4v mma_gram(uint4 a, uint4 b, float4v c) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ float4v mma_gram(uint2 a, uint2 b, float4v c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                    0, 0, 0);
+}
+__device__ __forceinline__ float4v mma16(half4 a, half4 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void prep_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__host__ __device__ constexpr int lower_tile(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8
+// within each row of 16 lanes (zeros shifted in), then the last lane of row 0
+// added to row 1 and of row 2 to row 3, then lane 31 added to rows 2 and 3.
+template <int kCtrl, int kRowMask, bool kZeroFill>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, kZeroFill));
+}
+__device__ __forceinline__ float wave_scan_incl(float v) {
+    v += dpp_move<0x111, 0xf, true>(v);   // row_shr:1
+    v += dpp_move<0x112, 0xf, true>(v);   // row_shr:2
+    v += dpp_move<0x114, 0xf, true>(v);   // row_shr:4
+    v += dpp_move<0x118, 0xf, true>(v);   // row_shr:8
+    v += dpp_move<0x142, 0xa, false>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc, false>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
 // Workspace layout: for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
 // 16x16 blocks of T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each
 // row-major fp16, then the float32 gates g[C], gamma[C], d[C].
 //
-// One workgroup handles kPrepChunks consecutive chunks of one head; the k
-// rows, alpha and beta of the next chunk are loaded into registers while the
-// current chunk is processed.  Rows past the end of the sequence load the last
-// row (their beta is 0, so A has zero rows there and they never matter).
-constexpr int kPrepChunks = 4;
-
+// Grid (ceil(B*H / kPrepWaves), ceil(chunks / cpw)): wave w of workgroup
+// (x, y) takes head bh = kPrepWaves x + w and its chunks y cpw + j, j < cpw.
+// Neighbouring workgroups run the same chunks of neighbouring heads, so the k
+// rows in flight at one time are whole token rows of the (token, head, d_k)
+// tensor rather than scattered 256-byte pieces.  cpw is chosen so that the
+// grid is about one round of resident workgroups: each wave then pays the
+// latency of its first k load once and hides the others behind its work.
+// Rows past the end of the sequence load the last row (their beta is 0, so A
+// has zero rows there and they never matter).
 template <int DK>
-__global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
-                                                   _Float16* __restrict__ ws, int T, int H, int nchunks) {
+                                                   _Float16* __restrict__ ws, int T, int H, int BH, int nchunks, int cpw) {
     using Cfg = PrepCfg<DK>;
-    using M = Mma<_Float16>;
-    constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDA = Cfg::LDA;
-    constexpr int NKP = (C * DK / 8 + 255) / 256;   // 16-byte k pieces per thread
-    __shared__ PrepSmem<DK> sm;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    using Frag = typename PrepFrag<DK>::type;
+    constexpr int KS = Cfg::KSTEP, LDA = Cfg::LDA, ABLK = Cfg::ABLK;
+    constexpr int FW = PrepFrag<DK>::kWide ? 8 : 4;   // bf16 elements per lane and K step
+    __shared__ PrepWaveSmem smem[kPrepWaves];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int lr = l & 15, lq = l >> 4;
-    const int bh = blockIdx.y;
+    PrepWaveSmem& sm = smem[w];
+    const int bh = static_cast<int>(blockIdx.x) * kPrepWaves + w;
+    if (bh >= BH) return;   // no workgroup barriers below
     const int b = bh / H, h = bh % H;
     const long tok0 = static_cast<long>(b) * T;
-    const int c_begin = blockIdx.x * kPrepChunks;
-    const int c_end = min(c_begin + kPrepChunks, nchunks);
+    auto chunk_of = [&](int j) { return static_cast<int>(blockIdx.y) * cpw + j; };
 
-    uint4 kr[NKP];
+    // lane (r + 16 g) of fragment [I][kk]: k row 16 I + r, columns kk * 32 + FW g .. + FW
+    Frag kf[NB][KS];
     float ar = 1.f, br = 0.f;
     auto load = [&](int chunk) {
         const int t0 = chunk * C;
 #pragma unroll
-        for (int i = 0; i < NKP; ++i) {
-            const int idx = min(tid + i * 256, C * DK / 8 - 1);
-            const int row = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            kr[i] = *reinterpret_cast<const uint4*>(k + ((tok0 + min(t0 + row, T - 1)) * H + h) * DK + c8);
+        for (int I = 0; I < NB; ++I) {
+            const uint16_t* p = k + ((tok0 + min(t0 + 16 * I + lr, T - 1)) * H + h) * DK + FW * lq;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) kf[I][kk] = *reinterpret_cast<const Frag*>(p + 32 * kk);
         }
-        if (w == 0) {
-            const long off = (tok0 + min(t0 + l, T - 1)) * H + h;
-            ar = alpha[off];
-            br = beta[off];
-        }
+        const long off = (tok0 + min(t0 + l, T - 1)) * H + h;
+        ar = alpha[off];
+        br = beta[off];
     };
-    if (c_begin < c_end) load(c_begin);
+    if (chunk_of(0) < nchunks) load(chunk_of(0));
 
-    for (int chunk = c_begin; chunk < c_end; ++chunk) {
+    for (int j = 0; j < cpw; ++j) {
+        const int chunk = chunk_of(j);
+        if (chunk >= nchunks) break;
         const int t0 = chunk * C;
-        // k rows (bf16 -> fp16) into LDS
-#pragma unroll
-        for (int i = 0; i < NKP; ++i) {
-            const int idx = tid + i * 256;
-            if (idx < C * DK / 8) {
-                const int row = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-                const uint32_t wds[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-                half8 hv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    hv[2 * j] = static_cast<_Float16>(__uint_as_float(wds[j] << 16));
-                    hv[2 * j + 1] = static_cast<_Float16>(__uint_as_float(wds[j] & 0xffff0000u));
-                }
-                *reinterpret_cast<half8*>(&sm.K[row * LDQ + c8]) = hv;
-            }
-        }
-        if (w == 0) {
-            // past the end: identity steps (alpha = 1, beta = 0)
+        // gates: in-chunk prefix sum of log alpha (identity steps past the end)
+        float lg;
+        {
             const float a = (t0 + l < T) ? ar : 1.f, be = (t0 + l < T) ? br : 0.f;
-            float lg = fmaxf(logf(a), kLogDecayFloor);
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float t = __shfl_up(lg, off, 64);
-                if (l >= off) lg += t;
-            }
+            lg = wave_scan_incl(fmaxf(logf(a), kLogDecayFloor));
             sm.g[l] = lg;
             sm.beta[l] = be;
         }
-        __syncthreads();
-        // the next chunk's loads fly while this one is processed
-        if (chunk + 1 < c_end) load(chunk + 1);
-
-        // A = strictLower(diag(beta) (Gamma o K K^T)), tiles computed transposed
-        // (K_J K_I^T) so that each lane holds 4 consecutive columns of one row.
-        // (Straight-line code: a loop header here would make the compiler wait
-        // for the next chunk's loads.)
+        prep_wave_sync();
+        // Gram tiles K_J K_I^T (I >= J) in two groups of five independent
+        // chains, each masked into A = strictLower(diag(beta) (Gamma o K K^T))
+        // at once.  Lane (r + 16 g) of tile (I, J) holds row 16 I + r, columns
+        // 16 J + 4 g .. + 4.
+        half4 ah[NTB];
 #pragma unroll
-        for (int it = 0; it < (NTB + Cfg::NW - 1) / Cfg::NW; ++it) {
-            const int tile = w + it * Cfg::NW;
-            if (tile >= NTB) break;
-            const int I = lower_block_row(tile), J = tile - I * (I + 1) / 2;
-            const float4v acc = M::range(sm.K + J * 16 * LDQ, LDQ, sm.K + I * 16 * LDQ, LDQ, 0, DK,
-                                         float4v{0.f, 0.f, 0.f, 0.f});
-            const int t = I * 16 + lr, i0 = J * 16 + 4 * lq;
-            const float gt = sm.g[t], bt = sm.beta[t];
-            float a[4];
+        for (int grp = 0; grp < 2; ++grp) {
+            float4v acc[5];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a[j] = (i0 + j < t) ? bt * __expf(gt - sm.g[i0 + j]) * acc[j] : 0.f;
-            if (I == J) *reinterpret_cast<float4v*>(&sm.Ad[I][lr * LDA + 4 * lq]) = float4v{a[0], a[1], a[2], a[3]};
-            *reinterpret_cast<half4*>(&sm.A16[t * LDC + i0]) = to_h4(a[0], a[1], a[2], a[3]);
+            for (int u = 0; u < 5; ++u) acc[u] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+                for (int u = 0; u < 5; ++u) {
+                    const int t = grp * 5 + u, I = lower_block_row(t), J = t - I * (I + 1) / 2;
+                    acc[u] = mma_gram(kf[J][kk], kf[I][kk], acc[u]);
+                }
+            // the fragments are dead after the second group: the next chunk's loads fly from here on
+            if (grp == 1 && j + 1 < cpw && chunk_of(j + 1) < nchunks) load(chunk_of(j + 1));
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int t = grp * 5 + u, I = lower_block_row(t), J = t - I * (I + 1) / 2;
+                const int row = I * 16 + lr, col0 = J * 16 + 4 * lq;
+                const float gt = sm.g[row], bt = sm.beta[row];
+                const float4v gi = *reinterpret_cast<const float4v*>(&sm.g[col0]);
+                float a[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = bt * __expf(gt - gi[e]) * acc[u][e];   // inf above the diagonal: not selected
+                    a[e] = (I > J || col0 + e < row) ? v : 0.f;
+                }
+                if (I == J)
+                    *reinterpret_cast<float4v*>(&sm.Ad[I * ABLK + lr * LDA + 4 * lq]) = float4v{a[0], a[1], a[2], a[3]};
+                else
+                    ah[t] = to_h4(a[0], a[1], a[2], a[3]);
+            }
         }
-        __syncthreads();
-        build_T<Cfg>(sm, w, l);
+        prep_wave_sync();
 
-        // T' = T diag(beta), lower blocks, 8 halfs per item
+        // diagonal blocks of T = (I + A)^-1: lane (c + 16 bd) solves column c of
+        // block bd, whose beta (token 16 bd + c) is the lane's own
+        {
+            const int bd = lq, c = lr;
+            const float* Ab = sm.Ad + bd * ABLK;
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float s0 = (t == c) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                for (int i4 = 0; i4 < (t + 3) / 4; ++i4) {
+                    const float4v a4 = *reinterpret_cast<const float4v*>(&Ab[t * LDA + 4 * i4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        if (i < t) {
+                            if (e & 1) s1 -= a4[e] * x[i];
+                            else s0 -= a4[e] * x[i];
+                        }
+                    }
+                }
+                x[t] = s0 + s1;
+            }
+            const float bc = sm.beta[l];
+            half8 lo, hi;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                lo[t] = static_cast<_Float16>(x[t] * bc);
+                hi[t] = static_cast<_Float16>(x[t + 8] * bc);
+            }
+            *reinterpret_cast<half8*>(&sm.Tc[bd * TBLK + c * 16]) = lo;
+            *reinterpret_cast<half8*>(&sm.Tc[bd * TBLK + c * 16 + 8]) = hi;
+            _Float16* Td = sm.Tr + lower_tile(bd, bd) * TBLK;
+            _Float16* Tud = sm.Tu + bd * TBLK;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                Td[t * 16 + c] = lo[t];
+                Td[(t + 8) * 16 + c] = hi[t];
+                Tud[t * 16 + c] = static_cast<_Float16>(x[t]);
+                Tud[(t + 8) * 16 + c] = static_cast<_Float16>(x[t + 8]);
+            }
+        }
+        prep_wave_sync();
+
+        // off-diagonal blocks, one sub-diagonal per step, in accumulator layout
+        // (lane (n + 16 g): rows 4 g .. + 4 of column n), which is the B operand
+        // layout of the next step's products
+        half4 tcl[NB], trl[NB], th[NTB];
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            tcl[I] = *reinterpret_cast<const half4*>(&sm.Tc[I * TBLK + lr * 16 + 4 * lq]);   // T'_II, B layout
+            trl[I] = *reinterpret_cast<const half4*>(&sm.Tu[I * TBLK + lr * 16 + 4 * lq]);   // T_II, A layout
+        }
+#pragma unroll
+        for (int lev = 1; lev < NB; ++lev) {
+#pragma unroll
+            for (int J = 0; J + lev < NB; ++J) {
+                const int I = J + lev;
+                float4v y = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int Kb = J; Kb < I; ++Kb) y = mma16(ah[lower_tile(I, Kb)], Kb == J ? tcl[J] : th[lower_tile(Kb, J)], y);
+                const float4v t = mma16(trl[I], to_h4(y), float4v{0.f, 0.f, 0.f, 0.f});
+                const half4 tn = to_h4(-t[0], -t[1], -t[2], -t[3]);
+                th[lower_tile(I, J)] = tn;
+                _Float16* To = sm.Tr + lower_tile(I, J) * TBLK;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) To[(4 * lq + e) * 16 + lr] = tn[e];
+            }
+        }
+        prep_wave_sync();
+
+        // T' out, in 16-byte pieces
         _Float16* dst = ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK;
 #pragma unroll
-        for (int it = 0; it < (NTB * TBLK / 8 + 255) / 256; ++it) {
-            const int idx = tid + it * 256;
-            if (idx >= NTB * TBLK / 8) break;
-            const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-            const int I = lower_block_row(blk), J = blk - I * (I + 1) / 2;
-            const half8 tv = *reinterpret_cast<const half8*>(&sm.tp.Tm[(I * 16 + r) * LDC + J * 16 + 8 * hh]);
-            half8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[e] = static_cast<_Float16>(static_cast<float>(tv[e]) * sm.beta[J * 16 + 8 * hh + e]);
-            *reinterpret_cast<half8*>(dst + blk * TBLK + r * 16 + 8 * hh) = o;
+        for (int it = 0; it < NTB * TBLK / 8 / 64; ++it) {
+            const int idx = l + it * 64;
+            *reinterpret_cast<half8*>(dst + 8 * idx) = *reinterpret_cast<const half8*>(&sm.Tr[8 * idx]);
         }
         // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
-        // (stored after the next chunk's loads have been issued)
-        if (w == 0) {
-            const float lg = sm.g[l], glast = sm.g[C - 1];
-            float* gate =
-                reinterpret_cast<float*>(ws + (static_cast<long>(bh) * nchunks + chunk) * WS_CHUNK + NTB * TBLK);
+        {
+            const float glast = __shfl(lg, 63, 64);
+            float* gate = reinterpret_cast<float*>(dst + NTB * TBLK);
             gate[l] = lg;
             gate[C + l] = expf(lg);
             gate[2 * C + l] = expf(glast - lg);
         }
-        __syncthreads();   // LDS is reused by the next chunk
+        prep_wave_sync();   // the staging area is rewritten by the next chunk
     }
 }
 
@@ -872,9 +932,14 @@ static hipError_t launch_t(const PrefillArgs& a) {
     const int nchunks = (a.T + C - 1) / C;
     _Float16* ws = static_cast<_Float16*>(a.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK>), dim3((nchunks + kPrepChunks - 1) / kPrepChunks, a.B * a.H), dim3(256), 0,
-                           a.stream,
-                           static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, a.T, a.H, nchunks);
+        // chunks per wave: about one round of resident workgroups, at most 16
+        const int BH = a.B * a.H;
+        const long gx = (BH + kPrepWaves - 1) / kPrepWaves;
+        const int cpw = static_cast<int>(
+            std::min<long>(16, std::max<long>(1, (gx * nchunks + kPrepResidentWGs - 1) / kPrepResidentWGs)));
+        const int gy = (nchunks + cpw - 1) / cpw;
+        hipLaunchKernelGGL((prep_kernel<DK>), dim3(static_cast<unsigned>(gx), gy), dim3(256), 0, a.stream,
+                           static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, a.T, a.H, BH, nchunks, cpw);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
