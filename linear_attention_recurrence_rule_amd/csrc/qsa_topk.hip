@@ -675,6 +675,9 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
 #pragma unroll
                     for (int kk = 0; kk < D / 32; ++kk) bv[u][kk] = *reinterpret_cast<const bf16x8*>(Bt + 32 * kk);
                 }
+                // all loads in flight before the first use (the scheduler would otherwise
+                // reuse one register set and wait on every load)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < kG; ++u)
 #pragma unroll
@@ -703,10 +706,9 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
         if (lane == 0) smax[w] = mx;
-        // the row is read back by wave 0: finish the stores and read through L2
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // the row is read back by wave 0; the barrier's workgroup-scope ordering
+        // covers the scratch row too (all waves of a workgroup share one CU)
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (w == 0) {
             float rmx = 0.f;
 #pragma unroll

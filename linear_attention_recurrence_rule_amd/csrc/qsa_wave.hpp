@@ -23,29 +23,33 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-__device__ __forceinline__ unsigned wave_suffix_incl(unsigned x) {     // sum over lanes >= this lane
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned y = __shfl_down(x, off);
-        if (lane + off < 64) x += y;
-    }
-    return x;
+// Wave-wide sums and scans with DPP lane moves (no LDS round trips): shifts
+// by 1, 2, 4 and 8 lanes within each row of 16 (zeros shifted in), then the
+// last lane of rows 0 and 2 added into rows 1 and 3, then lane 31 into rows 2
+// and 3.
+template <int kCtrl, int kRowMask, bool kZeroFill>
+__device__ __forceinline__ unsigned dpp_u(unsigned v) {
+    return static_cast<unsigned>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xf, kZeroFill));
 }
-__device__ __forceinline__ unsigned wave_prefix_excl(unsigned v) {     // sum over lanes < this lane
-    const int lane = threadIdx.x & 63;
-    unsigned x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x - v;
+__device__ __forceinline__ unsigned wave_scan_incl_u(unsigned x) {      // sum over lanes <= this lane
+    x += dpp_u<0x111, 0xf, true>(x);    // row_shr:1
+    x += dpp_u<0x112, 0xf, true>(x);    // row_shr:2
+    x += dpp_u<0x114, 0xf, true>(x);    // row_shr:4
+    x += dpp_u<0x118, 0xf, true>(x);    // row_shr:8
+    x += dpp_u<0x142, 0xa, false>(x);   // row_bcast:15
+    x += dpp_u<0x143, 0xc, false>(x);   // row_bcast:31
+    return x;
 }
 __device__ __forceinline__ unsigned wave_sum_u(unsigned x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(wave_scan_incl_u(x)), 63));
+}
+__device__ __forceinline__ unsigned wave_prefix_excl(unsigned v) {     // sum over lanes < this lane
+    return wave_scan_incl_u(v) - v;
+}
+__device__ __forceinline__ unsigned wave_suffix_incl(unsigned x) {     // sum over lanes >= this lane
+    const unsigned incl = wave_scan_incl_u(x);
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63)) - incl + x;
 }
 
 // Bin beta of an nbins histogram with count(> beta) < need <= count(>= beta);
