@@ -141,7 +141,7 @@ __device__ __forceinline__ half8 ld_split_tr(const _Float16* base, int m0, int k
 // the output.
 // ===========================================================================
 constexpr int kPrepWaves = 4;        // waves (chunks in flight) per workgroup
-constexpr int kPrepResidentWGs = 512; // two workgroups per CU
+constexpr int kPrepResidentWGs = 768; // three workgroups per CU
 
 template <int DK>
 struct PrepCfg {
@@ -150,12 +150,18 @@ struct PrepCfg {
     static constexpr int ABLK = 16 * LDA + 8;              // float stride between blocks (bank offset)
 };
 
-// One wave's staging area.
+// One wave's staging area.  The diagonal blocks of A are dead once the
+// substitution has read them, so the diagonal blocks of T reuse their space
+// (one wave's LDS reads and writes execute in program order).
 struct alignas(16) PrepWaveSmem {
-    float Ad[NB * (16 * (16 + 4) + 8)];   // diagonal blocks of A, float32 row-major
-    _Float16 Tr[NTB * TBLK];               // T', lower blocks row-major (the output)
-    _Float16 Tc[NB * TBLK];                // diagonal blocks of T', column-major
-    _Float16 Tu[NB * TBLK];                // diagonal blocks of T (unscaled), row-major
+    union {
+        float Ad[NB * (16 * (16 + 4) + 8)];   // diagonal blocks of A, float32 row-major
+        struct {
+            _Float16 Tc[NB * TBLK];           // diagonal blocks of T', column-major
+            _Float16 Tu[NB * TBLK];           // diagonal blocks of T (unscaled), row-major
+        } t;
+    };
+    _Float16 Tr[NTB * TBLK];                  // T', lower blocks row-major (the output)
     float g[C], beta[C];
 };
 
@@ -216,7 +222,7 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
 // Rows past the end of the sequence load the last row (their beta is 0, so A
 // has zero rows there and they never matter).
 template <int DK>
-__global__ __launch_bounds__(256, 2) void prep_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
                                                    _Float16* __restrict__ ws, int T, int H, int BH, int nchunks, int cpw) {
@@ -333,10 +339,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const uint16_t* __restrict
                 lo[t] = static_cast<_Float16>(x[t] * bc);
                 hi[t] = static_cast<_Float16>(x[t + 8] * bc);
             }
-            *reinterpret_cast<half8*>(&sm.Tc[bd * TBLK + c * 16]) = lo;
-            *reinterpret_cast<half8*>(&sm.Tc[bd * TBLK + c * 16 + 8]) = hi;
+            *reinterpret_cast<half8*>(&sm.t.Tc[bd * TBLK + c * 16]) = lo;
+            *reinterpret_cast<half8*>(&sm.t.Tc[bd * TBLK + c * 16 + 8]) = hi;
             _Float16* Td = sm.Tr + lower_tile(bd, bd) * TBLK;
-            _Float16* Tud = sm.Tu + bd * TBLK;
+            _Float16* Tud = sm.t.Tu + bd * TBLK;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 Td[t * 16 + c] = lo[t];
@@ -353,8 +359,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const uint16_t* __restrict
         half4 tcl[NB], trl[NB], th[NTB];
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
-            tcl[I] = *reinterpret_cast<const half4*>(&sm.Tc[I * TBLK + lr * 16 + 4 * lq]);   // T'_II, B layout
-            trl[I] = *reinterpret_cast<const half4*>(&sm.Tu[I * TBLK + lr * 16 + 4 * lq]);   // T_II, A layout
+            tcl[I] = *reinterpret_cast<const half4*>(&sm.t.Tc[I * TBLK + lr * 16 + 4 * lq]);   // T'_II, B layout
+            trl[I] = *reinterpret_cast<const half4*>(&sm.t.Tu[I * TBLK + lr * 16 + 4 * lq]);   // T_II, A layout
         }
 #pragma unroll
         for (int lev = 1; lev < NB; ++lev) {
