@@ -633,10 +633,151 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
 // queries x, x + kExactWGs, ...  The waves score the row 16 blocks at a time
 // with the MFMA step of the scoring passes (the query's heads as A rows 0..3;
 // eight groups' key loads in flight) into LDS (rows up to kExactLds blocks)
-// or the workgroup's scratch row (ld floats), then wave 0 selects on it
-// exactly.
+// or the workgroup's scratch row (ld floats), then the workgroup selects on
+// it exactly (select_row_wg).
 // ---------------------------------------------------------------------------
 constexpr int kExactWGs = 256;
+
+// Workgroup-cooperative form of select_row (the same rules and result) for
+// the exact pass: the NW waves share the value histogram and the gathering of
+// the threshold bin, wave 0 ranks that bin (or runs the radix select), and the
+// ordered compaction runs per contiguous wave segment of the row, a count pass
+// and then the writes at the segment's offset.  sw holds NW + 8 words.
+template <int NW>
+__device__ void select_row_wg(const float* row, int m, int KB, float mx, int* out, unsigned* hist, unsigned* sck,
+                              int* sci, unsigned* sw) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m4 = (m + 3) / 4;
+    const int seg = ((m4 + NW - 1) / NW + 63) / 64 * 64;   // float4 groups per wave, whole steps
+    const int g_lo = min(m4, w * seg), g_hi = min(m4, g_lo + seg);
+    auto for_seg = [&](auto f) {                           // f(v, x, ok) on whole-wave steps
+        for (int v0 = g_lo; v0 < g_hi; v0 += 64) {
+            const int v = v0 + lane;
+            const float4v x = reinterpret_cast<const float4v*>(row)[min(v, m4 - 1)];
+            f(v, x, v < g_hi);
+        }
+    };
+    for (int j = threadIdx.x; j < kBins; j += 64 * NW) hist[j] = 0;
+    if (threadIdx.x < 8) sw[NW + threadIdx.x] = 0;
+    __syncthreads();
+    bool fast = mx > 0.f;
+    if (fast) {
+        const float scale = static_cast<float>(kBins) / mx;
+        auto bin_of = [&](float v) {
+            return v == 0.f ? 0u : static_cast<unsigned>(min(kBins - 1, static_cast<int>(v * scale)));
+        };
+        unsigned zeros = 0;
+        for_seg([&](int v, const float4v& x, bool ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (!ok || 4 * v + e >= m) continue;
+                if (x[e] == 0.f) ++zeros;
+                else atomicAdd(&hist[bin_of(x[e])], 1u);
+            }
+        });
+        zeros = wave_sum_u(zeros);
+        if (lane == 0 && zeros) atomicAdd(&hist[0], zeros);
+        __syncthreads();
+        if (w == 0) {
+            unsigned above;
+            const unsigned beta = wave_threshold(hist, kBins / 64, KB, &above);
+            if (lane == 0) {
+                sw[NW] = beta;
+                sw[NW + 1] = above;
+                sw[NW + 2] = hist[beta];
+            }
+        }
+        __syncthreads();
+        const unsigned beta = sw[NW], above = sw[NW + 1], cb = sw[NW + 2];
+        fast = cb <= 64;
+        if (fast) {
+            // gather the threshold bin's entries (any order: they are ranked next)
+            for_seg([&](int v, const float4v& x, bool ok) {
+                unsigned inm = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (ok && 4 * v + e < m && bin_of(x[e]) == beta) inm |= 1u << e;
+                const unsigned cnt = __popc(inm);
+                const unsigned tot = wave_sum_u(cnt);
+                if (tot == 0) return;
+                unsigned base = 0;
+                if (lane == 0) base = atomicAdd(&sw[NW + 3], tot);
+                unsigned slot = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(base))) +
+                                wave_prefix_excl(cnt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (inm & (1u << e)) {
+                        sck[slot] = order_key(x[e]);
+                        sci[slot] = 4 * v + e;
+                        ++slot;
+                    }
+            });
+            __syncthreads();
+            if (w == 0) {
+                const unsigned need = KB - above;    // taken from this bin, 1 .. cb
+                unsigned k0 = 0;
+                int i0 = 0;
+                bool hit = false;
+                if (lane < static_cast<int>(cb)) {
+                    k0 = sck[lane];
+                    i0 = sci[lane];
+                    unsigned rank = 0;
+                    for (unsigned c = 0; c < cb; ++c) {
+                        const unsigned k1 = sck[c];
+                        rank += k1 > k0 || (k1 == k0 && sci[c] > i0);
+                    }
+                    hit = rank == need - 1;
+                }
+                const int src = __ffsll(static_cast<long long>(__ballot(hit))) - 1;
+                const unsigned ck = __shfl(k0, src);
+                const int ci = __shfl(i0, src);
+                if (lane == 0) {
+                    sw[NW + 4] = ck;
+                    sw[NW + 5] = static_cast<unsigned>(ci);
+                }
+            }
+        }
+    }
+    if (!fast && w == 0) {
+        unsigned ck;
+        int ci;
+        radix_cut_wave(row, m, KB, hist, ck, ci);
+        if (lane == 0) {
+            sw[NW + 4] = ck;
+            sw[NW + 5] = static_cast<unsigned>(ci);
+        }
+    }
+    __syncthreads();
+    const unsigned ckey = sw[NW + 4];
+    const int cidx = static_cast<int>(sw[NW + 5]);
+    // ordered compaction of the entries with (key, j) >= (ckey, cidx)
+    auto sel = [&](int v, const float4v& x, bool ok) {
+        unsigned sm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * v + e;
+            const unsigned u = order_key(x[e]);
+            if (ok && j < m && (u > ckey || (u == ckey && j >= cidx))) sm |= 1u << e;
+        }
+        return sm;
+    };
+    unsigned mine = 0;
+    for_seg([&](int v, const float4v& x, bool ok) { mine += __popc(sel(v, x, ok)); });
+    mine = wave_sum_u(mine);
+    if (lane == 0) sw[w] = mine;
+    __syncthreads();
+    unsigned base = 0;
+    for (int i = 0; i < w; ++i) base += sw[i];
+    for_seg([&](int v, const float4v& x, bool ok) {
+        const unsigned sm = sel(v, x, ok);
+        const unsigned cnt = __popc(sm);
+        unsigned pos = base + wave_prefix_excl(cnt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (sm & (1u << e)) out[pos++] = 4 * v + e;
+        base += wave_sum_u(cnt);
+    });
+}
 constexpr int kExactWaves = 16;      // waves per workgroup of the exact pass
 constexpr int kExactLds = 24576;     // rows up to this many blocks are scored into LDS
 
@@ -651,6 +792,7 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
     __shared__ unsigned sck[64];
     __shared__ int sci[64];
     __shared__ float smax[kExactWaves];
+    __shared__ unsigned sw[kExactWaves + 8];
     __shared__ __align__(16) float srow[kExactLds];
     for (int t = blockIdx.x; t < total; t += kExactWGs) {
         const long row = queue[t];
@@ -709,12 +851,10 @@ __global__ __launch_bounds__(1024) void qsa_exact_kernel(const void* __restrict_
         // the row is read back by wave 0; the barrier's workgroup-scope ordering
         // covers the scratch row too (all waves of a workgroup share one CU)
         __syncthreads();
-        if (w == 0) {
-            float rmx = 0.f;
+        float rmx = 0.f;
 #pragma unroll
-            for (int j = 0; j < kExactWaves; ++j) rmx = fmaxf(rmx, smax[j]);
-            select_row(sr, m, KB, rmx, idx + row * KB, shist, sck, sci);
-        }
+        for (int j = 0; j < kExactWaves; ++j) rmx = fmaxf(rmx, smax[j]);
+        select_row_wg<kExactWaves>(sr, m, KB, rmx, idx + row * KB, shist, sck, sci, sw);
         __syncthreads();
     }
 }
