@@ -204,14 +204,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
                                                        const float* __restrict__ beta, float* __restrict__ ws_g,
                                                        float* __restrict__ ws_T, float* __restrict__ ws_P,
                                                        float* __restrict__ ws_M, int T, int H, int nch) {
-    constexpr int LDK = DK + 4, LDA = C + 4;
+    constexpr int LDK = DK + 4, LDA = C + 4, LDT = C + 4;
     constexpr int kQA = C * LDK > C * LDA ? C * LDK : C * LDA;
+    constexpr int kKT = C * LDK > C * LDT + 4 * 256 ? C * LDK : C * LDT + 4 * 256;   // K, later T + 4 tiles
     const int c = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const long bhn = static_cast<long>(bh) * nch + c;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
 
-    __shared__ __align__(16) float sK[C * LDK];
+    __shared__ __align__(16) float sK[kKT];
     __shared__ __align__(16) float sQA[kQA];          // Q, then A = diag(beta) M
     __shared__ float sg[C], sb[C];
 
@@ -269,28 +270,66 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution, one column per quad of lanes:
-    // T[t][j] = [t == j] - sum_{i<t} A[t][i] T[i][j]; lane `part` of the quad
-    // keeps the rows i = part (mod 4) of its column in registers.
-    const int j = tid >> 2, part = tid & 3;
-    float tcol[C / 4];
+    // T = (I + A)^-1 in 16x16 blocks, assembled in sK (K is no longer read):
+    // wave w inverts diagonal block w by forward substitution (a quad of lanes
+    // per column, lane & 3 holding the rows i = part (mod 4)), then one block
+    // sub-diagonal per step on MFMA,
+    //     T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
+    // whose terms all lie on earlier sub-diagonals.
+    float* sT = sK;
+    float* sY = sK + C * LDT + 256 * wave;             // this wave's 16x16 scratch tile
+    {
+        const int bd = wave, c = l >> 2, part = l & 3;
+        const float* Ab = sQA + 16 * bd * LDA + 16 * bd;
+        float tc[4] = {0.f, 0.f, 0.f, 0.f};            // rows part, part + 4, ... of column c
 #pragma unroll
-    for (int m = 0; m < C / 4; ++m) tcol[m] = 0.f;
+        for (int t = 0; t < 16; ++t) {
+            float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < C; ++t) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < (t + 3) / 4; ++m) {
-            const int i = 4 * m + part;
-            if (i < t) s += sQA[t * LDA + i] * tcol[m];
+            for (int m = 0; m < 4; ++m) {
+                const int i = 4 * m + part;
+                if (i < t) s += Ab[t * LDA + i] * tc[m];
+            }
+            s = dpp_sum4(s);
+            const float v = (t == c ? 1.f : 0.f) - s;
+            if (part == (t & 3)) tc[t >> 2] = v;
         }
-        s = dpp_sum4(s);
-        const float v = (t == j ? 1.f : 0.f) - s;
-        if (part == (t & 3)) tcol[t >> 2] = v;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sT[(16 * bd + 4 * m + part) * LDT + 16 * bd + c] = tc[m];
     }
+    __syncthreads();
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int lev = 1; lev < 4; ++lev) {
+        if (wave + lev < 4) {
+            const int J = wave, I = J + lev;
+            float4v y = float4v{0.f, 0.f, 0.f, 0.f};
+            const float* Ai = sQA + 16 * I * LDA;
+            const float* Bj = sT + 16 * J;
+            if (lev == 1) y = mma_n<false, true, 16>(Ai, LDA, Bj, LDT, 16 * J, y);
+            else if (lev == 2) y = mma_n<false, true, 32>(Ai, LDA, Bj, LDT, 16 * J, y);
+            else y = mma_n<false, true, 48>(Ai, LDA, Bj, LDT, 16 * J, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sY[(4 * lg + e) * 16 + lr] = y[e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const float4v t =
+                mma_n<false, true, 16>(sT + 16 * I * LDT + 16 * I, LDT, sY, 16, 0, float4v{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * lg + e) * LDT + 16 * J + lr] = -t[e];
+        }
+        __syncthreads();
+    }
+    // T out, zero above the diagonal blocks
     float* gT = ws_T + bhn * C * C;
 #pragma unroll
-    for (int m = 0; m < C / 4; ++m) gT[(4 * m + part) * C + j] = tcol[m];
+    for (int it = 0; it < C * C / 4 / 256; ++it) {
+        const int idx = tid + 256 * it, row = idx / (C / 4), c4 = 4 * (idx % (C / 4));
+        float4v v = *reinterpret_cast<const float4v*>(&sT[row * LDT + c4]);
+        if (c4 / 16 > row / 16) v = float4v{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<float4v*>(&gT[row * C + c4]) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
