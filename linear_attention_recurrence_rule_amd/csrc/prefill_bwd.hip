@@ -103,6 +103,22 @@ __device__ __forceinline__ float dpp_sum4(float x) {          // sum over a quad
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
     return x;
 }
+// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes (zeros shifted in), then the last lane of
+// rows 0 and 2 added into rows 1 and 3, then lane 31 into rows 2 and 3.
+template <int kCtrl, int kRowMask, bool kZeroFill>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, kZeroFill));
+}
+__device__ __forceinline__ float dpp_scan64(float v) {
+    v += dpp_move<0x111, 0xf, true>(v);
+    v += dpp_move<0x112, 0xf, true>(v);
+    v += dpp_move<0x114, 0xf, true>(v);
+    v += dpp_move<0x118, 0xf, true>(v);
+    v += dpp_move<0x142, 0xa, false>(v);
+    v += dpp_move<0x143, 0xc, false>(v);
+    return v;
+}
 __device__ __forceinline__ float dpp_sum8(float x) {          // sum over 8 consecutive lanes
     x = dpp_sum4(x);
     return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
@@ -227,12 +243,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
         const int tg = c * C + l;
         const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
         const float a = alpha[gi], be = beta[gi];
-        float x = tg < T ? fmaxf(__logf(a), kLogFloor) : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {             // inclusive prefix sum over the chunk
-            const float y = __shfl_up(x, off);
-            if (l >= off) x += y;
-        }
+        const float x = dpp_scan64(tg < T ? fmaxf(__logf(a), kLogFloor) : 0.f);   // prefix sum over the chunk
         sg[l] = x;
         sb[l] = tg < T ? be : 0.f;
         ws_g[bhn * C + l] = x;
@@ -849,17 +860,11 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         const float dlam = sKX3[t];
         const float db = sDRv[t] - gam * sKX2[t] + sRowAM[t];
         float dg = gam * dgam + sRowPP[t] - sColPP[t] + sRowAA[t] - sColAA[t] - lam * dlam;
-        float tot = lam * dlam;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+        const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpp_scan64(lam * dlam)), 63));
         if (t == C - 1) dg += tot + gam * sSdS;
-        // reverse inclusive scan: dl_s = sum_{t >= s} dg_t
-        float x = dg;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(x, off);
-            if (t + off < 64) x += y;
-        }
+        // reverse inclusive scan dl_s = sum_{t >= s} dg_t: a prefix scan of the
+        // lane-reversed values, reversed back
+        const float x = __shfl(dpp_scan64(__shfl(dg, C - 1 - t)), C - 1 - t);
         if (tg < T) {
             const long gi = (static_cast<long>(b) * T + tg) * H + h;
             dbeta[gi] = db;
