@@ -3,9 +3,13 @@
 // mixer output, per (token, head) row of d_v values:
 //     out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w)
 // A pure stream (read y and z, write out once), bound by HBM bandwidth.
-// Each row is handled by d_v/4 lanes holding one float4 each; the row's sum of
-// squares is reduced with cross-lane shuffles, so no LDS is used.  A thread
-// covers kNormPasses rows and loads all of them before reducing any.
+// Each row is handled by d_v/8 lanes holding 8 values each (two 16-byte y
+// loads, one 16-byte z load and one 16-byte store for bf16); the row's sum of
+// squares is reduced with DPP lane moves inside the lane group, so no LDS is
+// used.  A thread covers kNormPasses rows and loads all of them before
+// reducing any.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -13,74 +17,102 @@ namespace gdn {
 
 constexpr int kNormPasses = 2;   // rows per thread, loaded before any is reduced
 
+// Sum over aligned groups of L lanes (L = 2, 4, 8, 16), every lane getting
+// the group's sum: quad swaps, then the half-row and row mirrors.
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    auto mv = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    x += mv(x, std::integral_constant<int, 0xB1>{});           // quad_perm [1, 0, 3, 2]
+    if constexpr (L >= 4) x += mv(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+    if constexpr (L >= 8) x += mv(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    if constexpr (L >= 16) x += mv(x, std::integral_constant<int, 0x140>{});  // row_mirror
+    return x;
+}
+
 template <int DV, bool kBf16>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restrict__ y,
                                                             const void* __restrict__ z,
                                                             const float* __restrict__ weight, float eps,
                                                             void* __restrict__ out, long rows) {
-    constexpr int kLanesPerRow = DV / 4;
+    constexpr int kLanesPerRow = DV / 8;
     constexpr int kRowsPerPass = 256 / kLanesPerRow;
+    static_assert(kLanesPerRow >= 2 && kLanesPerRow <= 16, "d_v in 16 .. 128");
     const int tid = threadIdx.x;
     const int sub = tid % kLanesPerRow;
     const long row0 = static_cast<long>(blockIdx.x) * kRowsPerPass * kNormPasses + tid / kLanesPerRow;
 
     // all loads first, so that each thread has several requests in flight
-    float4 yv[kNormPasses];
-    float zv[kNormPasses][4];
+    float yv[kNormPasses][8];
+    float zv[kNormPasses][8];
 #pragma unroll
     for (int p = 0; p < kNormPasses; ++p) {
         const long row = row0 + p * kRowsPerPass;
-        const long base = (row < rows ? row : rows - 1) * DV + sub * 4;   // clamped; not stored
-        yv[p] = *reinterpret_cast<const float4*>(y + base);
+        const long base = (row < rows ? row : rows - 1) * DV + sub * 8;   // clamped; not stored
+        const float4 y0 = *reinterpret_cast<const float4*>(y + base);
+        const float4 y1 = *reinterpret_cast<const float4*>(y + base + 4);
+        yv[p][0] = y0.x; yv[p][1] = y0.y; yv[p][2] = y0.z; yv[p][3] = y0.w;
+        yv[p][4] = y1.x; yv[p][5] = y1.y; yv[p][6] = y1.z; yv[p][7] = y1.w;
         if constexpr (kBf16) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(z) + base);
-            zv[p][0] = bf16_to_f32(static_cast<uint16_t>(raw.x & 0xffffu));
-            zv[p][1] = bf16_to_f32(static_cast<uint16_t>(raw.x >> 16));
-            zv[p][2] = bf16_to_f32(static_cast<uint16_t>(raw.y & 0xffffu));
-            zv[p][3] = bf16_to_f32(static_cast<uint16_t>(raw.y >> 16));
+            const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(z) + base);
+            const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                zv[p][2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xffffu));
+                zv[p][2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
+            }
         } else {
-            const float4 zz = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base);
-            zv[p][0] = zz.x; zv[p][1] = zz.y; zv[p][2] = zz.z; zv[p][3] = zz.w;
+            const float4 z0 = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base);
+            const float4 z1 = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base + 4);
+            zv[p][0] = z0.x; zv[p][1] = z0.y; zv[p][2] = z0.z; zv[p][3] = z0.w;
+            zv[p][4] = z1.x; zv[p][5] = z1.y; zv[p][6] = z1.z; zv[p][7] = z1.w;
         }
     }
-    float w[4] = {0.f, 0.f, 0.f, 0.f};
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0.f;
     if (weight) {
-        const float4 ww = reinterpret_cast<const float4*>(weight)[sub];
-        w[0] = ww.x; w[1] = ww.y; w[2] = ww.z; w[3] = ww.w;
+        const float4 w0 = reinterpret_cast<const float4*>(weight)[2 * sub];
+        const float4 w1 = reinterpret_cast<const float4*>(weight)[2 * sub + 1];
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
     }
 #pragma unroll
     for (int p = 0; p < kNormPasses; ++p) {
         const long row = row0 + p * kRowsPerPass;
-        float ss = yv[p].x * yv[p].x + yv[p].y * yv[p].y + yv[p].z * yv[p].z + yv[p].w * yv[p].w;
+        float ss = 0.f;
 #pragma unroll
-        for (int off = 1; off < kLanesPerRow; off <<= 1) ss += __shfl_xor(ss, off);
+        for (int i = 0; i < 8; ++i) ss += yv[p][i] * yv[p][i];
+        ss = group_sum<kLanesPerRow>(ss);
         if (row >= rows) continue;
         // hardware reciprocal square root and reciprocal (about 1 ulp each)
         const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + eps);
-        const float yy[4] = {yv[p].x, yv[p].y, yv[p].z, yv[p].w};
-        float o[4];
+        float o[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const float gate = __builtin_amdgcn_rcpf(1.0f + __expf(-zv[p][i]));
-            o[i] = gate * (yy[i] * inv) * (1.0f + w[i]);
+            o[i] = gate * (yv[p][i] * inv) * (1.0f + w[i]);
         }
-        const long base = row * DV + sub * 4;
+        const long base = row * DV + sub * 8;
         // streaming stores: the output is not read again here
         if constexpr (kBf16) {
-            const uint32_t lo = pack_bf16x2(o[0], o[1]);
-            const uint32_t hi = pack_bf16x2(o[2], o[3]);
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base));
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                              pack_bf16x2(o[6], o[7])},
+                                        reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + base));
         } else {
             __builtin_nontemporal_store(float4v{o[0], o[1], o[2], o[3]},
                                         reinterpret_cast<float4v*>(static_cast<float*>(out) + base));
+            __builtin_nontemporal_store(float4v{o[4], o[5], o[6], o[7]},
+                                        reinterpret_cast<float4v*>(static_cast<float*>(out) + base + 4));
         }
     }
 }
 
 template <int DV, bool kBf16>
 static hipError_t launch_norm_t(const NormArgs& a) {
-    constexpr int kRowsPerBlock = 256 / (DV / 4) * kNormPasses;
+    constexpr int kRowsPerBlock = 256 / (DV / 8) * kNormPasses;
     const long blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL((gated_rmsnorm_kernel<DV, kBf16>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        0, a.stream, a.y, a.z, a.weight, a.eps, a.out, a.rows);
