@@ -234,7 +234,7 @@ __device__ __forceinline__ unsigned bin_top(int b, int lo) {
 constexpr int kSampleFrom = 16;      // tiles below which the histogram pass reads every tile
 constexpr int kCapB = 1024;          // candidates a query can rank in the merge
 constexpr int kSlots = kCapB / 64;
-constexpr int kMapWords = 512;       // merge: output bitmap chunk (32768 blocks)
+constexpr int kMapWords = 256;       // merge: output bitmap chunk (16384 blocks)
 __device__ __forceinline__ int sampled_tile(int j) { return 8 * j + ((5 * j) & 7); }
 
 // ---------------------------------------------------------------------------
@@ -442,11 +442,11 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
 // (LDS) and held in registers (slot t of lane l: candidate 64 t + l); the
 // need = K_B - (outright count) largest bit patterns are found by bisection,
 // and among the ties at the cut the later blocks (bisection on the index).
-// The taken blocks are marked in an LDS bitmap, 32768 blocks at a time, and
+// The taken blocks are marked in an LDS bitmap, 16384 blocks at a time, and
 // written out in ascending order.  A band that missed (need outside
 // [1, candidates]) or an overflowing sub-list queues the query.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict__ info, const int* __restrict__ cnt,
+__global__ __launch_bounds__(256, 4) void qsa_merge_kernel(const uint2* __restrict__ info, const int* __restrict__ cnt,
                                                         const uint2* __restrict__ list, int* __restrict__ idx,
                                                         int* __restrict__ queue, int* __restrict__ qcount, int n,
                                                         int r, int KB, int cap) {
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(256) void qsa_merge_kernel(const uint2* __restrict_
     const unsigned thi = info[row].y;
     // lane l reads sub-list l % 16, entry pairs l / 16 + 4 t (16 bytes each):
     // 2 kBatch entries per lane in flight
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 8;
     const int sl = lane & 15;
     const int len = cnt[row * 16 + sl];
     const bool over = __ballot(len > cap) != 0ull;

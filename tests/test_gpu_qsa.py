@@ -145,6 +145,19 @@ def test_select_long_context_sampled_rows():
     _check_rows(idx[0], d["q"][0], d["kbar"][0], rows, r, K // r, "sampled")
 
 
+def test_select_rows_longer_than_one_bitmap_chunk():
+    """40000 tokens at r = 2 (20000 blocks): the latest rows have more
+    candidate blocks than one 16384-block bitmap chunk of the merge, so their
+    ascending output is assembled chunk by chunk."""
+    say("qsa select n=40000 r=2")
+    n, r, K = 40000, 2, 1024
+    d = qsa_select_inputs(1, n, r, 4, 128, "bf16", seed=31)
+    idx = host(gdn.gdn_qsa_select(dev(d["q"], "bf16"), dev(d["kbar"], "bf16"), r=r, K=K)).astype(np.int64)
+    rng = np.random.default_rng(32)
+    rows = sorted(set(rng.integers(2 * 16384, n, 16).tolist()) | {2 * 16384 - 1, 2 * 16384, n - 2, n - 1})
+    _check_rows(idx[0], d["q"][0], d["kbar"][0], rows, r, K // r, "beyond one chunk")
+
+
 @pytest.mark.parametrize("H", [1, 3])
 def test_select_other_head_counts(H):
     """Head counts other than four take the stored-score path."""
