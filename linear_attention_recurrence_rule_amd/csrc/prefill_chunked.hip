@@ -124,8 +124,9 @@ __device__ __forceinline__ half8 ld_split_tr(const _Float16* base, int m0, int k
 // chunk.  Every product runs from registers, so the waves never wait for one
 // another:
 //   * the Gram tiles K_J K_I^T come from bf16 MFMAs on k fragments loaded
-//     straight from HBM (each lane: 16 rows x 8 columns per 32-wide step; the
-//     same fragment serves as the A operand of one tile and the B operand of
+//     straight from HBM (lane (r + 16 g) of the fragment of token block I
+//     holds row 16 I + r, columns 8 g .. + 8 of each 32-wide step; the same
+//     fragment serves as the A operand of one tile and the B operand of
 //     another);
 //   * each lane then holds 4 consecutive columns of one row of A, which is
 //     exactly the A operand of a 16x16x16 MFMA, so A's sub-diagonal blocks stay
@@ -136,9 +137,9 @@ __device__ __forceinline__ half8 ld_split_tr(const _Float16* base, int m0, int k
 //     (the column scaling by beta commutes with the sum, so T' is built
 //     directly), whose accumulator layout is again the B operand of the next
 //     step.
-// The k fragments of the wave's next chunk are loaded as soon as the Gram
-// tiles no longer need them.  Per-wave LDS only stages the diagonal blocks and
-// the output.
+// The k fragments of the wave's next chunk reuse the registers of the
+// current one once its Gram tiles are formed.  Per-wave LDS only stages the
+// diagonal blocks and the output.
 // ===========================================================================
 constexpr int kPrepWaves = 4;        // waves (chunks in flight) per workgroup
 constexpr int kPrepResidentWGs = 768; // three workgroups per CU
@@ -287,7 +288,10 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
                     const int t = grp * 5 + u, I = lower_block_row(t), J = t - I * (I + 1) / 2;
                     acc[u] = mma_gram(kf[J][kk], kf[I][kk], acc[u]);
                 }
-            // the fragments are dead after the second group: the next chunk's loads fly from here on
+            // The fragments are dead after the second group, so the next
+            // chunk's loads may go out from here on.  (The compiler moves
+            // them to the loop's back edge; forcing them here, unconditional
+            // and behind a scheduling barrier, measured no faster.)
             if (grp == 1 && j + 1 < cpw && chunk_of(j + 1) < nchunks) load(chunk_of(j + 1));
 #pragma unroll
             for (int u = 0; u < 5; ++u) {
