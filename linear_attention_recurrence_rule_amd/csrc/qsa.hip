@@ -15,7 +15,7 @@
 // rotate-half pairs (j, j + rope_dims/2) by pos * base^(-2 j / rope_dims).
 //
 // Kernels:
-//   qsa_prep_kernel   one wave per row (a query head or a pooled key), two
+//   qsa_prep_kernel   eight rows per wave (query heads or pooled keys), two
 //                     dimensions per lane; the rotation angle is formed and
 //                     reduced modulo 2 pi in double precision, so that long
 //                     positions keep their phase.
@@ -27,6 +27,8 @@
 //                     per head, summed, written for complete blocks only.
 //   qsa_select_kernel one wave per query on the stored scores: select_row
 //                     (qsa_wave.hpp).
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 #include "qsa_wave.hpp"
@@ -37,9 +39,28 @@ namespace qsa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
-// prep: grid (rows / 4), 256 threads, one wave per row.  Rows [0, B n H) are
-// query heads, rows [B n H, B n H + B nb) pooled keys.
+// prep: grid (rows / (4 kPrepRows)), 256 threads; each wave takes kPrepRows
+// consecutive rows.  Rows [0, B n H) are query heads, rows [B n H, B n H +
+// B nb) pooled keys.  A lane's rotary frequencies (double precision, one
+// exp2 per dimension) are formed once and serve all of the wave's rows.
 // ---------------------------------------------------------------------------
+constexpr int kPrepRows = 8;
+
+// Sum over the wave with DPP lane moves (row shifts, then the row broadcasts
+// of lanes 15 and 31), read from lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    auto mv = [](float x, auto ctrl, auto rmask, auto bc) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                          decltype(rmask)::value, 0xf, decltype(bc)::value));
+    };
+    v += mv(v, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{}, std::true_type{});
+    v += mv(v, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{}, std::true_type{});
+    v += mv(v, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{}, std::true_type{});
+    v += mv(v, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{}, std::true_type{});
+    v += mv(v, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{}, std::false_type{});
+    v += mv(v, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{}, std::false_type{});
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 template <bool kBf16>
 __device__ __forceinline__ void store_out(void* p, long i, float x) {
     if constexpr (kBf16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
@@ -53,69 +74,81 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(const void* __restrict__ 
                                                        void* __restrict__ kbar_out, int B, int n, int H, int D, int r,
                                                        int rope_dims, double log2_base, float eps) {
     const int lane = threadIdx.x & 63;
-    const long row = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const long row0 = (static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRows;
     const long nq = static_cast<long>(B) * n * H;
     const int nb = n / r;
     const long nk = static_cast<long>(B) * nb;
-    if (row >= nq + nk) return;                      // whole waves drop out together
-    const bool is_q = row < nq;
-    float x[2];
-    long pos;
-    const float* w = is_q ? q_weight : k_weight;
-    if (is_q) {
-        pos = (row / H) % n;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int d = lane + 64 * e;
-            x[e] = d < D ? load_in<kBf16>(q_proj, row * D + d) : 0.f;
-        }
-    } else {
-        const long kr = row - nq, b = kr / nb, blk = kr - b * nb;
-        pos = blk * r;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int d = lane + 64 * e;
-            float s = 0.f;
-            if (d < D)
-                for (int j = 0; j < r; ++j) s += load_in<kBf16>(k_proj, (b * n + blk * r + j) * D + d);
-            x[e] = s / static_cast<float>(r);
-        }
-    }
-    // RMSNorm
-    const float ss = wave_sum(x[0] * x[0] + x[1] * x[1]);
-    const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + eps);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int d = lane + 64 * e;
-        x[e] *= inv;
-        if (w && d < D) x[e] *= w[d];
-    }
-    // partial rotary embedding: dimension d < rope_dims pairs with d +- half
+    // this lane's dimensions d = lane + 64 e, their rotary partners and frequencies
     const int half = rope_dims / 2;
-    float y[2];
+    int pl[2], pe[2];
+    double freq[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int d = lane + 64 * e;
         // the partner value lives in lane (d +- half) mod 64, slot (d +- half) / 64
         const int pd = d < half ? d + half : d - half;
-        const int pl = (pd >= 0 ? pd : 0) & 63, pe = (pd >= 0 ? pd : 0) >> 6;
-        const float p0 = __shfl(x[0], pl), p1 = __shfl(x[1], pl);
-        const float partner = pe ? p1 : p0;
-        y[e] = x[e];
-        if (d < rope_dims) {
-            const int j = d < half ? d : d - half;
-            const double ang = static_cast<double>(pos) * exp2(-2.0 * j / rope_dims * log2_base);
-            const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
-            const float c = cosf(static_cast<float>(red)), s = sinf(static_cast<float>(red));
-            y[e] = d < half ? x[e] * c - partner * s : x[e] * c + partner * s;
-        }
+        pl[e] = (pd >= 0 ? pd : 0) & 63;
+        pe[e] = (pd >= 0 ? pd : 0) >> 6;
+        const int j = d < half ? d : d - half;
+        freq[e] = d < rope_dims ? exp2(-2.0 * j / rope_dims * log2_base) : 0.0;
     }
-    void* out = is_q ? q_out : kbar_out;
-    const long base = (is_q ? row : row - nq) * D;
+    for (int i = 0; i < kPrepRows; ++i) {
+        const long row = row0 + i;
+        if (row >= nq + nk) return;                  // whole waves drop out together
+        const bool is_q = row < nq;
+        float x[2];
+        long pos;
+        const float* w = is_q ? q_weight : k_weight;
+        if (is_q) {
+            pos = (row / H) % n;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int d = lane + 64 * e;
-        if (d < D) store_out<kBf16>(out, base + d, y[e]);
+            for (int e = 0; e < 2; ++e) {
+                const int d = lane + 64 * e;
+                x[e] = d < D ? load_in<kBf16>(q_proj, row * D + d) : 0.f;
+            }
+        } else {
+            const long kr = row - nq, b = kr / nb, blk = kr - b * nb;
+            pos = blk * r;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int d = lane + 64 * e;
+                float s = 0.f;
+                if (d < D)
+                    for (int j = 0; j < r; ++j) s += load_in<kBf16>(k_proj, (b * n + blk * r + j) * D + d);
+                x[e] = s / static_cast<float>(r);
+            }
+        }
+        // RMSNorm
+        const float ss = wave_sum_dpp(x[0] * x[0] + x[1] * x[1]);
+        const float inv = 1.f / sqrtf(ss / static_cast<float>(D) + eps);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d = lane + 64 * e;
+            x[e] *= inv;
+            if (w && d < D) x[e] *= w[d];
+        }
+        // partial rotary embedding: dimension d < rope_dims pairs with d +- half
+        float y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d = lane + 64 * e;
+            const float p0 = __shfl(x[0], pl[e]), p1 = __shfl(x[1], pl[e]);
+            const float partner = pe[e] ? p1 : p0;
+            y[e] = x[e];
+            if (d < rope_dims) {
+                const double ang = static_cast<double>(pos) * freq[e];
+                const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
+                const float c = cosf(static_cast<float>(red)), s = sinf(static_cast<float>(red));
+                y[e] = d < half ? x[e] * c - partner * s : x[e] * c + partner * s;
+            }
+        }
+        void* out = is_q ? q_out : kbar_out;
+        const long base = (is_q ? row : row - nq) * D;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d = lane + 64 * e;
+            if (d < D) store_out<kBf16>(out, base + d, y[e]);
+        }
     }
 }
 
@@ -231,7 +264,7 @@ size_t qsa_select_workspace_bytes(int B, int n, int H, int r, int KB) {
 template <bool kBf16>
 static hipError_t launch_qsa_prep_t(const QsaPrepArgs& a) {
     const long rows = static_cast<long>(a.B) * a.n * a.H + static_cast<long>(a.B) * (a.n / a.r);
-    hipLaunchKernelGGL((qsa::qsa_prep_kernel<kBf16>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL((qsa::qsa_prep_kernel<kBf16>), dim3(static_cast<unsigned>((rows + 4 * qsa::kPrepRows - 1) / (4 * qsa::kPrepRows))), dim3(256), 0,
                        a.stream, a.q_proj, a.k_proj, a.q_weight, a.k_weight, a.q_out, a.kbar_out, a.B, a.n, a.H, a.D,
                        a.r, a.rope_dims, std::log2(static_cast<double>(a.rope_base)), a.eps);
     return hipGetLastError();
