@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(const void* __restrict__ 
             if (d < rope_dims) {
                 const double ang = static_cast<double>(pos) * freq[e];
                 const double red = ang - 6.283185307179586 * floor(ang * 0.15915494309189535);
-                const float c = cosf(static_cast<float>(red)), s = sinf(static_cast<float>(red));
+                float s, c;
+                sincosf(static_cast<float>(red), &s, &c);
                 y[e] = d < half ? x[e] * c - partner * s : x[e] * c + partner * s;
             }
         }
