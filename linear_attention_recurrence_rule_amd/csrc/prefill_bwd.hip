@@ -29,6 +29,8 @@
 //          dalpha_s = (sum_{t >= s} dg_t) / alpha_s.
 // Every contraction is an fp32 MFMA (16x16x4) on LDS tiles; the workspace
 // holds the per-chunk matrices and states in fp32.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -118,6 +120,18 @@ __device__ __forceinline__ float dpp_scan64(float v) {
     v += dpp_move<0x142, 0xa, false>(v);
     v += dpp_move<0x143, 0xc, false>(v);
     return v;
+}
+// bf16 MFMA on fragments (exact products, fp32 sums): 16x16x32 on 8-element
+// fragments, 16x16x16 on 4-element ones.
+__device__ __forceinline__ float4v mma_bf16(uint4 a, uint4 b, float4v c) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ float4v mma_bf16(uint2 a, uint2 b, float4v c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                    0, 0, 0);
 }
 __device__ __forceinline__ float dpp_sum8(float x) {          // sum over 8 consecutive lanes
     x = dpp_sum4(x);
@@ -221,8 +235,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
                                                        float* __restrict__ ws_T, float* __restrict__ ws_P,
                                                        float* __restrict__ ws_M, int T, int H, int nch) {
     constexpr int LDK = DK + 4, LDA = C + 4, LDT = C + 4;
-    constexpr int kQA = C * LDK > C * LDA ? C * LDK : C * LDA;
-    constexpr int kKT = C * LDK > C * LDT + 4 * 256 ? C * LDK : C * LDT + 4 * 256;   // K, later T + 4 tiles
+    // bf16 inputs go straight from HBM into MFMA fragments, so LDS holds only A and T
+    constexpr int kQA = !kBf16 && C * LDK > C * LDA ? C * LDK : C * LDA;
+    constexpr int kKT = !kBf16 && C * LDK > C * LDT + 4 * 256 ? C * LDK : C * LDT + 4 * 256;   // K, later T + 4 tiles
     const int c = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const long bhn = static_cast<long>(bh) * nch + c;
@@ -232,7 +247,35 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
     __shared__ __align__(16) float sQA[kQA];          // Q, then A = diag(beta) M
     __shared__ float sg[C], sb[C];
 
-    {
+    // bf16: lane (r + 16 g) of fragment [I][s] holds row 16 I + r, columns
+    // 32 s + 8 g .. + 8 (4-column fragments at d_k = 16); rows past T are zero.
+    using Frag = typename std::conditional<(DK >= 32), uint4, uint2>::type;
+    constexpr int KS = DK >= 32 ? DK / 32 : 1, FW = DK >= 32 ? 8 : 4;
+    // (wave w's own block, the A operand of its four tiles, is loaded apart so
+    // that no fragment array is indexed by the wave number)
+    Frag kf[kBf16 ? 4 : 1][KS], ka[KS], qf[KS];
+    if constexpr (kBf16) {
+        const int lr = l & 15, lg = l >> 4;
+        auto at = [&](int I) {
+            const int tg = c * C + 16 * I + lr;
+            return ((static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h) * DK + FW * lg;
+        };
+        auto live = [&](int I) { return c * C + 16 * I + lr < T; };
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const Frag kv = *reinterpret_cast<const Frag*>(static_cast<const uint16_t*>(k) + at(I) + 32 * st);
+                kf[I][st] = live(I) ? kv : Frag{};
+            }
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const Frag kv = *reinterpret_cast<const Frag*>(static_cast<const uint16_t*>(k) + at(wave) + 32 * st);
+            const Frag qv = *reinterpret_cast<const Frag*>(static_cast<const uint16_t*>(q) + at(wave) + 32 * st);
+            ka[st] = live(wave) ? kv : Frag{};
+            qf[st] = live(wave) ? qv : Frag{};
+        }
+    } else {
         RowTile<DK, 256, kBf16> tq, tk;
         tq.load(q, b, c, T, H, h);
         tk.load(k, b, c, T, H, h);
@@ -257,8 +300,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
         const int p = wave * 4 + u, ti = p >> 2, tj = p & 3;
         kk[u] = qk[u] = float4v{0.f, 0.f, 0.f, 0.f};
         if (tj <= ti) {
-            kk[u] = mma_n<false, false, DK>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, kk[u]);
-            qk[u] = mma_n<false, false, DK>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, qk[u]);
+            if constexpr (kBf16) {
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    kk[u] = mma_bf16(ka[st], kf[u][st], kk[u]);
+                    qk[u] = mma_bf16(qf[st], kf[u][st], qk[u]);
+                }
+            } else {
+                kk[u] = mma_n<false, false, DK>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, kk[u]);
+                qk[u] = mma_n<false, false, DK>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, qk[u]);
+            }
         }
     }
     __syncthreads();                                   // Q is no longer read: its space takes A
