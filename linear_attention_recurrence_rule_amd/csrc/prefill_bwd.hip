@@ -27,8 +27,10 @@
 //          dg_t = gamma_t (scale q_t.X1_t - beta_t k_t.X2_t) + rows/cols of dP o P
 //                 and dA o A - lam_t k_t.X3_t  (+ the chunk-end terms at t = n)
 //          dalpha_s = (sum_{t >= s} dg_t) / alpha_s.
-// Every contraction is an fp32 MFMA (16x16x4) on LDS tiles; the workspace
-// holds the per-chunk matrices and states in fp32.
+// Every contraction is an fp32 MFMA (16x16x4) on LDS tiles, except the
+// prep pass's Gram tiles of bf16 inputs, which are bf16 MFMAs (exact products,
+// fp32 sums) on fragments loaded straight from HBM; the workspace holds the
+// per-chunk matrices and states in fp32.
 #include <type_traits>
 
 #include "gdn_device.hpp"
