@@ -44,11 +44,19 @@ def prefill_bytes(B, T, H, dk, dv, in_bytes=2, with_final_state=True, with_initi
 
 
 def prefill_flops(B, T, H, dk, dv, C=64):
-    """Dense MFMA tile work per token-head of the chunked form (a chunk of C
-    tokens: K K^T, Q K^T, the (C x C)(C x d_v) products T R and P E, and the
-    three state products K S, Q S and K^T E; the diagonal-block inverse is
-    left out)."""
+    """Dense MFMA tile work per token-head of the chunked form as the kernels
+    evaluate it (a chunk of C tokens: K K^T, Q K^T, the (C x C)(C x d_v)
+    products T' R and P E, and the three state products K S, Q S and K^T E;
+    the diagonal-block inverse is left out): 6 d^2 + 8 C d at d_k = d_v = d.
+    The misses E = T'(V - diag(gamma) K S) take one C x C product where the
+    unfolded WY form, W = T diag(beta gamma) K and U = T diag(beta) V followed
+    by U - W S, takes two, hence prefill_flops_unfolded's 6 d^2 + 10 C d."""
     return B * T * H * (2 * 2 * C * dk + 2 * 2 * C * dv + 3 * 2 * dk * dv)
+
+
+def prefill_flops_unfolded(B, T, H, dk, dv, C=64):
+    """The same count with separate W and U products (one more C x C x d_k)."""
+    return prefill_flops(B, T, H, dk, dv, C) + B * T * H * 2 * 2 * C * dk
 
 
 def bwd_bytes(B, T, H, dk, dv, in_bytes=2):
@@ -97,6 +105,63 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_call"])
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+_POOL_DATA = {}
+
+
+def _oracle_heads(h0, h1):
+    """Worker of the pooled CPU baseline: the oracle over heads h0 .. h1-1 of
+    the sample in _POOL_DATA (inherited through fork), one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import gated_delta_recurrence
+    d = _POOL_DATA
+    sl = (slice(None), slice(None), slice(h0, h1))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        gated_delta_recurrence(d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl], d["beta"][sl])
+        return time.perf_counter() - t0
+
+
+def cpu_oracle_baseline(sample, H, Ts, max_workers=16):
+    """Time the float64 oracle on `sample` (B=1, Ts tokens, H heads): once on
+    one core, then as a process pool over heads on the cores this process may
+    use (at most max_workers).  Returns the cpu_baseline object."""
+    import concurrent.futures
+    import multiprocessing
+    from threadpoolctl import threadpool_limits
+    from oracle import gated_delta_recurrence
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        gated_delta_recurrence(sample["q"], sample["k"], sample["v"], sample["alpha"], sample["beta"])
+        t_one = time.perf_counter() - t0
+    cores = max(1, min(max_workers, len(os.sched_getaffinity(0)), H))
+    _POOL_DATA.clear()
+    _POOL_DATA.update(sample)
+    bounds = [(H * i // cores, H * (i + 1) // cores) for i in range(cores)]
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        list(ex.map(_oracle_heads, *zip(*bounds)))
+    t_pool = time.perf_counter() - t0
+    _POOL_DATA.clear()
+    model = cpu_model()
+    return {"value": Ts / t_pool, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "single_core_value": Ts / t_one,
+            "sample": f"float64 numpy oracle over the first {Ts} tokens of the long-prefill workload shape "
+                      f"(B=1, H={H}, d=128): {t_one:.1f} s on 1 core; {t_pool:.1f} s as a pool of {cores} "
+                      f"processes over heads (pool start-up included); CPU: {model}"}
+
+
 def calibrate_copy(nbytes=1 << 30, reps=4):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -106,6 +171,82 @@ def calibrate_copy(nbytes=1 << 30, reps=4):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
+
+
+def _time_calls(fn, reps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_prefill_short(dev, stream, to_dev, reps=20):
+    """B=4, H=16, T=4096 prefill (one call, zero initial state, final state out)."""
+    import torch
+    import linear_attention_recurrence_rule_amd as gdn
+    from workloads import CONFIGS, config_prefill_inputs
+    c = CONFIGS[1]
+    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
+    log(f"prefill short: B={B} T={T} H={H}")
+    d = config_prefill_inputs(1)
+    q, k, v = (to_dev(d[n], True) for n in ("q", "k", "v"))
+    alpha, beta = to_dev(d["alpha"], False), to_dev(d["beta"], False)
+    y = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, H, dk, dv, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    ms = _time_calls(lambda: gdn.gdn_prefill_fwd(q, k, v, alpha, beta, None, S, y, workspace=ws, stream=stream),
+                     reps, 3, stream)
+    nb = prefill_bytes(B, T, H, dk, dv)
+    gbps = nb / (ms * 1e-3) / 1e9
+    log(f"prefill short {ms * 1e3:.1f} us, {gbps:.0f} GB/s")
+    return {"workload": f"GDN prefill, B={B} T={T} H={H} d={dk}, bf16 q/k/v, fp32 state and y",
+            "avg_call_ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes_per_call": nb,
+            "achieved": gbps, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+            "mfma_frac_of_bf16_peak": prefill_flops(B, T, H, dk, dv) / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+
+
+def bench_prefill_segmented(dev, stream, to_dev, reps=3, distinct=8):
+    """B=1, H=16, T=262144 as 64 calls of 4096 tokens carrying the state through
+    initial_state/final_state (in place).  The first `distinct` 4096-token
+    segments of the workload are resident and cycled over the 64 calls."""
+    import torch
+    import linear_attention_recurrence_rule_amd as gdn
+    from workloads import CONFIGS, config_prefill_inputs
+    c = CONFIGS[4]
+    T, H, dk, dv, seg = c["T"], c["H"], c["dk"], c["dv"], c["segment"]
+    nseg = T // seg
+    log(f"prefill 262K: H={H}, {nseg} segments of {seg}")
+    segs = []
+    for s in range(distinct):
+        d = config_prefill_inputs(4, T=seg, t_begin=s * seg)
+        segs.append(tuple(to_dev(d[n], True) for n in ("q", "k", "v"))
+                    + (to_dev(d["alpha"], False), to_dev(d["beta"], False)))
+    y = torch.empty((1, seg, H, dv), dtype=torch.float32, device=dev)
+    S = torch.zeros((1, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(1, seg, H, dk, dv, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+
+    def sequence():
+        for i in range(nseg):
+            q, k, v, a, b = segs[i % distinct]
+            gdn.gdn_prefill_fwd(q, k, v, a, b, S, S, y, workspace=ws, stream=stream)
+    ms = _time_calls(sequence, reps, 1, stream)
+    nb = nseg * prefill_bytes(1, seg, H, dk, dv, with_initial_state=True)
+    gbps = nb / (ms * 1e-3) / 1e9
+    log(f"prefill 262K segmented {ms:.3f} ms, {gbps:.0f} GB/s")
+    return {"workload": f"GDN prefill, one {T}-token sequence, H={H} d={dk}, as {nseg} calls of {seg} tokens "
+                        "carrying the state", "avg_sequence_ms": ms, "avg_call_ms": ms / nseg,
+            "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb, "achieved": gbps, "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "mfma_frac_of_bf16_peak": prefill_flops(1, T, H, dk, dv) / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
 
 
 def main():
@@ -120,6 +261,8 @@ def main():
     ap.add_argument("--no-mtp", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-qsa", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the 4K-token and 262K-token segmented prefill workloads")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -134,10 +277,24 @@ def main():
         calibrate_copy()
         return
 
-    import torch
-    import linear_attention_recurrence_rule_amd as gdn
     from workloads import (CONFIGS, config_prefill_inputs, decode_initial_state, decode_step_inputs,
                            mtp_draft_inputs)
+
+    # ---------------- float64 CPU oracle on a bounded sample ----------------
+    # (first, before anything touches the GPU, so that the worker processes are
+    # forked from a process without a GPU context)
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        Ts, Hs = args.cpu_tokens, CONFIGS[2]["H"]
+        log(f"cpu oracle: B=1 H={Hs} T={Ts} (one core, then a pool over heads)")
+        ds = config_prefill_inputs(2, T=Ts)
+        cpu_baseline = cpu_oracle_baseline(ds, Hs, Ts)
+        del ds
+        log(f"cpu oracle {cpu_baseline['single_core_value']:.1f} tokens/s on one core, "
+            f"{cpu_baseline['value']:.1f} tokens/s on {cpu_baseline['cores']} cores")
+
+    import torch
+    import linear_attention_recurrence_rule_amd as gdn
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -196,6 +353,7 @@ def main():
     pf_bytes = prefill_bytes(B, T, H, dk, dv)
     pf_gbps = pf_bytes / (prefill_ms * 1e-3) / 1e9
     pf_tflops = prefill_flops(B, T, H, dk, dv) / (prefill_ms * 1e-3) / 1e12
+    pf_tflops_unf = prefill_flops_unfolded(B, T, H, dk, dv) / (prefill_ms * 1e-3) / 1e12
     nb = norm_bytes(B * T * H, dv)
     log(f"step {ms_step:.3f} ms; prefill kernel {prefill_ms:.3f} ms ({pf_gbps:.0f} GB/s); "
         f"epilogue {norm_ms:.3f} ms")
@@ -221,13 +379,20 @@ def main():
                      "achieved": pf_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": pf_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": pf_bytes, "avg_launch_ms": prefill_ms,
-                     "mfma_tflops": pf_tflops, "mfma_frac_of_bf16_peak": pf_tflops / BF16_MFMA_PEAK_TFLOPS},
+                     "mfma_tflops": pf_tflops, "mfma_frac_of_bf16_peak": pf_tflops / BF16_MFMA_PEAK_TFLOPS,
+                     "mfma_frac_of_bf16_peak_unfolded_count": pf_tflops_unf / BF16_MFMA_PEAK_TFLOPS},
         "epilogue": {"kernel": "gated_rmsnorm_kernel", "avg_launch_ms": norm_ms,
                      "achieved": nb / (norm_ms * 1e-3) / 1e9, "unit": "GB/s",
                      "frac": nb / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
     }
     del q, k, v, z, alpha, beta, y, out
     torch.cuda.empty_cache()
+
+    # ---------------- the 4K and 262K workloads ----------------
+    if not args.no_other_prefill:
+        result["prefill_short"] = bench_prefill_short(dev, stream, to_dev)
+        result["prefill_262k_segmented"] = bench_prefill_segmented(dev, stream, to_dev)
+        torch.cuda.empty_cache()
 
     # ---------------- decode: state GB/s over consecutive steps ----------------
     if not args.no_decode:
@@ -467,22 +632,8 @@ def main():
         del qp, kp, qo, ko, idx, wsq
         torch.cuda.empty_cache()
 
-    # ---------------- float64 CPU oracle on a bounded sample ----------------
-    if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-        from oracle import gated_delta_recurrence
-        Ts = args.cpu_tokens
-        log(f"cpu oracle: B=1 H={H} T={Ts} (single thread)")
-        ds = config_prefill_inputs(2, T=Ts)
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            gated_delta_recurrence(ds["q"], ds["k"], ds["v"], ds["alpha"], ds["beta"])
-            dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": Ts / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                                  "sample": f"float64 numpy oracle, first {Ts} tokens of the long-prefill "
-                                            f"workload shape (B=1, H={H}, d=128), {dt:.1f} s, "
-                                            f"{platform.processor() or platform.machine()}"}
-        log(f"cpu oracle {Ts / dt:.1f} tokens/s")
+    if cpu_baseline is not None:
+        result["cpu_baseline"] = cpu_baseline
 
     print(json.dumps(result), flush=True)
 

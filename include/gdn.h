@@ -51,7 +51,10 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 5, /* head size outside {16, 32, 64, 128}, or a size
                                 whose element count overflows the indexing     */
     GDN_ERR_LAUNCH = 6,      /* the HIP runtime rejected the kernel launch     */
-    GDN_ERR_WORKSPACE = 7    /* workspace NULL or smaller than required        */
+    GDN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required        */
+    GDN_ERR_DEVICE = 8       /* reported by gdn_prefill_status: a bounded wait
+                                inside the kernels gave up, so that call's
+                                outputs are invalid (its y rows hold NaN)      */
 } gdn_status;
 
 typedef enum {
@@ -77,10 +80,18 @@ typedef enum {
  *                 workspace must not be shared by calls that can overlap.
  *
  * With qkv_dtype == GDN_BF16 the dense chunk products run on fp16 MFMA with
- * float32 accumulation and a float32 state (bf16 inputs convert exactly to
- * fp16 when |x| <= 65504); with GDN_F32 they run on float32 MFMA.  T may be
- * any value >= 0 (T == 0 copies the initial state).  B * H must not exceed
- * 65535.
+ * float32 accumulation and a float32 state; with GDN_F32 they run on float32
+ * MFMA.  T may be any value >= 0 (T == 0 copies the initial state).  B * H
+ * must not exceed 65535.
+ *
+ * Range of the bf16 path.  q, k and v are converted to fp16 operands: bf16
+ * values of magnitude 2^-14 .. 65504 convert exactly, smaller ones become
+ * fp16 subnormals (losing low bits) or zero below 2^-25, larger ones become
+ * infinite.  The state S, the residual V - gamma K S, the misses E and the
+ * intra-chunk matrices also pass through fp16 operands, so |v|, the state's
+ * entries and |y| must stay well below 65504 (of order 10^3 or less keeps the
+ * products finite); unit-norm q and k keep the intra-chunk matrices small.
+ * The float32 path has no such limit.
  */
 gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta,
@@ -94,6 +105,23 @@ gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v,
  * for T == 0), or 0 with an invalid argument (the call reports the error).
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype);
+
+/*
+ * Device status of the last gdn_prefill_fwd call (with qkv_dtype GDN_BF16 and
+ * T > 0) that used this workspace.  The chunk walk hands data between waves
+ * through flags in on-chip memory, and every wait for such a flag is bounded
+ * so that a lost flag cannot hang the device.  A wait that gives up writes
+ * NaN into the y rows it could not compute and sets a status word at the start
+ * of the workspace; the next call on the workspace clears it.
+ *
+ * Synchronises hip_stream, then returns GDN_OK, or GDN_ERR_DEVICE when a wait
+ * gave up (GDN_ERR_NULL / GDN_ERR_ALIGN for a bad pointer, GDN_ERR_LAUNCH if
+ * the runtime fails).  The bound is 2^22 sleeps; the environment variable
+ * GDN_PREFILL_SPIN_LIMIT, read at each call, replaces it; a bound of 0 makes
+ * every such wait give up at once, which tests use to exercise the failure
+ * path (the kernels still finish normally).
+ */
+gdn_status gdn_prefill_status(const void* workspace, void* hip_stream);
 
 /*
  * One decode step for N live sequences (slinene page, Module A, one step of the
@@ -175,8 +203,12 @@ gdn_status gdn_frontend_fwd(const void* q_proj, const void* k_proj, const void* 
  *
  *   q, k, v, alpha, beta   the new block, [N, K, H, ...] as for verify
  *   state                  [N, H, d_k, d_v] float32, updated in place by the commit
- *   y, e                   the new block's outputs and misses (e may be NULL);
- *                          e may be the same buffer as prev_e
+ *   y, e                   the new block's outputs and misses (e may be NULL).
+ *                          e may be the same buffer as prev_e only when
+ *                          K == K_prev (each workgroup then reads its rows of
+ *                          prev_e before writing the same rows of e); that
+ *                          aliasing with K != K_prev returns GDN_ERR_SHAPE.
+ *                          Otherwise e and prev_e must not overlap.
  *   prev_*                 the previous block, [N, K_prev, H, ...], and its
  *                          accepted counts [N] int32 (clamped to 0..K_prev)
  *   K, K_prev in 1..8.
@@ -226,9 +258,10 @@ size_t gdn_prefill_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, gd
 
 /*
  * Multi-token (speculative) decode, part 1: verify a block of K draft tokens
- * per sequence from the live states (rainbus digest, inference section:
- * multi-token prediction drafts, the target model verifies; each draft token
- * is one step of the delta form, slinene page, Module A).  For t = 0 .. K-1,
+ * per sequence from the live states (rainbus digest, prerequisites section,
+ * the paragraph on multi-token prediction and speculative decoding: drafts are
+ * verified by the main model; each draft token is one step of the delta form,
+ * slinene page, Module A).  For t = 0 .. K-1,
  * starting from S = state:
  *     e_t = v_t - (alpha_t S)^T k_t;   S = alpha_t S + beta_t k_t e_t^T;
  *     y_t = scale * S^T q_t

@@ -9,14 +9,17 @@ kernels.  There is no fallback: if libgdn.so is missing, loading fails with an
 ImportError that says how to build it.
 """
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
-    "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_decode_step", "gdn_gated_rmsnorm",
+    "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_status", "gdn_decode_step",
+    "gdn_gated_rmsnorm",
     "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit", "gdn_decode_mtp_commit_verify",
     "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
     "gdn_qsa_select_workspace_bytes", "gdn_status_string",
@@ -58,6 +61,8 @@ def load_library():
     lib.gdn_prefill_fwd.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_status.argtypes = [vp, vp]
+    lib.gdn_prefill_status.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, f, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [fp, vp, fp, f, vp, lg, i, i, vp]
@@ -128,12 +133,36 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a binding with ``stream`` (when one is given) as torch's current
+    stream, so that every tensor it allocates (outputs and scratch) belongs to
+    the stream its kernels run on.  The caching allocator then cannot hand a
+    dropped scratch block to other work before those kernels are done with it."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def gdn_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype):
     """Scratch bytes gdn_prefill_fwd needs (dtype: torch.bfloat16 or torch.float32)."""
     code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
     return int(load_library().gdn_prefill_workspace_bytes(B, T, H, d_k, d_v, code))
 
 
+def gdn_prefill_status(workspace, stream=None):
+    """Synchronise ``stream`` and raise GdnError(GDN_ERR_DEVICE) if a bounded
+    wait inside the last bf16 gdn_prefill_fwd call on ``workspace`` gave up
+    (that call's y then holds NaN rows).  Returns None when the call was clean."""
+    _require_gpu(workspace, "workspace")
+    st = load_library().gdn_prefill_status(_ptr(workspace), _stream(stream, workspace.device))
+    if st:
+        raise GdnError(st, "gdn_prefill_status")
+
+
+@_on_stream
 def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, y=None,
                     scale=1.0, return_final_state=True, workspace=None, stream=None):
     """Chunked prefill.  q, k [B, T, H, d_k]; v [B, T, H, d_v] (bf16 or fp32, one
@@ -172,6 +201,7 @@ def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, 
     return y, final_state
 
 
+@_on_stream
 def gdn_decode_step(q, k, v, alpha, beta, state, y=None, scale=1.0, stream=None):
     """One decode step.  q, k [N, H, d_k]; v [N, H, d_v]; alpha, beta [N, H] fp32;
     state [N, H, d_k, d_v] fp32, updated in place.  Returns y [N, H, d_v] fp32."""
@@ -195,6 +225,7 @@ def gdn_decode_step(q, k, v, alpha, beta, state, y=None, scale=1.0, stream=None)
     return y
 
 
+@_on_stream
 def gdn_gated_rmsnorm(y, z, weight=None, eps=1e-6, out=None, stream=None):
     """sigmoid(z) * RMSNorm(y) * (1 + weight) over the last axis.  y fp32, z bf16
     or fp32 of the same shape; weight [d_v] fp32 or None.  Returns out (z's dtype)."""
@@ -216,6 +247,7 @@ def gdn_gated_rmsnorm(y, z, weight=None, eps=1e-6, out=None, stream=None):
     return out
 
 
+@_on_stream
 def gdn_frontend_fwd(q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, a_logit, b_logit, A, b_alpha,
                      q_hist=None, k_hist=None, v_hist=None, eps=1e-6, out=None, stream=None):
     """Front end: q, k = L2Norm(SiLU(ShortConv(proj))), v = SiLU(ShortConv(v_proj)),
@@ -262,6 +294,7 @@ def gdn_frontend_fwd(q_proj, k_proj, v_proj, conv_q, conv_k, conv_v, a_logit, b_
     return q, k, v, alpha, beta
 
 
+@_on_stream
 def gdn_decode_mtp_verify(q, k, v, alpha, beta, state, y=None, e=None, prefix_states=None, scale=1.0,
                           return_e=True, return_prefix_states=False, stream=None):
     """Verify a block of K draft tokens per sequence from the live states (read only).
@@ -295,6 +328,7 @@ def gdn_decode_mtp_verify(q, k, v, alpha, beta, state, y=None, e=None, prefix_st
     return y, e, prefix_states
 
 
+@_on_stream
 def gdn_decode_mtp_commit(k, alpha, beta, e, accepted, state, stream=None):
     """Advance each live state by its accepted drafts (int32 ``accepted`` [N] on the
     device, clamped to 0..K), using the misses ``e`` of gdn_decode_mtp_verify.
@@ -323,6 +357,7 @@ def gdn_prefill_bwd_workspace_bytes(B, T, H, d_k, d_v, dtype):
     return int(load_library().gdn_prefill_bwd_workspace_bytes(B, T, H, d_k, d_v, code))
 
 
+@_on_stream
 def gdn_prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, d_final_state=None, scale=1.0,
                     need_d_initial_state=True, workspace=None, out=None, stream=None):
     """Gradients of sum <dy, y> + <d_final_state, final_state> for gdn_prefill_fwd.
@@ -369,6 +404,7 @@ def gdn_prefill_bwd(q, k, v, alpha, beta, dy, initial_state=None, d_final_state=
     return dq, dk_, dv_, da, db, dS0
 
 
+@_on_stream
 def gdn_qsa_prep(q_proj, k_proj, r=4, rope_dims=64, rope_base=10000.0, eps=1e-6, q_weight=None, k_weight=None,
                  out=None, stream=None):
     """QSA indexer operands.  q_proj [B, n, H, D], k_proj [B, n, D] (bf16 or fp32, one
@@ -399,6 +435,7 @@ def gdn_qsa_select_workspace_bytes(B, n, H, D, r, K, dtype):
     return int(load_library().gdn_qsa_select_workspace_bytes(B, n, H, D, r, K, code))
 
 
+@_on_stream
 def gdn_qsa_select(q, kbar, r=4, K=2048, block_idx=None, workspace=None, stream=None):
     """Top-ceil(K / r) complete key blocks per query.  q [B, n, H, D], kbar
     [B, n // r, D] (bf16 or fp32).  Returns block_idx [B, n, ceil(K / r)] int32,
@@ -424,6 +461,7 @@ def gdn_qsa_select(q, kbar, r=4, K=2048, block_idx=None, workspace=None, stream=
     return block_idx
 
 
+@_on_stream
 def gdn_decode_mtp_commit_verify(q, k, v, alpha, beta, state, prev_k, prev_alpha, prev_beta, prev_e,
                                  prev_accepted, y=None, e=None, scale=1.0, return_e=True, stream=None):
     """Commit the previous block's accepted drafts onto ``state`` (in place) and

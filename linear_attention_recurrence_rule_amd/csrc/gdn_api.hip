@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <cstdlib>
 
 #include "../../include/gdn.h"
 #include "gdn_launch.hpp"
@@ -26,6 +27,16 @@ bool fits(long long a, long long b, long long c, long long d) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+// Bound of the prefill's in-kernel waits, in sleeps.  GDN_PREFILL_SPIN_LIMIT
+// overrides it so that tests can make a wait give up on purpose (the kernel
+// then finishes normally and reports it through the status word).
+int prefill_spin_limit() {
+    const char* env = std::getenv("GDN_PREFILL_SPIN_LIMIT");
+    if (!env || !*env) return 1 << 22;
+    const long v = std::strtol(env, nullptr, 10);
+    return v < 0 ? 0 : (v > (1L << 30) ? (1 << 30) : static_cast<int>(v));
+}
 
 }  // namespace
 
@@ -69,7 +80,18 @@ gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const fl
     gdn::PrefillArgs a{q, k, v, alpha, beta, initial_state, final_state, y,
                        B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale, workspace,
                        static_cast<hipStream_t>(hip_stream)};
+    a.spin_limit = prefill_spin_limit();
     return from_hip(gdn::launch_prefill(a));
+}
+
+gdn_status gdn_prefill_status(const void* workspace, void* hip_stream) {
+    if (!workspace) return GDN_ERR_NULL;
+    if (!aligned16(workspace)) return GDN_ERR_ALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    unsigned word = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_LAUNCH;
+    if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_LAUNCH;
+    return word == 0 ? GDN_OK : GDN_ERR_DEVICE;
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
@@ -296,6 +318,10 @@ gdn_status gdn_decode_mtp_commit_verify(const void* q, const void* k, const void
                           prev_k, static_cast<const void*>(prev_alpha), static_cast<const void*>(prev_beta),
                           static_cast<const void*>(prev_e), static_cast<const void*>(prev_accepted)})
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    // e may share prev_e's buffer only when both blocks have the same length:
+    // then each workgroup reads its own rows of prev_e before it writes the
+    // same rows of e.  With K != K_prev the rows belong to other workgroups.
+    if (e && e == prev_e && K != K_prev) return GDN_ERR_SHAPE;
     gdn::MtpArgs a{false, q, k, v, alpha, beta, state, y, e, nullptr, nullptr, N, K, H, d_k, d_v,
                    qkv_dtype == GDN_BF16, scale, static_cast<hipStream_t>(hip_stream)};
     a.pend_k = prev_k;
@@ -317,6 +343,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERR_UNSUPPORTED: return "unsupported head size or problem size";
         case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_DEVICE: return "an in-kernel wait gave up; that call's outputs are invalid (NaN)";
     }
     return "unknown status";
 }

@@ -18,8 +18,9 @@ struct PrefillArgs {
     int B, T, H, dk, dv;
     bool bf16;
     float scale;
-    void* workspace;             // bf16 path: per-chunk T' blocks (prefill_bf16_workspace_bytes)
+    void* workspace;             // bf16 path: status word + per-chunk T' blocks (prefill_bf16_workspace_bytes)
     hipStream_t stream;
+    int spin_limit = 1 << 22;    // sleeps before an in-kernel wait gives up (and reports it)
 };
 
 struct DecodeArgs {

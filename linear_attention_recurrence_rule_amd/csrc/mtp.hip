@@ -1,8 +1,9 @@
 // Multi-token (speculative) decode of the gated delta rule.
 //
 // The rainbus digest of "On the Design of Qwen3.8-Next Architecture" (its
-// inference section) describes drafting several tokens per step with
-// multi-token prediction and verifying them with the target model.  For the
+// prerequisites section, the paragraph on multi-token prediction and
+// speculative decoding) describes drafting several tokens at once and
+// verifying them with the main model in parallel.  For the
 // recurrent mixer a draft block of K tokens is K ordinary steps of the delta
 // form (slinene ai-papers-daily page, Module A) taken from a live state; when
 // the first j drafts are accepted, the live state must become the state after
@@ -77,7 +78,7 @@ template <int DK, int DV, int KM, bool kBf16, bool kPrefix, bool kCommit = false
 __global__ __launch_bounds__((MtpShape<DK, DV>::kThreads)) void mtp_verify_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
-    float* __restrict__ y, float* __restrict__ e_out, float* __restrict__ prefix, int K, int H,
+    float* __restrict__ y, float* e_out, float* __restrict__ prefix, int K, int H,
     float scale, PendingBlock pend) {
     using Sh = MtpShape<DK, DV>;
     constexpr int KQ = 2 * KM;                 // k_0..k_{KM-1}, q_0..q_{KM-1}

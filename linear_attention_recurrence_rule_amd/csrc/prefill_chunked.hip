@@ -53,6 +53,7 @@ constexpr int NGATE = 3 * C;             // per-chunk gate floats: g, gamma, d
 constexpr int WS_CHUNK = NTB * TBLK + 2 * NGATE;   // workspace halfs per (head, chunk)
 constexpr float kLogDecayFloor = -30.0f; // exp(-30) ~ 9e-14: alpha = 0 stays finite
 constexpr int kXcds = 8;
+constexpr int kStatusBytes = 256;        // workspace header holding the call's device status word
 
 // Row I of lower block number b in the order (0,0),(1,0),(1,1),(2,0),(2,1),
 // (2,2),(3,0),...; its column is b - I (I + 1) / 2.
@@ -209,7 +210,9 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
     return v;
 }
 
-// Workspace layout: for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
+// Workspace layout: a kStatusBytes header whose first word is the call's
+// device status (cleared by prep_kernel, set by a wait in main_kernel that
+// gave up), then for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
 // 16x16 blocks of T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each
 // row-major fp16, then the float32 gates g[C], gamma[C], d[C].
 //
@@ -226,7 +229,8 @@ template <int DK>
 __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
-                                                   _Float16* __restrict__ ws, int T, int H, int BH, int nchunks, int cpw) {
+                                                   _Float16* __restrict__ ws, unsigned* __restrict__ status,
+                                                   int T, int H, int BH, int nchunks, int cpw) {
     using Cfg = PrepCfg<DK>;
     using Frag = typename PrepFrag<DK>::type;
     constexpr int KS = Cfg::KSTEP, LDA = Cfg::LDA, ABLK = Cfg::ABLK;
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int lr = l & 15, lq = l >> 4;
     PrepWaveSmem& sm = smem[w];
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0u;   // this call's status
     const int bh = static_cast<int>(blockIdx.x) * kPrepWaves + w;
     if (bh >= BH) return;   // no workgroup barriers below
     const int b = bh / H, h = bh % H;
@@ -558,15 +563,28 @@ __device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK
     }
 }
 
-// Wait until the state wave has published E of `chunk`.  Bounded: a missing
-// flag ends the wait instead of hanging the device.
+// Wait until the state wave has published E of `chunk`.  Bounded by `spin`
+// sleeps, so that a missing flag ends the wait instead of hanging the device;
+// returns false when it gave up (the caller then reports it, see DevStatus).
 template <int DK>
-__device__ __forceinline__ void wait_published(MainSmem<DK>& sm, int chunk) {
+__device__ __forceinline__ bool wait_published(MainSmem<DK>& sm, int chunk, int spin) {
+    if (spin <= 0) return false;   // a bound of 0 gives up at once (tests of the failure path)
     for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
-        if (it > (1 << 22)) break;
+        if (it >= spin) return false;
         __builtin_amdgcn_s_sleep(1);
     }
+    return true;
 }
+
+// A wait that gave up sets bit 0 of the call's status word (read back by
+// gdn_prefill_status) and poisons the rows it would have written with NaN.
+struct DevStatus {
+    unsigned* word;
+    int spin;
+    __device__ __forceinline__ void fail() const {
+        if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+};
 
 // Loader role: during chunk c the loads of chunk c+2 are issued into one
 // register set and chunk c+1 (loaded during chunk c-1, in the other set) is
@@ -750,7 +768,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
 // split-K order, and y leaves as one 16-byte store per lane and block.
 template <int DK, int buf, int RP>
 __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int lane, float* ylane, long ytok,
-                                             int T, float scale) {
+                                             int T, float scale, const DevStatus& ds) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
     constexpr int Irow[2] = {RP, 3 - RP};
@@ -829,7 +847,9 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
         Pb[ii][0] = cat(ph[0], ph[1]);
         Pb[ii][1] = cat(ph[2], ph[3]);
     }
-    wait_published(sm, chunk);
+    const bool published = wait_published(sm, chunk, ds.spin);
+    if (!published) ds.fail();
+    const float ysc = published ? scale : __builtin_nanf("");
     // Y^T = E^T P^T + gamma (Q S)^T: lane (t + 16 g) holds row t, columns 4 g .. 4 g + 3
     const half8 Ea0 = ld_split<C>(sm.ET, lr, 0, lq), Ea1 = ld_split<C>(sm.ET, lr, 32, lq);
 #pragma unroll
@@ -843,7 +863,7 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
         // row, which merge in L2 (streaming stores measured 28% more HBM writes)
         if (t < T)
             *reinterpret_cast<float4v*>(ylane + t * ytok) =
-                float4v{scale * yv[0], scale * yv[1], scale * yv[2], scale * yv[3]};
+                float4v{ysc * yv[0], ysc * yv[1], ysc * yv[2], ysc * yv[3]};
     }
 }
 
@@ -851,13 +871,13 @@ __device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int la
 // points at this lane's four y columns of token 0; ytok is the token stride.
 template <int DK, int RP>
 __device__ __forceinline__ void output_role(MainSmem<DK>& sm, int nchunks, int lane, float* ylane, long ytok, int T,
-                                            float scale) {
+                                            float scale, const DevStatus& ds) {
     __syncthreads();
     for (int c = 0; c < nchunks; c += 2) {
-        output_chunk<DK, 0, RP>(sm, c, lane, ylane, ytok, T, scale);
+        output_chunk<DK, 0, RP>(sm, c, lane, ylane, ytok, T, scale, ds);
         __syncthreads();
         if (c + 1 < nchunks) {
-            output_chunk<DK, 1, RP>(sm, c + 1, lane, ylane, ytok, T, scale);
+            output_chunk<DK, 1, RP>(sm, c + 1, lane, ylane, ytok, T, scale, ds);
             __syncthreads();
         }
     }
@@ -868,7 +888,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ v, const _Float16* __restrict__ ws,
                                                    const float* __restrict__ S0, float* __restrict__ S_out,
                                                    float* __restrict__ y, int B, int T, int H, int DV, int nsl,
-                                                   float scale) {
+                                                   float scale, DevStatus ds) {
     using Cfg = MainCfg<DK>;
     __shared__ MainSmem<DK> sm;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -927,8 +947,8 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     } else if (is_out) {
         float* ylane = y + (tok0 * H + h) * static_cast<long>(DV) + col0 + 4 * lq;
         const long ytok = static_cast<long>(H) * DV;
-        if (w == Cfg::W_OUT0) output_role<DK, 0>(sm, nchunks, lane, ylane, ytok, T, scale);
-        else output_role<DK, 1>(sm, nchunks, lane, ylane, ytok, T, scale);
+        if (w == Cfg::W_OUT0) output_role<DK, 0>(sm, nchunks, lane, ylane, ytok, T, scale, ds);
+        else output_role<DK, 1>(sm, nchunks, lane, ylane, ytok, T, scale, ds);
     } else if (misc) {
         loader_role<DK, true>(sm, nchunks, lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
     } else {
@@ -940,7 +960,8 @@ template <int DK>
 static hipError_t launch_t(const PrefillArgs& a) {
     using Cfg = MainCfg<DK>;
     const int nchunks = (a.T + C - 1) / C;
-    _Float16* ws = static_cast<_Float16*>(a.workspace);
+    unsigned* status = static_cast<unsigned*>(a.workspace);
+    _Float16* ws = reinterpret_cast<_Float16*>(static_cast<char*>(a.workspace) + kStatusBytes);
     if (nchunks > 0) {
         // chunks per wave: about one round of resident workgroups, at most 16
         const int BH = a.B * a.H;
@@ -949,7 +970,8 @@ static hipError_t launch_t(const PrefillArgs& a) {
             std::min<long>(16, std::max<long>(1, (gx * nchunks + kPrepResidentWGs - 1) / kPrepResidentWGs)));
         const int gy = (nchunks + cpw - 1) / cpw;
         hipLaunchKernelGGL((prep_kernel<DK>), dim3(static_cast<unsigned>(gx), gy), dim3(256), 0, a.stream,
-                           static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, a.T, a.H, BH, nchunks, cpw);
+                           static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, status, a.T, a.H, BH, nchunks,
+                           cpw);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -958,7 +980,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((main_kernel<DK>), dim3(groups * kXcds * nsl), dim3(Cfg::NT), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), ws, a.initial_state, a.final_state, a.y,
-                       a.B, a.T, a.H, a.dv, nsl, a.scale);
+                       a.B, a.T, a.H, a.dv, nsl, a.scale, DevStatus{status, a.spin_limit});
     return hipGetLastError();
 }
 
@@ -966,7 +988,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
 
 size_t prefill_bf16_workspace_bytes(int B, int T, int H) {
     const long nchunks = (T + chunked::C - 1) / chunked::C;
-    return static_cast<size_t>(B) * H * nchunks * chunked::WS_CHUNK * sizeof(_Float16);
+    return chunked::kStatusBytes + static_cast<size_t>(B) * H * nchunks * chunked::WS_CHUNK * sizeof(_Float16);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a) {

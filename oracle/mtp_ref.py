@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): the HIP library never
 calls into this file, and this file never calls the HIP library.
 
 Source: the rainbus digest of "On the Design of Qwen3.8-Next Architecture"
-(its inference section: multi-token prediction drafts several tokens per
-step, which the target model then verifies) together with the delta form of
+(its prerequisites section, the paragraph on multi-token prediction and
+speculative decoding: a light module drafts several tokens at once, which the
+main model then verifies in parallel) together with the delta form of
 the recurrence on the slinene ai-papers-daily page, Module A.  A draft block
 of K tokens is K ordinary recurrence steps taken from a live state; when only
 the first j drafts are accepted, the live state must become the state after

@@ -15,7 +15,7 @@ import linear_attention_recurrence_rule_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE, ERR_DEVICE = range(9)
 FAKE = 0x10000          # an aligned, never-dereferenced address
 MISALIGNED = 0x10004
 
@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
                                     "gdn_decode_mtp_verify", "gdn_decode_step",
                                     "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_bwd",
                                     "gdn_prefill_bwd_workspace_bytes", "gdn_prefill_fwd",
-                                    "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
+                                    "gdn_prefill_status", "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
                                     "gdn_qsa_select_workspace_bytes", "gdn_status_string"]
 
 
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert gdn.gdn_status_string(OK) == "ok"
-    for s in range(1, 8):
+    for s in range(1, 9):
         assert gdn.gdn_status_string(s) and gdn.gdn_status_string(s) != "unknown status"
     assert gdn.gdn_status_string(99) == "unknown status"
 
@@ -76,7 +76,7 @@ def _prefill(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y=FAKE,
     (dict(ws=MISALIGNED), ERR_ALIGN),
     (dict(B=300, H=300), ERR_UNSUPPORTED),
     (dict(ws=None), ERR_WORKSPACE),
-    (dict(ws_bytes=5119), ERR_WORKSPACE),
+    (dict(ws_bytes=5119 + 256), ERR_WORKSPACE),
 ])
 def test_prefill_rejects(kwargs, status):
     assert _prefill(**kwargs) == status
@@ -84,14 +84,22 @@ def test_prefill_rejects(kwargs, status):
 
 def test_workspace_bytes():
     lib = gdn.load_library()
-    # bf16: per (sequence, head, 64-token chunk) the 10 lower fp16 16x16 blocks
-    # of T' (5120 bytes) and three float32 gate vectors of 64 (768 bytes)
+    # bf16: a 256-byte status header, then per (sequence, head, 64-token
+    # chunk) the 10 lower fp16 16x16 blocks of T' (5120 bytes) and three
+    # float32 gate vectors of 64 (768 bytes)
     per_chunk = 10 * 256 * 2 + 3 * 64 * 4
-    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 2 * per_chunk
-    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 2 * 3 * 2 * per_chunk
+    assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 256 + 2 * per_chunk
+    assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 256 + 2 * 3 * 2 * per_chunk
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 0) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 0, 3, 128, 128, 1) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 48, 128, 1) == 0
+
+
+def test_prefill_status_rejects_bad_pointers():
+    lib = gdn.load_library()
+    lib.gdn_prefill_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.gdn_prefill_status(None, None) == ERR_NULL
+    assert lib.gdn_prefill_status(MISALIGNED, None) == ERR_ALIGN
 
 
 def test_prefill_empty_without_state_is_a_no_op():
@@ -376,6 +384,7 @@ def _cv(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, y=FAKE, e=None, pk=FAKE,
     (dict(s=None), ERR_NULL),
     (dict(pk=MISALIGNED), ERR_ALIGN),
     (dict(e=MISALIGNED), ERR_ALIGN),
+    (dict(e=FAKE, pe=FAKE, K=4, Kp=3), ERR_SHAPE),   # e aliasing prev_e needs K == K_prev
 ])
 def test_mtp_commit_verify_rejects(kwargs, status):
     assert _cv(**kwargs) == status

@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import gated_delta_decode_step, gated_delta_recurrence
+from oracle import gated_delta_decode_step, gated_delta_recurrence, rel_err
+from tests import oracle_pool
 from tests.gpu_util import TOL, check, dev, host, say
 from workloads import decode_initial_state, decode_step_inputs, prefill_inputs
 import linear_attention_recurrence_rule_amd as gdn
@@ -49,15 +50,47 @@ def test_decode_equals_recurrence_over_steps():
     check("final state", host(state), S_ref, DEC_TOL)
 
 
-def test_decode_config3_full_shape():
-    """256 sequences x 32 heads, d = 128, bf16: every state for 4 steps."""
-    say("decode config 3 full shape")
-    S = decode_initial_state()
-    state = dev(S)
-    for step in range(4):
-        d = decode_step_inputs(step)
-        y = gdn.gdn_decode_step(dev(d["q"], "bf16"), dev(d["k"], "bf16"), dev(d["v"], "bf16"),
-                                dev(d["alpha"]), dev(d["beta"]), state)
-        y_ref, S = gated_delta_decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S)
-        check(f"step {step} y", host(y), y_ref, DEC_TOL)
-        check(f"step {step} state", host(state), S, DEC_TOL)
+def _samples(d, n, h):
+    return {x: d[x][n, h][:, None] for x in d}
+
+
+@pytest.mark.timeout(1200)
+def test_decode_config3_1000_steps():
+    """The decode workload (256 sequences x 32 heads, d = 128, bf16 inputs,
+    fp32 states) over its 1000 consecutive steps: every one of the 8192 states
+    and every y after each of the first 16 steps, then 64 fixed sampled
+    (sequence, head) states and their y after every step, and those 64 states
+    after the last step."""
+    say("decode config 3: 1000 steps")
+    S0 = decode_initial_state()
+    state = dev(S0)
+    rng = np.random.default_rng(333)
+    flat = np.sort(rng.choice(256 * 32, size=64, replace=False))
+    sn, sh = flat // 32, flat % 32
+    S_full = S0.astype(np.float64)
+    S_samp = None
+    worst_y = 0.0
+    batch = 16
+    for s0 in range(0, 1000, batch):
+        inputs = oracle_pool.map_tasks(decode_step_inputs, [(s,) for s in range(s0, min(1000, s0 + batch))])
+        for j, d in enumerate(inputs):
+            step = s0 + j
+            y = gdn.gdn_decode_step(dev(d["q"], "bf16"), dev(d["k"], "bf16"), dev(d["v"], "bf16"),
+                                    dev(d["alpha"]), dev(d["beta"]), state)
+            if step < 16:
+                y_ref, S_full = oracle_pool.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_full)
+                check(f"step {step} y (all states)", host(y), y_ref, DEC_TOL)
+                check(f"step {step} state (all states)", host(state), S_full, DEC_TOL)
+                if step == 15:
+                    S_samp = S_full[sn, sh][:, None].copy()
+                    S_full = None
+            else:
+                ds = _samples(d, sn, sh)
+                y_ref, S_samp = gated_delta_decode_step(ds["q"], ds["k"], ds["v"], ds["alpha"], ds["beta"], S_samp)
+                err = rel_err(host(y)[sn, sh][:, None], y_ref)
+                worst_y = max(worst_y, err)
+                assert err <= DEC_TOL, f"step {step}: sampled y error {err:.3e}"
+        if s0 % 160 == 0:
+            say(f"    through step {s0 + batch - 1}: worst sampled y error {worst_y:.3e}")
+    say(f"    steps 16..999, 64 sampled states: worst y error {worst_y:.3e}")
+    check("64 sampled states after 1000 steps", host(state)[sn, sh][:, None], S_samp, DEC_TOL)

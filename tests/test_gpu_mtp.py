@@ -210,3 +210,30 @@ def test_fused_rounds_follow_the_accepted_tokens():
         if cat["q"].shape[1]:
             check(f"seq {n} accepted y", cat["y"], y_ref, MTP_TOL)
         check(f"seq {n} state", S_gpu[n:n + 1], S_ref, MTP_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_commit_verify_with_e_aliasing_prev_e(dtype):
+    """The fused call with e written into prev_e's own buffer (K == K_prev):
+    the same state, y and e as with separate buffers."""
+    say(f"mtp commit+verify, e aliasing prev_e, {dtype}")
+    N, K, H, d_ = 7, 4, 3, 128
+    prev, S0 = _block(N, K, H, d_, d_, dtype, seed=61)
+    new, _ = _block(N, K, H, d_, d_, dtype, seed=62)
+    _, pe_ref, _ = mtp_verify(prev["q"], prev["k"], prev["v"], prev["alpha"], prev["beta"], S0)
+    acc = torch.from_numpy(np.array([0, K, 1, 2, 3, K, 0], dtype=np.int32)).cuda()
+    pk, pa, pb = dev(prev["k"], dtype), dev(prev["alpha"]), dev(prev["beta"])
+    blk = _gpu_block(new, dtype)
+    state_sep = dev(S0)
+    y_sep, e_sep = gdn.gdn_decode_mtp_commit_verify(*blk, state_sep, pk, pa, pb, dev(pe_ref), acc)
+    state_al = dev(S0)
+    shared = dev(pe_ref)
+    y_al, e_al = gdn.gdn_decode_mtp_commit_verify(*blk, state_al, pk, pa, pb, shared, acc, e=shared)
+    assert e_al.data_ptr() == shared.data_ptr()
+    np.testing.assert_array_equal(host(state_al), host(state_sep))
+    np.testing.assert_array_equal(host(y_al), host(y_sep))
+    np.testing.assert_array_equal(host(e_al), host(e_sep))
+    S1 = mtp_commit(prev["k"], prev["alpha"], prev["beta"], pe_ref, host(acc).astype(np.int32), S0)
+    y_ref, e_ref, _ = mtp_verify(new["q"], new["k"], new["v"], new["alpha"], new["beta"], S1)
+    check("aliased y", host(y_al), y_ref, MTP_TOL)
+    check("aliased e", host(e_al), e_ref, MTP_TOL)
