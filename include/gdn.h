@@ -107,6 +107,29 @@ gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v,
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype);
 
 /*
+ * gdn_prefill_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The scratch that gdn_prefill_fwd takes as `workspace` lives instead in a
+ * static device array of GDN_PREFILL_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library holds on each GPU it runs on until the process ends; the call
+ * allocates nothing.  Arguments, layouts and results are those of
+ * gdn_prefill_fwd (the same kernels run); the caller passes every input and
+ * output.  Returns GDN_ERR_WORKSPACE when gdn_prefill_workspace_bytes(...) for
+ * these sizes exceeds the array (bf16: 256 bytes plus 5,888 bytes per
+ * (sequence, head, 64-token chunk), i.e. B * H * ceil(T / 64) up to 22,795),
+ * GDN_ERR_LAUNCH if the array's device address cannot be obtained.  All calls
+ * on one GPU share its array, which keeps the last call's contents: calls that
+ * can overlap on one GPU (different streams, or host threads) race and must
+ * not be issued.  An in-kernel wait that gives up shows as NaN rows in y.
+ */
+#define GDN_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta,
+                                   const float* initial_state, float* final_state, float* y,
+                                   int B, int T, int H, int d_k, int d_v,
+                                   gdn_dtype qkv_dtype, float scale, void* hip_stream);
+
+/*
  * Device status of the last gdn_prefill_fwd call (with qkv_dtype GDN_BF16 and
  * T > 0) that used this workspace.  The chunk walk hands data between waves
  * through flags in on-chip memory, and every wait for such a flag is bounded

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "load_library", "library_path",
-    "gdn_prefill_fwd", "gdn_prefill_workspace_bytes", "gdn_prefill_status", "gdn_decode_step",
+    "gdn_prefill_fwd", "gdn_prefill_fwd_noalloc", "gdn_prefill_workspace_bytes", "gdn_prefill_status",
+    "gdn_decode_step",
     "gdn_gated_rmsnorm",
     "gdn_frontend_fwd", "gdn_decode_mtp_verify", "gdn_decode_mtp_commit", "gdn_decode_mtp_commit_verify",
     "gdn_prefill_bwd", "gdn_prefill_bwd_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
@@ -61,6 +62,8 @@ def load_library():
     lib.gdn_prefill_fwd.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i, i, i, i, i, i, f, vp]
+    lib.gdn_prefill_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_status.argtypes = [vp, vp]
     lib.gdn_prefill_status.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, f, vp]
@@ -198,6 +201,34 @@ def gdn_prefill_fwd(q, k, v, alpha, beta, initial_state=None, final_state=None, 
                              _ptr(workspace), ws_bytes, _stream(stream, dev))
     if st:
         raise GdnError(st, "gdn_prefill_fwd")
+    return y, final_state
+
+
+def gdn_prefill_fwd_noalloc(q, k, v, alpha, beta, initial_state, final_state, y, scale=1.0, stream=None):
+    """gdn_prefill_fwd whose scratch lives in the library's static per-GPU array
+    (GDN_PREFILL_NOALLOC_SCRATCH_BYTES): neither this binding nor the library
+    allocates anything, so the caller passes every output (``final_state``
+    may be None, or ``initial_state`` for an in-place update).  Calls that can
+    overlap on one GPU must not be issued (they share the array)."""
+    lib = load_library()
+    _require_gpu(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
+    _check(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    if y is None:
+        raise ValueError("gdn_prefill_fwd_noalloc needs a preallocated y")
+    _check(y, "y", (B, T, H, dv), torch.float32, dev)
+    st = lib.gdn_prefill_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+                                     _ptr(final_state), _ptr(y), B, T, H, dk, dv, _dtype_code(q), float(scale),
+                                     _stream(stream, dev))
+    if st:
+        raise GdnError(st, "gdn_prefill_fwd_noalloc")
     return y, final_state
 
 

@@ -5,6 +5,7 @@
 
 #include <climits>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "gdn_launch.hpp"
@@ -63,17 +64,32 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dt
     return workspace_needed(B, T, H, qkv_dtype);
 }
 
-gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* initial_state, float* final_state, float* y,
-                           int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
-                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+namespace {
+
+// Every argument check of gdn_prefill_fwd except the workspace's.
+gdn_status prefill_args_check(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                              const float* initial_state, const float* final_state, const float* y, int B, int T,
+                              int H, int d_k, int d_v, gdn_dtype qkv_dtype) {
     const gdn_status st = prefill_check(B, T, H, d_k, d_v, qkv_dtype);
     if (st != GDN_OK) return st;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !y)) return GDN_ERR_NULL;
     for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(beta),
                           static_cast<const void*>(initial_state), static_cast<const void*>(final_state),
-                          static_cast<const void*>(y), static_cast<const void*>(workspace)})
+                          static_cast<const void*>(y)})
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
+}  // namespace
+
+gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, float* final_state, float* y,
+                           int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = prefill_args_check(q, k, v, alpha, beta, initial_state, final_state, y, B, T, H, d_k, d_v,
+                                             qkv_dtype);
+    if (st != GDN_OK) return st;
+    if (workspace && !aligned16(workspace)) return GDN_ERR_ALIGN;
     const size_t need = workspace_needed(B, T, H, qkv_dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
     if (!final_state && T == 0) return GDN_OK;
@@ -82,6 +98,59 @@ gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const fl
                        static_cast<hipStream_t>(hip_stream)};
     a.spin_limit = prefill_spin_limit();
     return from_hip(gdn::launch_prefill(a));
+}
+
+// ---------------------------------------------------------------------------
+// gdn_prefill_fwd_noalloc: the same call with its scratch in a static device
+// array, for callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid hipMalloc).  Nothing
+// here allocates or frees.
+// ---------------------------------------------------------------------------
+namespace {
+
+// One array per GPU, held from module load until the process ends.
+static __device__ __align__(256) unsigned char scratch[GDN_PREFILL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void* g_scratch[kMaxDevices];   // the array's device address on each GPU
+
+// The device address of `scratch` on the current GPU.  In host code the
+// array's name is only a stand-in, so its address is looked up once per device,
+// with that device current, and kept; kernels only ever receive that address.
+hipError_t scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+gdn_status gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                                   const float* beta, const float* initial_state, float* final_state, float* y,
+                                   int B, int T, int H, int d_k, int d_v, gdn_dtype qkv_dtype, float scale,
+                                   void* hip_stream) {
+    const gdn_status st = prefill_args_check(q, k, v, alpha, beta, initial_state, final_state, y, B, T, H, d_k, d_v,
+                                             qkv_dtype);
+    if (st != GDN_OK) return st;
+    const size_t need = workspace_needed(B, T, H, qkv_dtype);
+    if (need > GDN_PREFILL_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    if (!final_state && T == 0) return GDN_OK;
+    void* ws = nullptr;
+    if (need > 0 && scratch_on_current_device(&ws) != hipSuccess) return GDN_ERR_LAUNCH;
+    return gdn_prefill_fwd(q, k, v, alpha, beta, initial_state, final_state, y, B, T, H, d_k, d_v, qkv_dtype, scale,
+                           ws, need, hip_stream);
 }
 
 gdn_status gdn_prefill_status(const void* workspace, void* hip_stream) {

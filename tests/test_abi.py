@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
                                     "gdn_decode_mtp_verify", "gdn_decode_step",
                                     "gdn_frontend_fwd", "gdn_gated_rmsnorm", "gdn_prefill_bwd",
                                     "gdn_prefill_bwd_workspace_bytes", "gdn_prefill_fwd",
-                                    "gdn_prefill_status", "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
+                                    "gdn_prefill_fwd_noalloc", "gdn_prefill_status",
+                                    "gdn_prefill_workspace_bytes", "gdn_qsa_prep", "gdn_qsa_select",
                                     "gdn_qsa_select_workspace_bytes", "gdn_status_string"]
 
 
@@ -93,6 +94,29 @@ def test_workspace_bytes():
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 0) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 0, 3, 128, 128, 1) == 0
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 48, 128, 1) == 0
+
+
+def _prefill_noalloc(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y=FAKE,
+                     B=1, T=8, H=2, dk=64, dv=64, dtype=1):
+    lib = gdn.load_library()
+    lib.gdn_prefill_fwd_noalloc.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 + [ctypes.c_float,
+                                                                                         ctypes.c_void_p]
+    return lib.gdn_prefill_fwd_noalloc(q, k, v, a, b, s0, sT, y, B, T, H, dk, dv, dtype, 1.0, None)
+
+
+def test_prefill_noalloc_rejects_sizes_beyond_its_scratch():
+    lib = gdn.load_library()
+    limit = 128 << 20
+    # 22795 (sequence, head, chunk) units fit the 128 MiB array, 22796 do not
+    assert lib.gdn_prefill_workspace_bytes(1, 22795 * 64, 1, 128, 128, 1) <= limit
+    assert lib.gdn_prefill_workspace_bytes(1, 22796 * 64, 1, 128, 128, 1) > limit
+    assert _prefill_noalloc(B=1, T=22796 * 64, H=1, dk=128, dv=128) == ERR_WORKSPACE
+    assert _prefill_noalloc(B=4, T=32768, H=32, dk=128, dv=128) == ERR_WORKSPACE
+    # argument errors are reported as by gdn_prefill_fwd (checked before anything else)
+    assert _prefill_noalloc(dtype=2) == ERR_DTYPE
+    assert _prefill_noalloc(dk=48) == ERR_UNSUPPORTED
+    assert _prefill_noalloc(q=None) == ERR_NULL
+    assert _prefill_noalloc(y=MISALIGNED) == ERR_ALIGN
 
 
 def test_prefill_status_rejects_bad_pointers():
