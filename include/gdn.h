@@ -52,9 +52,8 @@ typedef enum {
                                 whose element count overflows the indexing     */
     GDN_ERR_LAUNCH = 6,      /* the HIP runtime rejected the kernel launch     */
     GDN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required        */
-    GDN_ERR_DEVICE = 8       /* reported by gdn_prefill_status: a bounded wait
-                                inside the kernels gave up, so that call's
-                                outputs are invalid (its y rows hold NaN)      */
+    GDN_ERR_DEVICE = 8       /* reported by gdn_prefill_status: the call wrote
+                                non-finite y or state values                   */
 } gdn_status;
 
 typedef enum {
@@ -115,12 +114,12 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dt
  * allocates nothing.  Arguments, layouts and results are those of
  * gdn_prefill_fwd (the same kernels run); the caller passes every input and
  * output.  Returns GDN_ERR_WORKSPACE when gdn_prefill_workspace_bytes(...) for
- * these sizes exceeds the array (bf16: 256 bytes plus 5,888 bytes per
- * (sequence, head, 64-token chunk), i.e. B * H * ceil(T / 64) up to 22,795),
+ * these sizes exceeds the array (bf16: 256 bytes plus 6,144 bytes per
+ * (sequence, head, 64-token chunk), i.e. B * H * ceil(T / 64) up to 21,845),
  * GDN_ERR_LAUNCH if the array's device address cannot be obtained.  All calls
  * on one GPU share its array, which keeps the last call's contents: calls that
  * can overlap on one GPU (different streams, or host threads) race and must
- * not be issued.  An in-kernel wait that gives up shows as NaN rows in y.
+ * not be issued.
  */
 #define GDN_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 gdn_status gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
@@ -131,18 +130,16 @@ gdn_status gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
 
 /*
  * Device status of the last gdn_prefill_fwd call (with qkv_dtype GDN_BF16 and
- * T > 0) that used this workspace.  The chunk walk hands data between waves
- * through flags in on-chip memory, and every wait for such a flag is bounded
- * so that a lost flag cannot hang the device.  A wait that gives up writes
- * NaN into the y rows it could not compute and sets a status word at the start
- * of the workspace; the next call on the workspace clears it.
+ * T > 0) that used this workspace.  The chunk walk notes whether it wrote any
+ * non-finite y or final-state value in a status word at the start of the
+ * workspace (the next call on the workspace clears it).  With finite inputs
+ * that only happens when an input or intermediate leaves the fp16 operand
+ * range of the bf16 path (see gdn_prefill_fwd), so a caller that cannot bound
+ * its inputs can check here instead of scanning the outputs.
  *
- * Synchronises hip_stream, then returns GDN_OK, or GDN_ERR_DEVICE when a wait
- * gave up (GDN_ERR_NULL / GDN_ERR_ALIGN for a bad pointer, GDN_ERR_LAUNCH if
- * the runtime fails).  The bound is 2^22 sleeps; the environment variable
- * GDN_PREFILL_SPIN_LIMIT, read at each call, replaces it; a bound of 0 makes
- * every such wait give up at once, which tests use to exercise the failure
- * path (the kernels still finish normally).
+ * Synchronises hip_stream, then returns GDN_OK, or GDN_ERR_DEVICE when a
+ * non-finite value was written (GDN_ERR_NULL / GDN_ERR_ALIGN for a bad
+ * pointer, GDN_ERR_LAUNCH if the runtime fails).
  */
 gdn_status gdn_prefill_status(const void* workspace, void* hip_stream);
 

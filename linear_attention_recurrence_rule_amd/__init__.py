@@ -156,9 +156,10 @@ def gdn_prefill_workspace_bytes(B, T, H, d_k, d_v, dtype):
 
 
 def gdn_prefill_status(workspace, stream=None):
-    """Synchronise ``stream`` and raise GdnError(GDN_ERR_DEVICE) if a bounded
-    wait inside the last bf16 gdn_prefill_fwd call on ``workspace`` gave up
-    (that call's y then holds NaN rows).  Returns None when the call was clean."""
+    """Synchronise ``stream`` and raise GdnError(GDN_ERR_DEVICE) if the last
+    bf16 gdn_prefill_fwd call on ``workspace`` wrote a non-finite y or final
+    state value (with finite inputs: an input or intermediate outside the fp16
+    operand range).  Returns None when the call was clean."""
     _require_gpu(workspace, "workspace")
     st = load_library().gdn_prefill_status(_ptr(workspace), _stream(stream, workspace.device))
     if st:

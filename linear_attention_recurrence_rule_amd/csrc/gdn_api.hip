@@ -4,7 +4,6 @@
 #include <stdint.h>
 
 #include <climits>
-#include <cstdlib>
 #include <mutex>
 
 #include "../../include/gdn.h"
@@ -28,16 +27,6 @@ bool fits(long long a, long long b, long long c, long long d) {
 }
 
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
-
-// Bound of the prefill's in-kernel waits, in sleeps.  GDN_PREFILL_SPIN_LIMIT
-// overrides it so that tests can make a wait give up on purpose (the kernel
-// then finishes normally and reports it through the status word).
-int prefill_spin_limit() {
-    const char* env = std::getenv("GDN_PREFILL_SPIN_LIMIT");
-    if (!env || !*env) return 1 << 22;
-    const long v = std::strtol(env, nullptr, 10);
-    return v < 0 ? 0 : (v > (1L << 30) ? (1 << 30) : static_cast<int>(v));
-}
 
 }  // namespace
 
@@ -96,7 +85,6 @@ gdn_status gdn_prefill_fwd(const void* q, const void* k, const void* v, const fl
     gdn::PrefillArgs a{q, k, v, alpha, beta, initial_state, final_state, y,
                        B, T, H, d_k, d_v, qkv_dtype == GDN_BF16, scale, workspace,
                        static_cast<hipStream_t>(hip_stream)};
-    a.spin_limit = prefill_spin_limit();
     return from_hip(gdn::launch_prefill(a));
 }
 
@@ -412,7 +400,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERR_UNSUPPORTED: return "unsupported head size or problem size";
         case GDN_ERR_LAUNCH: return "HIP kernel launch failed";
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
-        case GDN_ERR_DEVICE: return "an in-kernel wait gave up; that call's outputs are invalid (NaN)";
+        case GDN_ERR_DEVICE: return "the call wrote non-finite y or state (inputs outside the fp16 operand range?)";
     }
     return "unknown status";
 }

@@ -20,7 +20,6 @@ struct PrefillArgs {
     float scale;
     void* workspace;             // bf16 path: status word + per-chunk T' blocks (prefill_bf16_workspace_bytes)
     hipStream_t stream;
-    int spin_limit = 1 << 22;    // sleeps before an in-kernel wait gives up (and reports it)
 };
 
 struct DecodeArgs {

@@ -3,7 +3,9 @@
 // evaluated 64 tokens at a time in its chunkwise WY / UT-transform form).
 //
 // Per chunk of C = 64 tokens with start state S (g = in-chunk prefix sum of
-// log alpha, gamma = exp(g), Gamma_ti = exp(g_t - g_i), d_t = exp(g_last - g_t)):
+// log alpha, gamma = exp(g), Gamma_ti = exp(g_t - g_i), d_t = exp(g_last - g_t);
+// the kernels keep g in base-2 units, g2 = g / ln 2, so that every decay
+// factor is one native 2^x):
 //   A  = strictLower(diag(beta) (Gamma o K K^T)),   T' = (I + A)^-1 diag(beta)
 //   E  = T' (V - diag(gamma) K S)          (rows: beta_t times token t's miss)
 //   Y  = diag(gamma) Q S + P E,            P = lower(Gamma o Q K^T)
@@ -13,30 +15,7 @@
 // sequential kernel (main_kernel) then runs the chunks of one (head,
 // 16-column value slice) in order.
 //
-// main_kernel: 8 waves with fixed roles, one workgroup barrier per chunk.
-//   wave 0      state wave: K S, R = V - gamma K S, E = T' R, S += K^T D E.
-//               The float32 state slice never leaves registers; every MFMA
-//               operand it produces (S, R, E) is fed to the next MFMA straight
-//               from the accumulator registers (split-K operand layout below),
-//               so the chain has no LDS round trip.
-//   waves 1, 2  output waves (token blocks {0,3} and {1,2}): Q S and P (built
-//               transposed so it feeds the MFMA from registers), then, once
-//               the state wave has published E, Y += P E -> y.
-//   waves 3..7  loader waves (q and k on waves 3, 5, 6, 7; v, T' and the
-//               gates on wave 4, which shares the state wave's SIMD): chunk
-//               c+1 goes to the other LDS buffer from registers loaded during
-//               the previous chunk.
-// Loads run one chunk ahead in two register sets; they are unconditional
-// (addresses clamped to the last token, whose copies past the end of the
-// sequence are harmless: beta = 0 there) so that the compiler's wait counts
-// stay exact across the chunk loop.
-// Split-K operand layout: for a 16x16x32 MFMA, slot s of lane (m + 16 g) holds
-// K-index 16*(s/4) + 4 g + s%4 of its row/column.  Two 16x16 accumulator tiles
-// (lane (n + 16 g) holds rows 4 g .. 4 g + 3 of column n) stacked along K are
-// exactly such a B operand, and A operands are read from LDS in the same order.
-// LDS tiles are fp16 row-major with 16-byte chunks XOR-swizzled by row; the
-// operands that need a tile transposed (K^T, and V in accumulator order) are
-// read with gfx950's transposing LDS load instead of a second, transposed copy.
+// main_kernel's roles and periods are described where it is defined below.
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -49,9 +28,9 @@ constexpr int C = 64;                    // tokens per chunk
 constexpr int NB = C / 16;               // 16-token blocks per chunk
 constexpr int NTB = NB * (NB + 1) / 2;   // lower 16x16 blocks of a chunk matrix
 constexpr int TBLK = 256;                // halfs per 16x16 block
-constexpr int NGATE = 3 * C;             // per-chunk gate floats: g, gamma, d
+constexpr int NGATE = 4 * C;             // per-chunk gate floats: g2, gamma, d, w
 constexpr int WS_CHUNK = NTB * TBLK + 2 * NGATE;   // workspace halfs per (head, chunk)
-constexpr float kLogDecayFloor = -30.0f; // exp(-30) ~ 9e-14: alpha = 0 stays finite
+constexpr float kLog2DecayFloor = -43.280851f;   // log2 of e^-30 ~ 9e-14: alpha = 0 stays finite
 constexpr int kXcds = 8;
 constexpr int kStatusBytes = 256;        // workspace header holding the call's device status word
 
@@ -211,8 +190,8 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
 }
 
 // Workspace layout: a kStatusBytes header whose first word is the call's
-// device status (cleared by prep_kernel, set by a wait in main_kernel that
-// gave up), then for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
+// device status (cleared by prep_kernel; main_kernel sets bit 0 when it wrote
+// a non-finite y and bit 1 for a non-finite final state), then for each (b*H + h, chunk), WS_CHUNK halfs: the NTB lower
 // 16x16 blocks of T' in the order (0,0),(1,0),(1,1),(2,0),...,(3,3), each
 // row-major fp16, then the float32 gates g[C], gamma[C], d[C].
 //
@@ -271,7 +250,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
         float lg;
         {
             const float a = (t0 + l < T) ? ar : 1.f, be = (t0 + l < T) ? br : 0.f;
-            lg = wave_scan_incl(fmaxf(logf(a), kLogDecayFloor));
+            lg = wave_scan_incl(fmaxf(__log2f(a), kLog2DecayFloor));
             sm.g[l] = lg;
             sm.beta[l] = be;
         }
@@ -307,7 +286,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
                 float a[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = bt * __expf(gt - gi[e]) * acc[u][e];   // inf above the diagonal: not selected
+                    const float v = bt * __builtin_amdgcn_exp2f(gt - gi[e]) * acc[u][e];   // inf above the diagonal: not selected
                     a[e] = (I > J || col0 + e < row) ? v : 0.f;
                 }
                 if (I == J)
@@ -396,13 +375,19 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
             const int idx = l + it * 64;
             *reinterpret_cast<half8*>(dst + 8 * idx) = *reinterpret_cast<const half8*>(&sm.Tr[8 * idx]);
         }
-        // gates for the chunk walk: g, gamma = exp(g), d = exp(g_last - g)
+        // gates for the chunk walk, all in base 2: g2, gamma = 2^g2,
+        // d = 2^(g2_last - g2) and w = 2^(g2_b - g2), where g2_b is the value
+        // at the end of the token's 16-token block (the column factor of the
+        // off-diagonal decay blocks of P, which are then u_t w_i with
+        // u_t = 2^(g2_t - g2_b) <= 1 and w_i <= 1)
         {
             const float glast = __shfl(lg, 63, 64);
+            const float gblk = __shfl(lg, l | 15, 64);
             float* gate = reinterpret_cast<float*>(dst + NTB * TBLK);
             gate[l] = lg;
-            gate[C + l] = expf(lg);
-            gate[2 * C + l] = expf(glast - lg);
+            gate[C + l] = __builtin_amdgcn_exp2f(lg);
+            gate[2 * C + l] = __builtin_amdgcn_exp2f(glast - lg);
+            gate[3 * C + l] = __builtin_amdgcn_exp2f(gblk - lg);
         }
         prep_wave_sync();   // the staging area is rewritten by the next chunk
     }
@@ -411,41 +396,88 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
 // ===========================================================================
 // main_kernel: the sequential chunk walk for one (head, 16-column slice).
 // ===========================================================================
+//
+// One workgroup of 8 waves per (sequence b, head h, 16 value columns); wave w
+// runs on SIMD w % 4.  The walk is cut into periods that end at a workgroup
+// barrier.  In period p:
+//   wave 0 (state)      chunk p: K S, R = V - gamma K S, E = T' R (written to
+//                       ET[p & 1]), S <- gamma_last S + K^T D E, and the fp16
+//                       copy of the new state to ST[(p + 1) & 1];
+//   waves 1, 5, 2, 6    (output, one per 16-token block 3, 0, 2, 1): gamma (Q S)
+//                       and P of chunk p from S_p (ST[p & 1]), K_p and their own
+//                       q rows, which they load from memory two periods ahead;
+//                       then y of chunk p - 1 = gamma (Q S) + P E from the
+//                       gamma Q S and P of chunk p - 1 kept in registers and
+//                       E_{p-1} from ET[(p - 1) & 1];
+//   wave 3 (misc)       v slice, T' and gates of chunk p + 1 into LDS;
+//   waves 4 and 7 (k)   k of chunk p + 1 into LDS (bf16 -> fp16).
+// Nothing a period reads is written in the same period, so no role waits on
+// another between barriers.  Loaders and the output waves' q loads run two
+// chunks ahead in two register sets (chunk c in set c & 1).
+//
+// Memory access goes through buffer descriptors whose base moves by whole
+// chunks in scalar registers: each lane's offsets are computed once, and
+// rows past the end of the sequence read as zeros and are not written (the
+// descriptor's size ends at token T).  Zero rows past the end are harmless:
+// there beta = 0 and alpha = 1 (prep_kernel), so T' has zero rows and columns
+// for them, they reach neither E nor the state, and their y is not stored.
+//
+// Split-K operand layout: for a 16x16x32 MFMA, slot s of lane (m + 16 g) holds
+// K-index 16*(s/4) + 4 g + s%4 of its row/column.  Two 16x16 accumulator tiles
+// (lane (n + 16 g) holds rows 4 g .. 4 g + 3 of column n) stacked along K are
+// exactly such a B operand, and A operands are read from LDS in the same order.
+// LDS tiles are fp16 row-major with 16-byte chunks XOR-swizzled by row; the
+// operands that need a tile transposed (K^T, and V in accumulator order) are
+// read with gfx950's transposing LDS load instead of a second, transposed copy.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes) (raw, stride 0): loads past the
+// end return zeros, stores past the end are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
+    const long b = bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(b),
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, int voff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, int voff, float4v v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 0);
+}
+
 template <int DK>
 struct MainCfg {
     static constexpr int SV = 16;                  // value columns per workgroup
     static constexpr int NT = 512;                 // 8 waves
-    // Waves w and w + 4 share a SIMD.  The state wave (0) shares its SIMD with
-    // the lightest role, the misc loader (4); the q/k loaders are waves 3, 5,
-    // 6 and 7.
-    static constexpr int W_STATE = 0, W_OUT0 = 1;  // state wave, output waves 1 and 2
-    static constexpr int W_MISC = 4;               // v, T' and gates loader
-    static constexpr int NQKW = 4;                 // q and k loader waves
-    static constexpr int LQK = NQKW * 64;          // q/k loader threads
+    // roles: state 0; output waves 1, 5 (blocks 3, 0; SIMD 1) and 2, 6 (blocks 2, 1; SIMD 2)
+    static constexpr int W_STATE = 0, W_MISC = 3, W_K0 = 4, W_K1 = 7;
     static constexpr int QC = DK / 8;              // 16-byte pieces per q/k row
-    static constexpr int NQ = (64 * QC + LQK - 1) / LQK;   // k (and q) pieces per thread
-    static constexpr int NVI = 64 * (SV / 8) / 64;         // v pieces per misc lane
+    static constexpr int KPL = C * QC / 64;        // k pieces per lane-slot and chunk
+    static constexpr int NK0 = KPL * 3 / 8;        // ... on wave 4 (SIMD 0, with the state wave)
+    static constexpr int NK1 = KPL - NK0;          // ... on wave 7 (SIMD 3, with the misc wave)
+    static constexpr int NVI = C * (SV / 8) / 64;  // v pieces per misc lane
     static constexpr int NTI = NTB * TBLK / 8 / 64;        // T' pieces per misc lane
     static constexpr int NGI = (NGATE / 4 + 63) / 64;      // gate pieces per misc lane
     static constexpr int NMI = NVI + NTI + NGI;            // misc pieces per lane
-    static constexpr int NA = 2 * NQ > NMI ? 2 * NQ : NMI;
-    static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1; // 32-wide K steps over d_k
+    static constexpr int KSTEP = DK >= 32 ? DK / 32 : 1;   // 32-wide K steps over d_k
     static constexpr int NST = DK / 16;            // 16-row state tiles
     static_assert(NTB * TBLK / 8 == NTI * 64, "T' pieces fill the misc wave");
     static_assert(NGATE / 4 <= 64 * NGI, "gate pieces fit the misc wave");
+    static_assert(NK0 + NK1 == KPL && NK1 >= 1, "k pieces split over two waves");
 };
 
 template <int DK>
 struct alignas(16) MainSmem {
     using Cfg = MainCfg<DK>;
     _Float16 K[2][C * DK];
-    _Float16 Q[2][C * DK];
     _Float16 Tp[2][C * C];
     _Float16 V[2][C * Cfg::SV];     // v slice, row-major (token, column)
-    _Float16 ST[2][Cfg::SV * DK];   // f16 state slice transposed, by chunk parity
-    _Float16 ET[Cfg::SV * C];       // E of the current chunk, transposed
-    float gate[2][NGATE];           // g, gamma, d of each buffered chunk
-    int flagE;
+    _Float16 ST[2][Cfg::SV * DK];   // fp16 state slice transposed: S_p in ST[p & 1]
+    _Float16 ET[2][Cfg::SV * C];    // E of chunk p, transposed, in ET[p & 1]
+    float gate[2][NGATE];           // g2, gamma, d, w of each buffered chunk
 };
 
 __device__ __forceinline__ half8 bf16x8_to_h8(const uint4& r) {
@@ -459,175 +491,171 @@ __device__ __forceinline__ half8 bf16x8_to_h8(const uint4& r) {
     return o;
 }
 
-template <int DK>
-struct Prefetch {
-    uint4 a[MainCfg<DK>::NA];
-    int chunk;
-};
-
-// Loader pieces are 16 bytes.  q/k waves (MISC = false): a[i] holds k and
-// a[NQ + i] q at (token t, piece cq), with consecutive pieces of one row on
-// consecutive lanes, so a wave's load covers whole rows.  Misc wave: a[0 .. NVI) hold v (token, piece of the
-// slice), then NTI pieces of T' (its 10 lower blocks, in order), then the
-// gate pieces.  Loads are unconditional: tokens past the end read the last
-// token's row and pieces past the gates re-read the last one (always in
-// bounds), so no load sits behind a branch.
-template <int DK, bool MISC>
-__device__ __forceinline__ void loader_load(Prefetch<DK>& pf, int chunk, int lt, int lane, const uint16_t* q,
-                                            const uint16_t* k, const uint16_t* v, const _Float16* ws, long tok0,
-                                            int T, int H, int DV, int col0, int h, long wsbase) {
-    using Cfg = MainCfg<DK>;
-    const int t0 = chunk * C;
-    pf.chunk = chunk;
-    auto row = [&](int t) { return (tok0 + min(t0 + t, T - 1)) * H + h; };
-    if constexpr (!MISC) {
-#pragma unroll
-        for (int i = 0; i < Cfg::NQ; ++i) {
-            const int idx = min(lt + i * Cfg::LQK, 64 * Cfg::QC - 1);
-            const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
-            pf.a[i] = *reinterpret_cast<const uint4*>(k + row(t) * DK + cq * 8);
-            pf.a[Cfg::NQ + i] = *reinterpret_cast<const uint4*>(q + row(t) * DK + cq * 8);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < Cfg::NVI; ++i) {
-            const int idx = lane + i * 64;
-            const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
-            pf.a[i] = *reinterpret_cast<const uint4*>(v + row(t) * DV + col0 + cv * 8);
-        }
-        const uint4* src = reinterpret_cast<const uint4*>(ws + wsbase + static_cast<long>(chunk) * WS_CHUNK);
-#pragma unroll
-        for (int i = 0; i < Cfg::NTI + Cfg::NGI; ++i)
-            pf.a[Cfg::NVI + i] = src[min(lane + i * 64, WS_CHUNK / 8 - 1)];
-    }
-}
-
-// bf16 pieces (q, k, v) -> fp16 pieces in place; T' and gate pieces are
-// stored as they are.  Rows past the end of the sequence hold a copy of the
-// last row and need no zeroing: there beta = 0 and alpha = 1 (set by
-// prep_kernel), so T' has zero rows and columns for them and they reach
-// neither E nor the state, and their y rows are never stored.
-// The empty asm pins every converted piece to this point, so that the
-// conversion is not sunk next to the stores.
-template <int DK, bool MISC>
-__device__ __forceinline__ void loader_convert(Prefetch<DK>& pf) {
-    using Cfg = MainCfg<DK>;
-    constexpr int N = MISC ? Cfg::NVI : 2 * Cfg::NQ;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const half8 hv = bf16x8_to_h8(pf.a[i]);
-        pf.a[i] = *reinterpret_cast<const uint4*>(&hv);
-        asm volatile("" : "+v"(pf.a[i].x), "+v"(pf.a[i].y), "+v"(pf.a[i].z), "+v"(pf.a[i].w));
-    }
-}
-
 // 16-byte LDS store (half8 carries the 16-byte alignment that the uint4 type
 // lacks, so this is one ds_write_b128 rather than two 8-byte writes).
+__device__ __forceinline__ void st16(void* dst, const half8& v) { *reinterpret_cast<half8*>(dst) = v; }
 __device__ __forceinline__ void st16(void* dst, const uint4& v) {
     *reinterpret_cast<half8*>(dst) = *reinterpret_cast<const half8*>(&v);
 }
 
-template <int DK, bool MISC, int buf>
-__device__ __forceinline__ void loader_store(const Prefetch<DK>& pf, MainSmem<DK>& sm, int lt, int lane) {
-    using Cfg = MainCfg<DK>;
-    if constexpr (!MISC) {
-#pragma unroll
-        for (int i = 0; i < Cfg::NQ; ++i) {
-            const int idx = lt + i * Cfg::LQK;
-            if (idx < 64 * Cfg::QC) {
-                const int t = idx / Cfg::QC, cq = idx % Cfg::QC;
-                st16(&sm.K[buf][swz<DK>(t, cq * 8)], pf.a[i]);
-                st16(&sm.Q[buf][swz<DK>(t, cq * 8)], pf.a[Cfg::NQ + i]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < Cfg::NVI; ++i) {
-            const int idx = lane + i * 64;
-            const int t = idx / (Cfg::SV / 8), cv = idx % (Cfg::SV / 8);
-            st16(&sm.V[buf][t * Cfg::SV + cv * 8], pf.a[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < Cfg::NTI; ++i) {
-            const int idx = lane + i * 64;
-            const int blk = idx / 32, r = (idx % 32) / 2, hh = idx % 2;
-            const int I = lower_block_row(blk), J = blk - I * (I + 1) / 2;
-            st16(&sm.Tp[buf][swz<C>(I * 16 + r, J * 16 + 8 * hh)], pf.a[Cfg::NVI + i]);
-        }
-#pragma unroll
-        for (int i = 0; i < Cfg::NGI; ++i) {
-            const int idx = lane + i * 64;
-            if (idx < NGATE / 4)
-                st16(&sm.gate[buf][4 * idx], pf.a[Cfg::NVI + Cfg::NTI + i]);
-        }
-    }
+// Per-walk constants every role needs.  The q, k, v and y pointers are those
+// of token 0, head 0 of this sequence: a chunk's descriptor starts at its first
+// token and ends at token T of the sequence, and the lane offsets add the head
+// (and slice) column, so no access leaves the sequence's rows.
+struct Walk {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const _Float16* ws;  // this head's first chunk in the workspace
+    float* y;
+    long rowq;           // elements between consecutive tokens of q / k (H * DK)
+    long rowv;           // ... of v and y (H * DV)
+    unsigned hq;         // element offset of this head in a q / k row (h * DK)
+    unsigned hv;         // ... of this head's slice in a v / y row (h * DV + col0)
+    int T, nchunks;
+    float scale;
+    unsigned* status;    // the call's status word
+};
+
+// Sets `bit` of the call's status word when any lane of the wave saw a
+// non-finite value (an input or intermediate outside the fp16 operand range,
+// or non-finite inputs).
+__device__ __forceinline__ void report_nonfinite(unsigned* status, bool bad, unsigned bit) {
+    if (__any(bad) && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool nonfinite(float4v v) {
+    return !(__builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) && __builtin_isfinite(v[2]) &&
+             __builtin_isfinite(v[3]));
 }
 
-// Wait until the state wave has published E of `chunk`.  Bounded by `spin`
-// sleeps, so that a missing flag ends the wait instead of hanging the device;
-// returns false when it gave up (the caller then reports it, see DevStatus).
-template <int DK>
-__device__ __forceinline__ bool wait_published(MainSmem<DK>& sm, int chunk, int spin) {
-    if (spin <= 0) return false;   // a bound of 0 gives up at once (tests of the failure path)
-    for (int it = 0; __hip_atomic_load(&sm.flagE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= chunk; ++it) {
-        if (it >= spin) return false;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return true;
+// End of a period.  The scheduling barriers keep the compiler from moving
+// work across it: left alone it hoists the next period's bf16 -> fp16
+// conversions above the barrier, which makes the loaders wait for their
+// newest loads as well.
+__device__ __forceinline__ void period_end() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
-// A wait that gave up sets bit 0 of the call's status word (read back by
-// gdn_prefill_status) and poisons the rows it would have written with NaN.
-struct DevStatus {
-    unsigned* word;
-    int spin;
-    __device__ __forceinline__ void fail() const {
-        if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------------------
+// Loader roles.  Chunk c's pieces live in register set c & 1.
+// ---------------------------------------------------------------------------
+template <int DK, int N>
+struct Pieces {
+    uint4 a[2][N];
+};
+
+// k loader: lane-slot ls (0 .. 63) of wave with `first` piece index; pieces
+// i = first + j * 64 + ls cover whole rows (16 consecutive pieces per row at
+// d_k = 128), so a wave's load is a run of contiguous rows.
+template <int DK, int N>
+struct KLoader {
+    int voff[N];     // byte offset of each piece from the chunk's first k row
+    int loff[N];     // its swizzled LDS offset (halfs)
+    __device__ void init(int first, int ls, const Walk& w) {
+        using Cfg = MainCfg<DK>;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = first + j * 64 + ls;
+            const int t = i / Cfg::QC, cq = i % Cfg::QC;
+            voff[j] = static_cast<int>((static_cast<unsigned>(t) * static_cast<unsigned>(w.rowq) + w.hq + cq * 8u) * 2u);
+            loff[j] = swz<DK>(t, cq * 8);
+        }
+    }
+    template <int set>
+    __device__ void load(Pieces<DK, N>& p, const Walk& w, int chunk) const {
+        const long t0 = static_cast<long>(chunk) * C;
+        const rsrc_t r = make_rsrc(w.k + t0 * w.rowq, (w.T - t0) * w.rowq * 2);
+#pragma unroll
+        for (int j = 0; j < N; ++j) p.a[set][j] = bload16(r, voff[j]);
+    }
+    template <int set, int buf>
+    __device__ void store(const Pieces<DK, N>& p, MainSmem<DK>& sm) const {
+#pragma unroll
+        for (int j = 0; j < N; ++j) st16(&sm.K[buf][loff[j]], bf16x8_to_h8(p.a[set][j]));
     }
 };
 
-// Loader role: during chunk c the loads of chunk c+2 are issued into one
-// register set and chunk c+1 (loaded during chunk c-1, in the other set) is
-// converted and stored to the other LDS buffer.  One barrier after the
-// prologue and one per chunk, as in the other roles.
-template <int DK, bool MISC>
-__device__ __forceinline__ void loader_role(MainSmem<DK>& sm, int nchunks, int lt, int lane, const uint16_t* q,
-                                            const uint16_t* k,
-                                            const uint16_t* v, const _Float16* ws, long tok0, int T, int H,
-                                            int DV, int col0, int h, long wsbase) {
-    Prefetch<DK> pa, pb;
-    auto ld = [&](Prefetch<DK>& pf, int c) {
-        loader_load<DK, MISC>(pf, min(c, nchunks - 1), lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
-    };
-    // chunk c goes to LDS buffer c & 1 (a compile-time constant at each call)
-    auto put = [&](Prefetch<DK>& pf, auto buf) { loader_store<DK, MISC, decltype(buf)::value>(pf, sm, lt, lane); };
-    const std::integral_constant<int, 0> even{};
-    const std::integral_constant<int, 1> odd{};
-    if (nchunks > 0) {
-        ld(pa, 0);
-        loader_convert<DK, MISC>(pa);
-        put(pa, even);
-        ld(pa, 1);
+// misc loader: v slice (converted), T' blocks and gates (fp16 / fp32 as stored).
+template <int DK>
+struct MiscLoader {
+    using Cfg = MainCfg<DK>;
+    int voff[Cfg::NVI], loff_v[Cfg::NVI], loff_t[Cfg::NTI];
+    int lane;
+    __device__ void init(int l, const Walk& w) {
+        lane = l;
+#pragma unroll
+        for (int j = 0; j < Cfg::NVI; ++j) {
+            const int i = l + j * 64, t = i / (Cfg::SV / 8), cv = i % (Cfg::SV / 8);
+            voff[j] = static_cast<int>((static_cast<unsigned>(t) * static_cast<unsigned>(w.rowv) + w.hv + cv * 8u) * 2u);
+            loff_v[j] = t * Cfg::SV + cv * 8;
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::NTI; ++j) {
+            const int i = l + j * 64, blk = i / 32, r = (i % 32) / 2, hh = i % 2;
+            const int I = lower_block_row(blk), J = blk - I * (I + 1) / 2;
+            loff_t[j] = swz<C>(I * 16 + r, J * 16 + 8 * hh);
+        }
     }
-    __syncthreads();
-    // Chunk pairs in an unconditional body (exact wait counts), odd tail after.
-    // Loads past the last chunk re-read it (clamped).  When c + 2 == nchunks
-    // the second store writes that copy into the buffer of chunk c, which
-    // nothing reads any more (chunk c + 1 is the last).
-    int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
-        ld(pb, c + 2);
-        loader_convert<DK, MISC>(pa);
-        put(pa, odd);    // chunk c + 1
-        __syncthreads();
-        ld(pa, c + 3);
-        loader_convert<DK, MISC>(pb);
-        put(pb, even);   // chunk c + 2
-        __syncthreads();
+    template <int set>
+    __device__ void load(Pieces<DK, Cfg::NMI>& p, const Walk& w, int chunk) const {
+        const long t0 = static_cast<long>(chunk) * C;
+        const rsrc_t rv = make_rsrc(w.v + t0 * w.rowv, (w.T - t0) * w.rowv * 2);
+#pragma unroll
+        for (int j = 0; j < Cfg::NVI; ++j) p.a[set][j] = bload16(rv, voff[j]);
+        const bool live = chunk < w.nchunks;
+        const rsrc_t rw = make_rsrc(w.ws + static_cast<long>(chunk) * WS_CHUNK, live ? WS_CHUNK * 2 : 0);
+#pragma unroll
+        for (int j = 0; j < Cfg::NTI + Cfg::NGI; ++j) p.a[set][Cfg::NVI + j] = bload16(rw, (lane + j * 64) * 16);
     }
-    if (c < nchunks) __syncthreads();
+    template <int set, int buf>
+    __device__ void store(const Pieces<DK, Cfg::NMI>& p, MainSmem<DK>& sm) const {
+#pragma unroll
+        for (int j = 0; j < Cfg::NVI; ++j) st16(&sm.V[buf][loff_v[j]], bf16x8_to_h8(p.a[set][j]));
+#pragma unroll
+        for (int j = 0; j < Cfg::NTI; ++j) st16(&sm.Tp[buf][loff_t[j]], p.a[set][Cfg::NVI + j]);
+#pragma unroll
+        for (int j = 0; j < Cfg::NGI; ++j) {
+            const int i = lane + j * 64;
+            if (i < NGATE / 4) st16(&sm.gate[buf][4 * i], p.a[set][Cfg::NVI + Cfg::NTI + j]);
+        }
+    }
+};
+
+// Loader role: prologue stores chunk 0 and has chunks 1 and 2 in flight; in
+// period p it stores chunk p + 1 (buffer (p + 1) & 1, register set
+// (p + 1) & 1) and then loads chunk p + 3 into the set it just emptied.
+// The period bodies are unconditional, so that the compiler's wait counts
+// stay exact across the loop (a load skipped on some path would make it wait
+// for the newest loads too, exposing their latency every period): loads past
+// the last chunk read zeros (the descriptors' sizes end at T) and the stores
+// past it fill a buffer that nothing reads any more.
+template <int DK, class L, class P>
+__device__ __forceinline__ void loader_role(const L& ld, P& pcs, MainSmem<DK>& sm, const Walk& w) {
+    const int n = w.nchunks;
+    ld.template load<0>(pcs, w, 0);
+    ld.template load<1>(pcs, w, 1);
+    ld.template store<0, 0>(pcs, sm);
+    ld.template load<0>(pcs, w, 2);
+    period_end();
+    // n + 1 periods, in pairs: p even stores set 1 -> buffer 1, p odd set 0 -> buffer 0
+    int p = 0;
+    for (; p + 1 <= n; p += 2) {
+        ld.template store<1, 1>(pcs, sm);
+        ld.template load<1>(pcs, w, p + 3);
+        period_end();
+        ld.template store<0, 0>(pcs, sm);
+        ld.template load<0>(pcs, w, p + 4);
+        period_end();
+    }
+    if (p <= n) period_end();
 }
 
+// ---------------------------------------------------------------------------
+// State role.
+// ---------------------------------------------------------------------------
 template <int DK>
 struct StateRegs {
     float4v S[MainCfg<DK>::NST];     // float32 state slice, accumulator layout
@@ -643,13 +671,21 @@ __device__ __forceinline__ void state_refresh_operand(StateRegs<DK>& st) {
     }
 }
 
-// One chunk of the state chain (state wave), software-pipelined by hand: each
-// group of MFMAs finds its operand fragments already in registers because
-// their LDS reads were issued one group earlier.  Scheduling barriers keep the
-// compiler from sinking the reads back next to their uses (it would otherwise
-// wait on every read).
+// The fp16 state slice, transposed, for the output waves: ST[lr][16 r + 4 lq + j].
+template <int DK>
+__device__ __forceinline__ void state_publish(const StateRegs<DK>& st, _Float16* STb, int lane) {
+    const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < MainCfg<DK>::NST; ++r)
+        *reinterpret_cast<half4*>(&STb[swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
+}
+
+// One chunk of the state chain, software-pipelined by hand: each group of
+// MFMAs finds its operand fragments already in registers because their LDS
+// reads were issued one group earlier.  Scheduling barriers keep the compiler
+// from sinking the reads back next to their uses.
 template <int DK, int buf>
-__device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int chunk, int lane) {
+__device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int lane) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
     constexpr int NST = Cfg::NST;
@@ -657,6 +693,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
     const _Float16* Tb = sm.Tp[buf];
+    const float* gate = sm.gate[buf];
     auto kfrag = [&](int I, int kk) {
         return DK >= 32 ? ld_split<DK>(Kb, I * 16 + lr, kk * 32, lq) : ld_split_lo<DK>(Kb, I * 16 + lr, 0, lq);
     };
@@ -697,8 +734,8 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     }
     float4v gm[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][C + I * 16 + 4 * lq]);
-    const float gl = sm.gate[buf][C + C - 1];
+    for (int I = 0; I < NB; ++I) gm[I] = *reinterpret_cast<const float4v*>(&gate[C + I * 16 + 4 * lq]);
+    const float gl = gate[C + C - 1];
     __builtin_amdgcn_sched_barrier(0);
     // R = V - gamma K S, as the split-K B operand of T' R
     half4 rh[NB];
@@ -718,10 +755,9 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
 #pragma unroll
     for (int r = 0; r < NST; ++r) st.S[r] *= gl;
     __builtin_amdgcn_sched_barrier(0);
-    // publish E for the output waves before the state update
+    // E for the output waves of the next period
 #pragma unroll
-    for (int I = 0; I < NB; ++I) *reinterpret_cast<half4*>(&sm.ET[swz<C>(lr, I * 16 + 4 * lq)]) = to_h4(e[I]);
-    __hip_atomic_store(&sm.flagE, chunk + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int I = 0; I < NB; ++I) *reinterpret_cast<half4*>(&sm.ET[buf][swz<C>(lr, I * 16 + 4 * lq)]) = to_h4(e[I]);
     // second half of K^T and the decay-to-chunk-end factors, read while T' R runs
     half8 kt1[NH][2];
 #pragma unroll
@@ -733,7 +769,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     }
     float4v dc[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4v*>(&sm.gate[buf][2 * C + I * 16 + 4 * lq]);
+    for (int I = 0; I < NB; ++I) dc[I] = *reinterpret_cast<const float4v*>(&gate[2 * C + I * 16 + 4 * lq]);
     __builtin_amdgcn_sched_barrier(0);
     // D E as the B operand of K^T (D E)
     half4 eh[NB];
@@ -754,133 +790,206 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
             st.S[NH + r] = mma(kt1[r][1], Eb1, st.S[NH + r]);
         }
     }
-    _Float16* STn = sm.ST[buf ^ 1];
-#pragma unroll
-    for (int r = 0; r < NST; ++r) *reinterpret_cast<half4*>(&STn[swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
     state_refresh_operand(st);
+    state_publish<DK>(st, sm.ST[buf ^ 1], lane);
 }
 
-// One chunk of output for output wave RP, which owns token blocks I0 = RP and
-// I1 = 3 - RP (so both waves build five of the ten lower P tiles).  Its q
-// rows, the k rows and the fp16 state slice come from LDS.  Everything is
-// computed transposed (K_J Q_I^T for P, S^T Q^T, E^T P^T), so that each lane
-// holds one token row: P feeds the last MFMA straight from registers in the
-// split-K order, and y leaves as one 16-byte store per lane and block.
-template <int DK, int buf, int RP>
-__device__ __forceinline__ void output_chunk(MainSmem<DK>& sm, int chunk, int lane, float* ylane, long ytok,
-                                             int T, float scale, const DevStatus& ds) {
+template <int DK>
+__device__ __forceinline__ void state_role(MainSmem<DK>& sm, const Walk& w, const float* S0, float* S_out,
+                                           long sbase, int DV, int lane) {
+    using Cfg = MainCfg<DK>;
+    const int lr = lane & 15, lq = lane >> 4;
+    StateRegs<DK> st;
+#pragma unroll
+    for (int r = 0; r < Cfg::NST; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.S[r][j] = S0 ? S0[sbase + static_cast<long>(r * 16 + 4 * lq + j) * DV + lr] : 0.f;
+    state_refresh_operand(st);
+    state_publish<DK>(st, sm.ST[0], lane);
+    period_end();
+    const int n = w.nchunks;
+    int p = 0;
+    for (; p + 1 < n; p += 2) {
+        state_chunk<DK, 0>(sm, st, lane);
+        period_end();
+        state_chunk<DK, 1>(sm, st, lane);
+        period_end();
+    }
+    if (p < n) {
+        state_chunk<DK, 0>(sm, st, lane);
+        period_end();
+        ++p;
+    }
+    period_end();   // the output waves' last period
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < Cfg::NST; ++r) bad |= nonfinite(st.S[r]);
+    report_nonfinite(w.status, bad, 2u);
+    if (S_out) {
+#pragma unroll
+        for (int r = 0; r < Cfg::NST; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S_out[sbase + static_cast<long>(r * 16 + 4 * lq + j) * DV + lr] = st.S[r][j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Output role.  Four waves, one per 16-token block I of the chunk: blocks 3
+// and 0 share SIMD 1, blocks 2 and 1 SIMD 2, so that each SIMD interleaves two
+// independent instruction streams.  Everything is computed transposed
+// (K_J Q_I^T for P, S^T Q^T, E^T P^T), so that each lane holds one token row:
+// P feeds the last MFMA straight from registers in the split-K order, and y
+// leaves as one 16-byte store per lane.
+// ---------------------------------------------------------------------------
+template <int DK>
+struct OutRegs {
+    static constexpr int KS = MainCfg<DK>::KSTEP;
+    uint4 qraw[2][KS];      // bf16 q of chunk c in set c & 1 (this wave's block)
+    half8 qh[KS];           // fp16 q of the current chunk
+    half8 Pb[2][2];         // P of chunk c in set c & 1, B operand of E^T P^T
+    float4v qsg[2];         // gamma (Q S)^T of chunk c in set c & 1
+    int qoff;               // byte offset of the lane's q piece in a chunk
+    int yoff;               // byte offset of the lane's y piece in a chunk
+    bool bad;               // a non-finite y was written
+};
+
+template <int DK, int set>
+__device__ __forceinline__ void out_load_q(OutRegs<DK>& o, const Walk& w, int chunk) {
+    constexpr int KS = MainCfg<DK>::KSTEP;
+    const long t0 = static_cast<long>(chunk) * C;
+    const rsrc_t r = make_rsrc(w.q + t0 * w.rowq, (w.T - t0) * w.rowq * 2);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) o.qraw[set][kk] = bload16(r, o.qoff + kk * 64);
+}
+
+// Period work of the output wave of block I.  Everything runs unconditionally
+// (exact wait counts across the loop).  Order: the q conversion first
+// (registers only, while the LDS traffic of the period start drains), then
+// gamma Q S and P of chunk c (in the last period, c = nchunks, of stale
+// buffers and zero q: computed and never used), then y of chunk c - 1 from the
+// P and gamma Q S kept in the other set, then the q loads of chunk c + 2.
+template <int DK, int I, int buf>
+__device__ __forceinline__ void output_period(MainSmem<DK>& sm, OutRegs<DK>& o, const Walk& w, int c, int lane) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
-    constexpr int Irow[2] = {RP, 3 - RP};
-    constexpr int Jmax = 3 - RP;   // highest k block either q block needs
     const int lr = lane & 15, lq = lane >> 4;
+    constexpr int cs = buf;   // chunk c lives in set c & 1 == buf
+    // q of chunk c: bf16 -> fp16 (loaded two periods ago)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) o.qh[kk] = (DK >= 32 || lq < 2) ? bf16x8_to_h8(o.qraw[cs][kk]) : half8{};
     const _Float16* Kb = sm.K[buf];
-    const _Float16* Qb = sm.Q[buf];
     const _Float16* STb = sm.ST[buf];
+    const float* gate = sm.gate[buf];
     // contiguous K-slices: lane (r + 16 g) holds K-index 8 g .. 8 g + 7 of step
     // kk (for d_k = 16 only g < 2 carry data; the rest are zero)
     auto frag = [&](const _Float16* base, int row, int kk) {
         return (DK >= 32 || lq < 2) ? ld8<DK>(base, row, kk * 32 + 8 * lq) : half8{};
     };
-    half8 sf[KS], qf[2][KS], kf[2][KS];
+    half8 sf[KS], kf[2][KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         sf[kk] = frag(STb, lr, kk);
-        qf[0][kk] = frag(Qb, Irow[0] * 16 + lr, kk);
-        qf[1][kk] = frag(Qb, Irow[1] * 16 + lr, kk);
         kf[0][kk] = frag(Kb, lr, kk);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // (Q S)^T = S^T Q^T for both blocks: lane (t + 16 g) gets columns 4 g .. 4 g + 3 of row t
-    float4v qs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        qs[0] = mma(sf[kk], qf[0][kk], qs[0]);
-        qs[1] = mma(sf[kk], qf[1][kk], qs[1]);
-    }
+    // (Q S)^T = S^T Q^T, interleaved with the first P tile: lane (t + 16 g)
+    // gets columns 4 g .. 4 g + 3 of row t
+    float4v qs = {0.f, 0.f, 0.f, 0.f};
     // (Q K^T)^T tiles J <= I: k block J is read once, one block ahead of its MFMAs
-    float4v pacc[2][NB];
+    float4v pacc[NB];
 #pragma unroll
-    for (int J = 0; J <= Jmax; ++J) {
-        if (J + 1 <= Jmax) {
+    for (int J = 0; J <= I; ++J) {
+        if (J + 1 <= I) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) kf[(J + 1) & 1][kk] = frag(Kb, (J + 1) * 16 + lr, kk);
         }
         __builtin_amdgcn_sched_barrier(0);
-        pacc[0][J] = pacc[1][J] = float4v{0.f, 0.f, 0.f, 0.f};
+        pacc[J] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            if (J <= Irow[0]) pacc[0][J] = mma(kf[J & 1][kk], qf[0][kk], pacc[0][J]);
-            pacc[1][J] = mma(kf[J & 1][kk], qf[1][kk], pacc[1][J]);
+            if (J == 0) qs = mma(sf[kk], o.qh[kk], qs);
+            pacc[J] = mma(kf[J & 1][kk], o.qh[kk], pacc[J]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     // P = Gamma o (Q K^T) on the lower tiles, lane row t = 16 I + lr, columns
-    // i = 16 J + 4 lq + j; only the diagonal tile needs the i <= t mask (the
-    // exponentials of its masked entries may overflow; the select drops them).
-    float4v gi4[NB];
-#pragma unroll
-    for (int J = 0; J <= Jmax; ++J) gi4[J] = *reinterpret_cast<const float4v*>(&sm.gate[buf][J * 16 + 4 * lq]);
-    half8 Pb[2][2];
-    float gam_t[2];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const int I = Irow[ii];
+    // i = 16 J + 4 lq + j.  Below the diagonal block the decay factors as
+    // 2^(g2_t - g2_b) w_i (g2_b: end of block J), one power per lane and tile;
+    // the diagonal tile takes 2^(g2_t - g2_i) per entry with i <= t (the
+    // powers of masked entries may overflow; the select drops them).
+    {
         const int t = I * 16 + lr;
-        const float gt = sm.gate[buf][t];
-        gam_t[ii] = sm.gate[buf][C + t];
+        const float gt = gate[t];
+        o.qsg[cs] = qs * gate[C + t];
         half4 ph[NB];
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
             if (J > I) {
                 ph[J] = half4{};
-                continue;
-            }
-            float p[4] = {__expf(gt - gi4[J][0]) * pacc[ii][J][0], __expf(gt - gi4[J][1]) * pacc[ii][J][1],
-                          __expf(gt - gi4[J][2]) * pacc[ii][J][2], __expf(gt - gi4[J][3]) * pacc[ii][J][3]};
-            if (J == I) {
+            } else if (J < I) {
+                const float4v wi = *reinterpret_cast<const float4v*>(&gate[3 * C + J * 16 + 4 * lq]);
+                const float u = __builtin_amdgcn_exp2f(gt - gate[J * 16 + 15]);
+                ph[J] = to_h4((u * wi) * pacc[J]);
+            } else {
+                const float4v gi = *reinterpret_cast<const float4v*>(&gate[J * 16 + 4 * lq]);
+                float pe[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] = (4 * lq + j <= lr) ? p[j] : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const float v = __builtin_amdgcn_exp2f(gt - gi[j]) * pacc[J][j];
+                    pe[j] = (4 * lq + j <= lr) ? v : 0.f;
+                }
+                ph[J] = to_h4(pe[0], pe[1], pe[2], pe[3]);
             }
-            ph[J] = to_h4(p[0], p[1], p[2], p[3]);
         }
-        Pb[ii][0] = cat(ph[0], ph[1]);
-        Pb[ii][1] = cat(ph[2], ph[3]);
+        o.Pb[cs][0] = cat(ph[0], ph[1]);
+        o.Pb[cs][1] = cat(ph[2], ph[3]);
     }
-    const bool published = wait_published(sm, chunk, ds.spin);
-    if (!published) ds.fail();
-    const float ysc = published ? scale : __builtin_nanf("");
-    // Y^T = E^T P^T + gamma (Q S)^T: lane (t + 16 g) holds row t, columns 4 g .. 4 g + 3
-    const half8 Ea0 = ld_split<C>(sm.ET, lr, 0, lq), Ea1 = ld_split<C>(sm.ET, lr, 32, lq);
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-        const int I = Irow[ii];
-        float4v yv = {gam_t[ii] * qs[ii][0], gam_t[ii] * qs[ii][1], gam_t[ii] * qs[ii][2], gam_t[ii] * qs[ii][3]};
-        yv = mma(Ea0, Pb[ii][0], yv);
-        if (I >= 2) yv = mma(Ea1, Pb[ii][1], yv);
-        const int t = chunk * C + I * 16 + lr;
+    __builtin_amdgcn_sched_barrier(0);
+    // y of chunk c - 1:  Y^T = E^T P^T + gamma (Q S)^T.  At c = 0 the
+    // descriptor has size 0 and the stores are dropped.
+    {
+        constexpr int ps = cs ^ 1;
+        const _Float16* ETp = sm.ET[buf ^ 1];
+        const long t0 = static_cast<long>(c - 1) * C;
+        const rsrc_t ry = make_rsrc(w.y + t0 * w.rowv, c > 0 ? (w.T - t0) * w.rowv * 4 : 0);
+        float4v yv = mma(ld_split<C>(ETp, lr, 0, lq), o.Pb[ps][0], o.qsg[ps]);
+        if constexpr (I >= 2) yv = mma(ld_split<C>(ETp, lr, 32, lq), o.Pb[ps][1], yv);
+        yv = yv * w.scale;
+        // rows past T and the dropped c = 0 rows do not count
+        const int t = static_cast<int>(t0) + I * 16 + lr;
+        o.bad |= (c > 0 && t < w.T) && nonfinite(yv);
         // a plain store: the slices of a head write 64-byte pieces of each y
-        // row, which merge in L2 (streaming stores measured 28% more HBM writes)
-        if (t < T)
-            *reinterpret_cast<float4v*>(ylane + t * ytok) =
-                float4v{ysc * yv[0], ysc * yv[1], ysc * yv[2], ysc * yv[3]};
+        // row, which merge in L2
+        bstore16(ry, o.yoff, yv);
     }
+    // q of chunk c + 2 into the set chunk c used
+    out_load_q<DK, cs>(o, w, c + 2);
 }
 
-// Output role: one barrier after the prologue and one per chunk.  ylane
-// points at this lane's four y columns of token 0; ytok is the token stride.
-template <int DK, int RP>
-__device__ __forceinline__ void output_role(MainSmem<DK>& sm, int nchunks, int lane, float* ylane, long ytok, int T,
-                                            float scale, const DevStatus& ds) {
-    __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-        output_chunk<DK, 0, RP>(sm, c, lane, ylane, ytok, T, scale, ds);
-        __syncthreads();
-        if (c + 1 < nchunks) {
-            output_chunk<DK, 1, RP>(sm, c + 1, lane, ylane, ytok, T, scale, ds);
-            __syncthreads();
-        }
+template <int DK, int I>
+__device__ __forceinline__ void output_role(MainSmem<DK>& sm, const Walk& w, int lane) {
+    const int lr = lane & 15, lq = lane >> 4;
+    OutRegs<DK> o;
+    const unsigned t = I * 16 + lr;
+    o.qoff = static_cast<int>((t * static_cast<unsigned>(w.rowq) + w.hq + 8u * lq) * 2u);
+    o.yoff = static_cast<int>((t * static_cast<unsigned>(w.rowv) + w.hv + 4u * lq) * 4u);
+    o.bad = false;
+    out_load_q<DK, 0>(o, w, 0);
+    out_load_q<DK, 1>(o, w, 1);
+    period_end();
+    const int n = w.nchunks;
+    int p = 0;
+    for (; p + 1 <= n; p += 2) {
+        output_period<DK, I, 0>(sm, o, w, p, lane);
+        period_end();
+        output_period<DK, I, 1>(sm, o, w, p + 1, lane);
+        period_end();
     }
+    if (p <= n) {
+        output_period<DK, I, 0>(sm, o, w, p, lane);
+        period_end();
+    }
+    report_nonfinite(w.status, o.bad, 1u);
 }
 
 template <int DK>
@@ -888,11 +997,10 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ v, const _Float16* __restrict__ ws,
                                                    const float* __restrict__ S0, float* __restrict__ S_out,
                                                    float* __restrict__ y, int B, int T, int H, int DV, int nsl,
-                                                   float scale, DevStatus ds) {
+                                                   float scale, unsigned* status) {
     using Cfg = MainCfg<DK>;
     __shared__ MainSmem<DK> sm;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15, lq = lane >> 4;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     // block -> (head, slice): the slices of a head share block ids modulo kXcds
     const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
     const int bh = (jx / nsl) * kXcds + xcd;
@@ -901,58 +1009,56 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     const int b = bh / H, h = bh % H;
     const int col0 = slice * Cfg::SV;
     const long tok0 = static_cast<long>(b) * T;
-    const int nchunks = (T + C - 1) / C;
-    const long wsbase = static_cast<long>(bh) * nchunks * WS_CHUNK;
-
-    const bool is_state = (w == Cfg::W_STATE);
-    const bool is_out = (w >= Cfg::W_OUT0 && w < Cfg::W_OUT0 + 2);
-    const bool misc = (w == Cfg::W_MISC);
-    const int lt = (w == 3 ? 0 : w - 4) * 64 + lane;   // q/k loader thread index (waves 3, 5, 6, 7)
+    Walk w;
+    w.rowq = static_cast<long>(H) * DK;
+    w.rowv = static_cast<long>(H) * DV;
+    w.q = q + tok0 * w.rowq;
+    w.k = k + tok0 * w.rowq;
+    w.v = v + tok0 * w.rowv;
+    w.y = y + tok0 * w.rowv;
+    w.hq = static_cast<unsigned>(h * DK);
+    w.hv = static_cast<unsigned>(h * DV + col0);
+    w.T = T;
+    w.nchunks = (T + C - 1) / C;
+    w.ws = ws + static_cast<long>(bh) * w.nchunks * WS_CHUNK;
+    w.scale = scale;
+    w.status = status;
 
     // T' is zero above its diagonal blocks; those halves of both buffers are never written again
     for (int idx = tid; idx < 2 * C * C; idx += Cfg::NT) (&sm.Tp[0][0])[idx] = static_cast<_Float16>(0.f);
-    if (tid == 0) sm.flagE = 0;
     __syncthreads();
 
     // Each role runs its own loop with the same barrier sequence: one barrier
-    // after the prologue and one after every chunk.  Keeping the roles in
-    // separate loops keeps their registers from being live at the same time.
-    if (is_state) {
-        StateRegs<DK> st;
-#pragma unroll
-        for (int r = 0; r < Cfg::NST; ++r) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                st.S[r][j] = S0 ? S0[(static_cast<long>(bh) * DK + r * 16 + 4 * lq + j) * DV + col0 + lr] : 0.f;
-            *reinterpret_cast<half4*>(&sm.ST[0][swz<DK>(lr, r * 16 + 4 * lq)]) = to_h4(st.S[r]);
-        }
-        state_refresh_operand(st);
-        __syncthreads();
-        // chunk pairs, so that each chunk's LDS buffer is a compile-time constant
-        for (int c = 0; c < nchunks; c += 2) {
-            state_chunk<DK, 0>(sm, st, c, lane);
-            __syncthreads();
-            if (c + 1 < nchunks) {
-                state_chunk<DK, 1>(sm, st, c + 1, lane);
-                __syncthreads();
-            }
-        }
-        if (S_out) {
-#pragma unroll
-            for (int r = 0; r < Cfg::NST; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S_out[(static_cast<long>(bh) * DK + r * 16 + 4 * lq + j) * DV + col0 + lr] = st.S[r][j];
-        }
-    } else if (is_out) {
-        float* ylane = y + (tok0 * H + h) * static_cast<long>(DV) + col0 + 4 * lq;
-        const long ytok = static_cast<long>(H) * DV;
-        if (w == Cfg::W_OUT0) output_role<DK, 0>(sm, nchunks, lane, ylane, ytok, T, scale, ds);
-        else output_role<DK, 1>(sm, nchunks, lane, ylane, ytok, T, scale, ds);
-    } else if (misc) {
-        loader_role<DK, true>(sm, nchunks, lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+    // after the prologue and one after every period (nchunks + 1 periods).
+    if (wv == Cfg::W_STATE) {
+        state_role<DK>(sm, w, S0, S_out, static_cast<long>(bh) * DK * DV + col0, DV, lane);
+    } else if (wv == 1) {
+        output_role<DK, 3>(sm, w, lane);
+    } else if (wv == 5) {
+        output_role<DK, 0>(sm, w, lane);
+    } else if (wv == 2) {
+        output_role<DK, 2>(sm, w, lane);
+    } else if (wv == 6) {
+        output_role<DK, 1>(sm, w, lane);
+    } else if (wv == Cfg::W_MISC) {
+        MiscLoader<DK> ld;
+        ld.init(lane, w);
+        Pieces<DK, Cfg::NMI> pcs;
+        loader_role<DK>(ld, pcs, sm, w);
+    } else if (wv == Cfg::W_K0 && Cfg::NK0 > 0) {
+        KLoader<DK, (Cfg::NK0 > 0 ? Cfg::NK0 : 1)> ld;
+        ld.init(0, lane, w);
+        Pieces<DK, (Cfg::NK0 > 0 ? Cfg::NK0 : 1)> pcs;
+        loader_role<DK>(ld, pcs, sm, w);
+    } else if (wv == Cfg::W_K1) {
+        KLoader<DK, Cfg::NK1> ld;
+        ld.init(Cfg::NK0 * 64, lane, w);
+        Pieces<DK, Cfg::NK1> pcs;
+        loader_role<DK>(ld, pcs, sm, w);
     } else {
-        loader_role<DK, false>(sm, nchunks, lt, lane, q, k, v, ws, tok0, T, H, DV, col0, h, wsbase);
+        // idle waves: the same barrier sequence
+        period_end();
+        for (int p = 0; p <= w.nchunks; ++p) period_end();
     }
 }
 
@@ -980,7 +1086,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((main_kernel<DK>), dim3(groups * kXcds * nsl), dim3(Cfg::NT), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), ws, a.initial_state, a.final_state, a.y,
-                       a.B, a.T, a.H, a.dv, nsl, a.scale, DevStatus{status, a.spin_limit});
+                       a.B, a.T, a.H, a.dv, nsl, a.scale, status);
     return hipGetLastError();
 }
 
