@@ -114,8 +114,8 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int d_k, int d_v, gdn_dt
  * allocates nothing.  Arguments, layouts and results are those of
  * gdn_prefill_fwd (the same kernels run); the caller passes every input and
  * output.  Returns GDN_ERR_WORKSPACE when gdn_prefill_workspace_bytes(...) for
- * these sizes exceeds the array (bf16: 256 bytes plus 6,144 bytes per
- * (sequence, head, 64-token chunk), i.e. B * H * ceil(T / 64) up to 21,845),
+ * these sizes exceeds the array (bf16: 256 bytes plus 7,168 bytes per
+ * (sequence, head, 64-token chunk), i.e. B * H * ceil(T / 64) up to 18,724),
  * GDN_ERR_LAUNCH if the array's device address cannot be obtained.  All calls
  * on one GPU share its array, which keeps the last call's contents: calls that
  * can overlap on one GPU (different streams, or host threads) race and must

@@ -88,7 +88,7 @@ def test_workspace_bytes():
     # bf16: a 256-byte status header, then per (sequence, head, 64-token
     # chunk) the 10 lower fp16 16x16 blocks of T' (5120 bytes) and four
     # float32 gate vectors of 64 (1024 bytes)
-    per_chunk = 10 * 256 * 2 + 4 * 64 * 4
+    per_chunk = 6 * 512 * 2 + 4 * 64 * 4
     assert lib.gdn_prefill_workspace_bytes(1, 8, 2, 64, 64, 1) == 256 + 2 * per_chunk
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 1) == 256 + 2 * 3 * 2 * per_chunk
     assert lib.gdn_prefill_workspace_bytes(2, 65, 3, 128, 128, 0) == 0
@@ -107,10 +107,10 @@ def _prefill_noalloc(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, sT=FAKE, y
 def test_prefill_noalloc_rejects_sizes_beyond_its_scratch():
     lib = gdn.load_library()
     limit = 128 << 20
-    # 21845 (sequence, head, chunk) units fit the 128 MiB array, 21846 do not
-    assert lib.gdn_prefill_workspace_bytes(1, 21845 * 64, 1, 128, 128, 1) <= limit
-    assert lib.gdn_prefill_workspace_bytes(1, 21846 * 64, 1, 128, 128, 1) > limit
-    assert _prefill_noalloc(B=1, T=21846 * 64, H=1, dk=128, dv=128) == ERR_WORKSPACE
+    # 18724 (sequence, head, chunk) units fit the 128 MiB array, 18725 do not
+    assert lib.gdn_prefill_workspace_bytes(1, 18724 * 64, 1, 128, 128, 1) <= limit
+    assert lib.gdn_prefill_workspace_bytes(1, 18725 * 64, 1, 128, 128, 1) > limit
+    assert _prefill_noalloc(B=1, T=18725 * 64, H=1, dk=128, dv=128) == ERR_WORKSPACE
     assert _prefill_noalloc(B=4, T=32768, H=32, dk=128, dv=128) == ERR_WORKSPACE
     # argument errors are reported as by gdn_prefill_fwd (checked before anything else)
     assert _prefill_noalloc(dtype=2) == ERR_DTYPE

@@ -48,7 +48,7 @@ def test_noalloc_in_place_state_and_oversize_rejection():
     check("in-place y", host(y), y_ref, TOL["bf16"])
     check("in-place state", host(state), S_ref, TOL["bf16"])
     # one (sequence, head, chunk) unit more than the array holds: refused on the host
-    T_big = 21846 * 64
+    T_big = 18725 * 64
     q = torch.empty((1, T_big, 1, 128), dtype=torch.bfloat16, device="cuda")
     g = torch.empty((1, T_big, 1), device="cuda")
     with pytest.raises(gdn.GdnError) as err:
