@@ -102,6 +102,90 @@ __device__ __forceinline__ float4v mma_sym_n(const float* A, int lda, int r0, co
     return acc;
 }
 
+// The same contractions on fp16 MFMAs, for bf16 inputs: each lane reads the
+// operand values of mma_n's split-K layout from the fp32 LDS tiles, rounds
+// them to fp16, and feeds eight at a time to 16x16x32 MFMAs (a remainder of
+// four to one 16x16x16 MFMA); the k grouping differs from mma_n's but is the
+// same for both operands, so the sum is the same contraction, with fp32
+// accumulation.  One MFMA then covers 32 values of k instead of 4.
+__device__ __forceinline__ float4v mma_h8(const float* a, const float* b, float4v acc) {
+    half8 x, y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = static_cast<_Float16>(a[e]);
+        y[e] = static_cast<_Float16>(b[e]);
+    }
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
+}
+__device__ __forceinline__ float4v mma_h4(const float* a, const float* b, float4v acc) {
+    half4 x, y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = static_cast<_Float16>(a[e]);
+        y[e] = static_cast<_Float16>(b[e]);
+    }
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, acc, 0, 0, 0);
+}
+template <int S>
+__device__ __forceinline__ float4v mma_h_run(const float (&a)[S], const float (&b)[S], float4v acc) {
+#pragma unroll
+    for (int s = 0; s + 8 <= S; s += 8) acc = mma_h8(a + s, b + s, acc);
+    if constexpr (S % 8 == 4) acc = mma_h4(a + S - 4, b + S - 4, acc);
+    return acc;
+}
+template <bool kAt, bool kBr, int N>
+__device__ __forceinline__ float4v mma_n_h(const float* A, int lda, const float* B, int ldb, int k0, float4v acc) {
+    constexpr int S = N / 4;
+    const int l = threadIdx.x & 63, r = l & 15, kb = k0 + (l >> 4) * S;
+    float a[S], b[S];
+#pragma unroll
+    for (int s = 0; s < S; s += 4) {
+        if constexpr (kAt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[s + e] = A[(kb + s + e) * lda + r];
+        } else {
+            const float4v x = *reinterpret_cast<const float4v*>(&A[r * lda + kb + s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[s + e] = x[e];
+        }
+        if constexpr (kBr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[s + e] = B[(kb + s + e) * ldb + r];
+        } else {
+            const float4v x = *reinterpret_cast<const float4v*>(&B[r * ldb + kb + s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[s + e] = x[e];
+        }
+    }
+    return mma_h_run<S>(a, b, acc);
+}
+template <int N>
+__device__ __forceinline__ float4v mma_sym_n_h(const float* A, int lda, int r0, const float* B, int ldb, int k0,
+                                               float4v acc) {
+    constexpr int S = N / 4;
+    const int l = threadIdx.x & 63, r = r0 + (l & 15), kb = k0 + (l >> 4) * S;
+    float a[S], b[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        a[s] = A[r * lda + kb + s] + A[(kb + s) * lda + r];
+        b[s] = B[(kb + s) * ldb + (l & 15)];
+    }
+    return mma_h_run<S>(a, b, acc);
+}
+// Contraction in the precision of the inputs: fp16 operands for bf16 inputs,
+// fp32 for fp32 inputs.
+template <bool kHalf, bool kAt, bool kBr, int N>
+__device__ __forceinline__ float4v mma_x(const float* A, int lda, const float* B, int ldb, int k0, float4v acc) {
+    if constexpr (kHalf) return mma_n_h<kAt, kBr, N>(A, lda, B, ldb, k0, acc);
+    else return mma_n<kAt, kBr, N>(A, lda, B, ldb, k0, acc);
+}
+template <bool kHalf, int N>
+__device__ __forceinline__ float4v mma_sym_x(const float* A, int lda, int r0, const float* B, int ldb, int k0,
+                                             float4v acc) {
+    if constexpr (kHalf) return mma_sym_n_h<N>(A, lda, r0, B, ldb, k0, acc);
+    else return mma_sym_n<N>(A, lda, r0, B, ldb, k0, acc);
+}
+
 __device__ __forceinline__ float dpp_sum4(float x) {          // sum over a quad
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
@@ -309,8 +393,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
                     qk[u] = mma_bf16(qf[st], kf[u][st], qk[u]);
                 }
             } else {
-                kk[u] = mma_n<false, false, DK>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, kk[u]);
-                qk[u] = mma_n<false, false, DK>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, qk[u]);
+                kk[u] = mma_x<kBf16, false, false, DK>(&sK[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, kk[u]);
+                qk[u] = mma_x<kBf16, false, false, DK>(&sQA[16 * ti * LDK], LDK, &sK[16 * tj * LDK], LDK, 0, qk[u]);
             }
         }
     }
@@ -370,16 +454,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
             float4v y = float4v{0.f, 0.f, 0.f, 0.f};
             const float* Ai = sQA + 16 * I * LDA;
             const float* Bj = sT + 16 * J;
-            if (lev == 1) y = mma_n<false, true, 16>(Ai, LDA, Bj, LDT, 16 * J, y);
-            else if (lev == 2) y = mma_n<false, true, 32>(Ai, LDA, Bj, LDT, 16 * J, y);
-            else y = mma_n<false, true, 48>(Ai, LDA, Bj, LDT, 16 * J, y);
+            if (lev == 1) y = mma_x<kBf16, false, true, 16>(Ai, LDA, Bj, LDT, 16 * J, y);
+            else if (lev == 2) y = mma_x<kBf16, false, true, 32>(Ai, LDA, Bj, LDT, 16 * J, y);
+            else y = mma_x<kBf16, false, true, 48>(Ai, LDA, Bj, LDT, 16 * J, y);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sY[(4 * lg + e) * 16 + lr] = y[e];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const float4v t =
-                mma_n<false, true, 16>(sT + 16 * I * LDT + 16 * I, LDT, sY, 16, 0, float4v{0.f, 0.f, 0.f, 0.f});
+                mma_x<kBf16, false, true, 16>(sT + 16 * I * LDT + 16 * I, LDT, sY, 16, 0, float4v{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int e = 0; e < 4; ++e) sT[(16 * I + 4 * lg + e) * LDT + 16 * J + lr] = -t[e];
         }
@@ -491,8 +575,8 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(const void* __restrict_
         // 1. K S for row block rb, d_k columns [0, KH) or [KH, DK)
         if (half == 0 || KH < DK) {
             float4v ks = {0.f, 0.f, 0.f, 0.f};
-            if (half == 0) ks = mma_n<false, false, KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, 0, ks);
-            else if constexpr (KH < DK) ks = mma_n<false, false, DK - KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, KH, ks);
+            if (half == 0) ks = mma_x<kBf16, false, false, KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, 0, ks);
+            else if constexpr (KH < DK) ks = mma_x<kBf16, false, false, DK - KH>(&sK[16 * rb * LDK], LDK, sSt, LDS_, KH, ks);
 #pragma unroll
             for (int j = 0; j < 4; ++j) sKSp[half][(l & 15) * LDR + 16 * rb + 4 * (l >> 4) + j] = ks[j];
         }
@@ -506,7 +590,7 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(const void* __restrict_
         // 2. E = T R (T lower triangular), written out; (lam E)^T kept for the update
         if (wave < 4) {
             float4v e = {0.f, 0.f, 0.f, 0.f};
-            e = mma_n<false, false, C>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, e);   // T is zero above the diagonal
+            e = mma_x<kBf16, false, false, C>(&sT[16 * wave * LDT], LDT, sRt, LDR, 0, e);   // T is zero above the diagonal
             const float gn = sg[C - 1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -519,7 +603,7 @@ __global__ __launch_bounds__(512) void bwd_states_kernel(const void* __restrict_
         // 3. S' = gamma_n S + K^T (lam E)
         if (owns) {
             const float gam_n = __expf(sg[C - 1]);
-            st = mma_n<true, false, C>(&sK[16 * wave], LDK, sEt, LDR, 0, gam_n * st);
+            st = mma_x<kBf16, true, false, C>(&sK[16 * wave], LDK, sEt, LDR, 0, gam_n * st);
 #pragma unroll
             for (int j = 0; j < 4; ++j) sSt[(l & 15) * LDS_ + 16 * wave + 4 * (l >> 4) + j] = st[j];
         }
@@ -633,10 +717,10 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
             float4v acc = {0.f, 0.f, 0.f, 0.f};
             float4v kd = {0.f, 0.f, 0.f, 0.f};
             if (half == 0) {
-                acc = mma_n<true, false, C>(&sP[16 * rb], LDX, sdYt, LDX, 0, acc);   // P^T is zero below the diagonal
-                if constexpr (KA > 0) kd = mma_n<false, false, KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, 0, kd);
+                acc = mma_x<kBf16, true, false, C>(&sP[16 * rb], LDX, sdYt, LDX, 0, acc);   // P^T is zero below the diagonal
+                if constexpr (KA > 0) kd = mma_x<kBf16, false, false, KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, 0, kd);
             } else {
-                kd = mma_n<false, false, DK - KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, KA, kd);
+                kd = mma_x<kBf16, false, false, DK - KA>(&sK[16 * rb * LDK], LDK, sdSt, LDS_, KA, kd);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -657,7 +741,7 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
         // 2. dR = T^T dE, dV = diag(beta) dR (waves 0..3); dS starts with gamma_n dS' + Q^T (scale gamma dY)
         if (wave < 4) {
             float4v r = {0.f, 0.f, 0.f, 0.f};
-            r = mma_n<true, false, C>(&sT[16 * wave], LDX, sdEt, LDX, 0, r);   // T^T is zero below the diagonal
+            r = mma_x<kBf16, true, false, C>(&sT[16 * wave], LDX, sdEt, LDX, 0, r);   // T^T is zero below the diagonal
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * wave + 4 * (l >> 4) + j, tg = c * C + t;
@@ -667,10 +751,10 @@ __global__ __launch_bounds__(512) void bwd_dstates_kernel(
             }
         }
         const float gam_n = __expf(sg[C - 1]);
-        if (owns) ds = mma_n<true, false, C>(&sQ[16 * wave], LDK, sB1t, LDX, 0, gam_n * ds);
+        if (owns) ds = mma_x<kBf16, true, false, C>(&sQ[16 * wave], LDK, sB1t, LDX, 0, gam_n * ds);
         __syncthreads();
         // 3. dS += K^T (-beta gamma dR)
-        if (owns) ds = mma_n<true, false, C>(&sK[16 * wave], LDK, sB2t, LDX, 0, ds);
+        if (owns) ds = mma_x<kBf16, true, false, C>(&sK[16 * wave], LDK, sB2t, LDX, 0, ds);
         __syncthreads();                       // every read of this chunk's tiles is done
         if (owns) {
 #pragma unroll
@@ -783,17 +867,17 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             const int p = wave + 8 * u;
             if (p < NP) {
                 const int ti = p / NB, tj = p - ti * NB;
-                x1[u] = mma_n<false, false, SL>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x1[u]);
-                x2[u] = mma_n<false, false, SL>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x2[u]);
-                x3[u] = mma_n<false, false, SL>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, x3[u]);
+                x1[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x1[u]);
+                x2[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x2[u]);
+                x3[u] = mma_x<kBf16, false, false, SL>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, x3[u]);
             }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
             if (tj <= ti) {
-                x4[u] = mma_n<false, false, SL>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x4[u]);
-                x5[u] = mma_n<false, false, SL>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x5[u]);
+                x4[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x4[u]);
+                x5[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x5[u]);
             }
         }
         __syncthreads();
@@ -939,9 +1023,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 aq[j] = scale * gam * x1[u][j];
                 ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
             }
-            aq = mma_n<false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
-            ak = mma_sym_n<C>(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, ak);
-            ak = mma_n<true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
+            aq = mma_x<kBf16, false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
+            ak = mma_sym_x<kBf16, C>(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, ak);
+            ak = mma_x<kBf16, true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j, tg = c * C + row;

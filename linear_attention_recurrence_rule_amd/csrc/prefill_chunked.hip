@@ -516,14 +516,14 @@ struct Walk {
     unsigned hv;         // ... of this head's slice in a v / y row (h * DV + col0)
     int T, nchunks;
     float scale;
-    unsigned* status;    // the call's status word
+    unsigned* status;    // the call's status word (null without a workspace: T = 0)
 };
 
 // Sets `bit` of the call's status word when any lane of the wave saw a
 // non-finite value (an input or intermediate outside the fp16 operand range,
 // or non-finite inputs).
 __device__ __forceinline__ void report_nonfinite(unsigned* status, bool bad, unsigned bit) {
-    if (__any(bad) && (threadIdx.x & 63) == 0)
+    if (status && __any(bad) && (threadIdx.x & 63) == 0)
         __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool nonfinite(float4v v) {
@@ -1142,7 +1142,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
     using Cfg = MainCfg<DK>;
     const int nchunks = (a.T + C - 1) / C;
     unsigned* status = static_cast<unsigned*>(a.workspace);
-    _Float16* ws = reinterpret_cast<_Float16*>(static_cast<char*>(a.workspace) + kStatusBytes);
+    _Float16* ws = status ? reinterpret_cast<_Float16*>(static_cast<char*>(a.workspace) + kStatusBytes) : nullptr;
     if (nchunks > 0) {
         // chunks per wave: about one round of resident workgroups, at most 16
         const int BH = a.B * a.H;

@@ -7,16 +7,16 @@ import torch
 
 from oracle import gated_delta_backward
 from tests import oracle_pool
-from tests.gpu_util import check, dev, host, say
+from tests.gpu_util import TOL, check, dev, host, say
 from workloads import config_prefill_inputs, prefill_inputs
 import linear_attention_recurrence_rule_amd as gdn
 
 pytestmark = pytest.mark.gpu
 
-# Every contraction of the backward is float32 MFMA on exact inputs, with
-# float32 chunk matrices and states in between; the float32 bound applies to
-# both input dtypes.
-BWD_TOL = 1e-4
+# For fp32 inputs every contraction of the backward is float32 MFMA, with
+# float32 chunk matrices and states in between (the float32 bound, 1e-4); for
+# bf16 inputs the contractions take fp16 operands with float32 accumulation
+# (the bf16 bound, 2e-2).
 NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "d_initial_state")
 
 
@@ -28,7 +28,7 @@ def _run(d, dtype, dy, S0=None, dST=None, scale=1.0):
     return [host(x) for x in out]
 
 
-def _compare(got, ref, tol=BWD_TOL, heads=None):
+def _compare(got, ref, tol, heads=None):
     for name, g, r in zip(NAMES, got, ref):
         if heads is not None:
             g = g[:, :, heads] if g.ndim >= 3 and name != "d_initial_state" else g[:, heads]
@@ -48,7 +48,7 @@ def test_bwd_small(D, dtype, T):
     got = _run(d, dtype, dy, d["initial_state"], dST, scale=0.8)
     ref = gated_delta_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dy, d["initial_state"], dST,
                                scale=0.8)
-    _compare(got, ref)
+    _compare(got, ref, TOL[dtype])
 
 
 def test_bwd_without_states():
@@ -59,7 +59,7 @@ def test_bwd_without_states():
     dy = np.random.default_rng(9).standard_normal((B, T, H, D)).astype(np.float32)
     got = _run(d, "bf16", dy)
     ref = gated_delta_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dy)
-    _compare(got, ref)
+    _compare(got, ref, TOL["bf16"])
 
 
 def test_bwd_empty_sequence_passes_the_state_gradient_through():
@@ -83,7 +83,7 @@ def test_bwd_4k_tokens():
     dST = rng.standard_normal((1, 4, 128, 128)).astype(np.float32)
     got = _run(d, "bf16", dy, None, dST)
     ref = gated_delta_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dy, None, dST)
-    _compare(got, ref)
+    _compare(got, ref, TOL["bf16"])
 
 
 @pytest.mark.timeout(900)
@@ -97,4 +97,4 @@ def test_bwd_long_workload_full_launch_all_heads():
     got = _run(d, "bf16", dy)
     say("bwd long workload: oracle over all 32 heads")
     ref = oracle_pool.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dy)
-    _compare(got, ref)
+    _compare(got, ref, TOL["bf16"])
