@@ -66,7 +66,8 @@ def bwd_bytes(B, T, H, dk, dv, in_bytes=2):
 
 
 def bwd_flops(B, T, H, d, C=64):
-    """fp32 MFMA tile work of the four backward passes per token-head: the
+    """MFMA tile work of the four backward passes per token-head (fp16 operands
+    for bf16 inputs, fp32 for fp32 inputs): the
     C x d x d products (K S, K^T E, K dS', Q^T dY, K^T dR and the three X1..X3
     contractions over d_v) and the C x C x d ones (the two Gram products, T R,
     P^T dY, T^T dE, X4, X5 and the four C x C by C x d products of dq, dk)."""

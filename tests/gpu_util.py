@@ -43,8 +43,9 @@ def check(name, got, ref, tol):
 
 
 def prefill(q, k, v, alpha, beta, initial_state=None, **kw):
-    """gdn_prefill_fwd with a workspace of its own, followed by a check that no
-    bounded wait inside the kernels gave up (gdn_prefill_status)."""
+    """gdn_prefill_fwd with a workspace of its own (or the one passed), followed
+    by a check of the call's device status word (gdn_prefill_status: no
+    non-finite y or state)."""
     import linear_attention_recurrence_rule_amd as gdn
     B, T, H, dk = q.shape
     need = gdn.gdn_prefill_workspace_bytes(B, T, H, dk, v.shape[-1], q.dtype)
