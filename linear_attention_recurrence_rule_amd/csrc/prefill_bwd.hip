@@ -105,32 +105,27 @@ __device__ __forceinline__ float4v mma_sym_n(const float* A, int lda, int r0, co
 // The same contractions on fp16 MFMAs, for bf16 inputs: each lane reads the
 // operand values of mma_n's split-K layout from the fp32 LDS tiles, rounds
 // them to fp16, and feeds eight at a time to 16x16x32 MFMAs (a remainder of
-// four to one 16x16x16 MFMA); the k grouping differs from mma_n's but is the
+// four padded with zeros); the k grouping differs from mma_n's but is the
 // same for both operands, so the sum is the same contraction, with fp32
-// accumulation.  One MFMA then covers 32 values of k instead of 4.
+// accumulation.  One MFMA then covers 32 values of k instead of 4.  Only the
+// 16x16x32 shape touches these accumulators: on gfx950 a 16x16x16 f16 MFMA
+// that reads an accumulator just written by a 16x16x32 one has given wrong
+// sums.
+template <int N>
 __device__ __forceinline__ float4v mma_h8(const float* a, const float* b, float4v acc) {
-    half8 x, y;
+    half8 x = {}, y = {};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < N; ++e) {
         x[e] = static_cast<_Float16>(a[e]);
         y[e] = static_cast<_Float16>(b[e]);
     }
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
 }
-__device__ __forceinline__ float4v mma_h4(const float* a, const float* b, float4v acc) {
-    half4 x, y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[e] = static_cast<_Float16>(a[e]);
-        y[e] = static_cast<_Float16>(b[e]);
-    }
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, acc, 0, 0, 0);
-}
 template <int S>
 __device__ __forceinline__ float4v mma_h_run(const float (&a)[S], const float (&b)[S], float4v acc) {
 #pragma unroll
-    for (int s = 0; s + 8 <= S; s += 8) acc = mma_h8(a + s, b + s, acc);
-    if constexpr (S % 8 == 4) acc = mma_h4(a + S - 4, b + S - 4, acc);
+    for (int s = 0; s + 8 <= S; s += 8) acc = mma_h8<8>(a + s, b + s, acc);
+    if constexpr (S % 8 == 4) acc = mma_h8<4>(a + S - 4, b + S - 4, acc);
     return acc;
 }
 template <bool kAt, bool kBr, int N>
