@@ -181,6 +181,21 @@ __device__ __forceinline__ float4v mma_sym_x(const float* A, int lda, int r0, co
     else return mma_sym_n<N>(A, lda, r0, B, ldb, k0, acc);
 }
 
+// acc += A B^T over the 32 values of k of two fp16 tiles held row-major in
+// LDS (16 rows each, k along the row, leading dimension ld): lane group g
+// takes k = 8 g .. 8 g + 7 of both operands, one 16-byte read each.
+__device__ __forceinline__ half8 frag_h(const _Float16* A, int ld) {
+    const int l = threadIdx.x & 63;
+    return *reinterpret_cast<const half8*>(A + (l & 15) * ld + 8 * (l >> 4));
+}
+__device__ __forceinline__ float4v mma_hh(half8 a, half8 b, float4v acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ half4 to_h4(float4v x) {
+    return half4{static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]), static_cast<_Float16>(x[2]),
+                 static_cast<_Float16>(x[3])};
+}
+
 __device__ __forceinline__ float dpp_sum4(float x) {          // sum over a quad
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
@@ -813,8 +828,7 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     for (int u = 0; u < 2; ++u) x4[u] = x5[u] = float4v{0.f, 0.f, 0.f, 0.f};
     float drv = 0.f, sds = 0.f;
 
-    // phase-2 operands are loaded into registers first; each dv slab is
-    // loaded one slab ahead of its use
+    // phase-2 operands are loaded into registers first
     RowTile<D, 512, kBf16> tq, tk;
     MatTile<512> tp, tm;
     tq.load(q, b, c, T, H, h);
@@ -825,57 +839,154 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     const int si = tid % (D * SL / 4), sr = si >> 2, sc = si & 3;  // state item: row sr, columns 4 sc..
     const int tg0 = c * C + rt, tc0 = tg0 < T ? tg0 : T - 1;
     const long row0 = (static_cast<long>(b) * T + tc0) * H + h;
-    float4v fdy, fdr, fe, fs, fds;
-    Raw4<kBf16> fv;
-    auto fetch = [&](int v0) {
-        fdy = *reinterpret_cast<const float4v*>(&dy[row0 * D + v0 + 4 * rc]);
-        fv = raw_load<kBf16>(v, row0 * D + v0 + 4 * rc);
-        fdr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + rt) * D + v0 + 4 * rc]);
-        fe = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + rt) * D + v0 + 4 * rc]);
-        fs = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + sr) * D + v0 + 4 * sc]);
-        fds = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + sr) * D + v0 + 4 * sc]);
-    };
-    fetch(0);
-    for (int v0 = 0; v0 < D; v0 += SL) {
-        if (tid < C * SL / 4) {
-            float4v xdy = fdy, xv = raw_cvt<kBf16>(fv);
-            if (tg0 >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<float4v*>(&sdY[rt * LDL + 4 * rc]) = xdy;
-            *reinterpret_cast<float4v*>(&sdR[rt * LDL + 4 * rc]) = fdr;
-            *reinterpret_cast<float4v*>(&sE[rt * LDL + 4 * rc]) = fe;
-            *reinterpret_cast<float4v*>(&sV[rt * LDL + 4 * rc]) = xv;
-            drv += fdr.x * xv.x + fdr.y * xv.y + fdr.z * xv.z + fdr.w * xv.w;
-        }
-        if (tid < D * SL / 4) {
-            *reinterpret_cast<float4v*>(&sS[sr * LDL + 4 * sc]) = fs;
-            *reinterpret_cast<float4v*>(&sdS[sr * LDL + 4 * sc]) = fds;
-            sds += fs.x * fds.x + fs.y * fds.y + fs.z * fds.z + fs.w * fds.w;
-        }
-        if (v0 == 0) {
-            tq.store(sQ, LDK, c, T);
-            tk.store(sK, LDK, c, T);
-        }
-        __syncthreads();
-        fetch(v0 + SL < D ? v0 + SL : v0);
+    if constexpr (kBf16 && D >= 64) {
+        // bf16 inputs: 32-column d_v slabs (whole 128-byte lines of the fp32
+        // rows, one load item per thread and row array), rounded to fp16 once
+        // when stored, so that each MFMA operand is one 16-byte LDS read and
+        // each MFMA covers 32 values of d_v.  Row stride 40 halfs (80 bytes)
+        // keeps the 16-byte operand reads free of bank conflicts.
+        constexpr int SH = 32, LDH = SH + 8, NSH = D / SH, NSI = D / 64;
+        constexpr int kDepthH = NSH < 3 ? NSH : 3;
+        static_assert((3 * C + 2 * D) * LDH * 2 <= kRegion * 4, "fp16 slabs fit the slab region");
+        _Float16* hY = reinterpret_cast<_Float16*>(sR);   // dY slab, C x LDH
+        _Float16* hR = hY + C * LDH;                      // dR slab
+        _Float16* hE = hR + C * LDH;                      // E slab
+        _Float16* hS = hE + C * LDH;                      // S slab, D x LDH
+        _Float16* hD = hS + D * LDH;                      // dS slab
+        const int hr = tid >> 3, hc = tid & 7;            // row item: row hr, columns 4 hc ..
+        const int tgh = c * C + hr, tch = tgh < T ? tgh : T - 1;
+        const long rowh = (static_cast<long>(b) * T + tch) * H + h;
+        struct SlabH {
+            float4v dy, dr, e, s[NSI], ds[NSI];
+            Raw4<true> v;
+        };
+        SlabH f[kDepthH];
+        auto fetch = [&](SlabH& x, int v0) {
+            x.dy = *reinterpret_cast<const float4v*>(&dy[rowh * D + v0 + 4 * hc]);
+            x.v = raw_load<true>(v, rowh * D + v0 + 4 * hc);
+            x.dr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + hr) * D + v0 + 4 * hc]);
+            x.e = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + hr) * D + v0 + 4 * hc]);
 #pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const int p = wave + 8 * u;
-            if (p < NP) {
-                const int ti = p / NB, tj = p - ti * NB;
-                x1[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x1[u]);
-                x2[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x2[u]);
-                x3[u] = mma_x<kBf16, false, false, SL>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, x3[u]);
+            for (int i = 0; i < NSI; ++i) {
+                x.s[i] = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
+                x.ds[i] = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
             }
-        }
+        };
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
-            if (tj <= ti) {
-                x4[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x4[u]);
-                x5[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x5[u]);
+        for (int s = 0; s < kDepthH; ++s) fetch(f[s], s * SH);
+#pragma unroll
+        for (int s = 0; s < NSH; ++s) {
+            SlabH& x = f[s % kDepthH];
+            {
+                float4v xdy = x.dy, xv = raw_cvt<true>(x.v);
+                if (tgh >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<half4*>(&hY[hr * LDH + 4 * hc]) = to_h4(xdy);
+                *reinterpret_cast<half4*>(&hR[hr * LDH + 4 * hc]) = to_h4(x.dr);
+                *reinterpret_cast<half4*>(&hE[hr * LDH + 4 * hc]) = to_h4(x.e);
+                drv += x.dr.x * xv.x + x.dr.y * xv.y + x.dr.z * xv.z + x.dr.w * xv.w;
+#pragma unroll
+                for (int i = 0; i < NSI; ++i) {
+                    *reinterpret_cast<half4*>(&hS[(hr + 64 * i) * LDH + 4 * hc]) = to_h4(x.s[i]);
+                    *reinterpret_cast<half4*>(&hD[(hr + 64 * i) * LDH + 4 * hc]) = to_h4(x.ds[i]);
+                    sds += x.s[i].x * x.ds[i].x + x.s[i].y * x.ds[i].y + x.s[i].z * x.ds[i].z +
+                           x.s[i].w * x.ds[i].w;
+                }
             }
+            if (s == 0) {
+                tq.store(sQ, LDK, c, T);
+                tk.store(sK, LDK, c, T);
+            }
+            __syncthreads();
+            if (s + kDepthH < NSH) fetch(x, (s + kDepthH) * SH);
+            // the same pairs as the fp32 path; repeated fragment reads of one
+            // tile (the B tiles of a wave's pairs, E as both operands) are the
+            // same loads and are read once
+#pragma unroll
+            for (int u = 0; u < PPW; ++u) {
+                const int p = wave + 8 * u;
+                if (p < NP) {
+                    const int ti = p / NB, tj = p - ti * NB;
+                    const half8 bS = frag_h(&hS[16 * tj * LDH], LDH), bD = frag_h(&hD[16 * tj * LDH], LDH);
+                    x1[u] = mma_hh(frag_h(&hY[16 * ti * LDH], LDH), bS, x1[u]);
+                    x2[u] = mma_hh(frag_h(&hR[16 * ti * LDH], LDH), bS, x2[u]);
+                    x3[u] = mma_hh(frag_h(&hE[16 * ti * LDH], LDH), bD, x3[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
+                if (tj <= ti) {
+                    const half8 bE = frag_h(&hE[16 * tj * LDH], LDH);
+                    x4[u] = mma_hh(frag_h(&hY[16 * ti * LDH], LDH), bE, x4[u]);
+                    x5[u] = mma_hh(frag_h(&hR[16 * ti * LDH], LDH), bE, x5[u]);
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        // d_v slabs in flight: slab s is loaded kDepth slabs before its use, into
+        // register set s % kDepth (the slab loop is unrolled, so the sets are
+        // fixed registers and every load is unconditional)
+        constexpr int NS = D / SL;
+        constexpr int kDepth = NS < 4 ? NS : 4;
+        struct Slab {
+            float4v dy, dr, e, s, ds;
+            Raw4<kBf16> v;
+        };
+        Slab f[kDepth];
+        auto fetch = [&](Slab& x, int v0) {
+            x.dy = *reinterpret_cast<const float4v*>(&dy[row0 * D + v0 + 4 * rc]);
+            x.v = raw_load<kBf16>(v, row0 * D + v0 + 4 * rc);
+            x.dr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + rt) * D + v0 + 4 * rc]);
+            x.e = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + rt) * D + v0 + 4 * rc]);
+            x.s = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + sr) * D + v0 + 4 * sc]);
+            x.ds = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + sr) * D + v0 + 4 * sc]);
+        };
+    #pragma unroll
+        for (int s = 0; s < kDepth; ++s) fetch(f[s], s * SL);
+    #pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            Slab& x = f[s % kDepth];
+            if (tid < C * SL / 4) {
+                float4v xdy = x.dy, xv = raw_cvt<kBf16>(x.v);
+                if (tg0 >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<float4v*>(&sdY[rt * LDL + 4 * rc]) = xdy;
+                *reinterpret_cast<float4v*>(&sdR[rt * LDL + 4 * rc]) = x.dr;
+                *reinterpret_cast<float4v*>(&sE[rt * LDL + 4 * rc]) = x.e;
+                *reinterpret_cast<float4v*>(&sV[rt * LDL + 4 * rc]) = xv;
+                drv += x.dr.x * xv.x + x.dr.y * xv.y + x.dr.z * xv.z + x.dr.w * xv.w;
+            }
+            if (tid < D * SL / 4) {
+                *reinterpret_cast<float4v*>(&sS[sr * LDL + 4 * sc]) = x.s;
+                *reinterpret_cast<float4v*>(&sdS[sr * LDL + 4 * sc]) = x.ds;
+                sds += x.s.x * x.ds.x + x.s.y * x.ds.y + x.s.z * x.ds.z + x.s.w * x.ds.w;
+            }
+            if (s == 0) {
+                tq.store(sQ, LDK, c, T);
+                tk.store(sK, LDK, c, T);
+            }
+            __syncthreads();
+            if (s + kDepth < NS) fetch(x, (s + kDepth) * SL);
+    #pragma unroll
+            for (int u = 0; u < PPW; ++u) {
+                const int p = wave + 8 * u;
+                if (p < NP) {
+                    const int ti = p / NB, tj = p - ti * NB;
+                    x1[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x1[u]);
+                    x2[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sS[16 * tj * LDL], LDL, 0, x2[u]);
+                    x3[u] = mma_x<kBf16, false, false, SL>(&sE[16 * ti * LDL], LDL, &sdS[16 * tj * LDL], LDL, 0, x3[u]);
+                }
+            }
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int p = wave + 8 * u, ti = p >> 2, tj = p & 3;
+                if (tj <= ti) {
+                    x4[u] = mma_x<kBf16, false, false, SL>(&sdY[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x4[u]);
+                    x5[u] = mma_x<kBf16, false, false, SL>(&sdR[16 * ti * LDL], LDL, &sE[16 * tj * LDL], LDL, 0, x5[u]);
+                }
+            }
+            __syncthreads();
+        }
     }
 
     // ---- phase 2 ----
@@ -903,8 +1014,12 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         sQX1[tid] = sKX2[tid] = sKX3[tid] = 0.f;
     }
     if (tid == 0) sSdS = 0.f;
-    // dR . v per row: 4 lanes per row hold the partial sums
-    {
+    // dR . v per row: the partial sums sit in the lanes of the row's load
+    // items (8 lanes per row with 32-column fp16 slabs, 4 with 16-column ones)
+    if constexpr (kBf16 && D >= 64) {
+        const float s = dpp_sum8(drv);
+        if ((tid & 7) == 0) sDRv[tid >> 3] = s;
+    } else {
         const float s = dpp_sum4(drv);
         if (tid < C * SL / 4 && (tid & 3) == 0) sDRv[tid >> 2] = s;
     }
