@@ -145,6 +145,10 @@ struct QsaSelectArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
+// Chunk-start states S_c ([B H nchunks][d][d] fp32) and E_c ([B H nchunks][64][d]
+// fp32) of the bf16 chunked walk, without y; d_k = d_v in {64, 128}; the
+// workspace as for launch_prefill_bf16.
+hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);

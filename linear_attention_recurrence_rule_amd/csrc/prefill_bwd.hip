@@ -1184,8 +1184,35 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
     const dim3 gc(nch, BH), gs((D / 16) * 8 * ((BH + 7) / 8), 1);
     hipLaunchKernelGGL((bwd::bwd_prep_kernel<D, kBf16>), gc, dim3(256), 0, a.stream, a.q, a.k, a.alpha, a.beta,
                        g, Tm, P, M, a.T, a.H, nch);
-    hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.k, a.v, a.beta,
-                       a.initial_state, g, Tm, S, E, a.T, a.H, nch, BH);
+    if constexpr (kBf16 && D >= 64) {
+        // S_c and E_c from the forward's chunked walk (the same chain, with its
+        // own T' and base-2 gates); its workspace sits in the dS region, which
+        // the reverse walk fills only afterwards
+        static_assert(sizeof(float) * D * D >= 7168, "the forward's per-chunk workspace fits the dS slot");
+        PrefillArgs pa{};
+        pa.q = a.q;
+        pa.k = a.k;
+        pa.v = a.v;
+        pa.alpha = a.alpha;
+        pa.beta = a.beta;
+        pa.initial_state = a.initial_state;
+        pa.final_state = nullptr;
+        pa.y = nullptr;
+        pa.B = a.B;
+        pa.T = a.T;
+        pa.H = a.H;
+        pa.dk = D;
+        pa.dv = D;
+        pa.bf16 = true;
+        pa.scale = a.scale;
+        pa.workspace = dS;
+        pa.stream = a.stream;
+        const hipError_t e = launch_prefill_bf16_states(pa, S, E);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.k, a.v, a.beta,
+                           a.initial_state, g, Tm, S, E, a.T, a.H, nch, BH);
+    }
     hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.q, a.k, a.beta,
                        a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, BH,
                        a.scale);

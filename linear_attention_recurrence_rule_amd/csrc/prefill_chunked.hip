@@ -683,6 +683,16 @@ struct StateRegs {
     half8 Sb[MainCfg<DK>::KSTEP];    // its fp16 B operand of K S
 };
 
+// State-saving walk (for the backward pass): the state wave leaves S_p (the
+// fp32 state slice at the start of chunk p) and E_p in these buffers during
+// period p, and the copy waves write them out in period p + 1.
+template <int DK>
+struct SaveBufs {
+    float S[2][16][DK + 4];   // [slice column][d_k row]
+    float E[2][16][C + 4];    // [slice column][token of the chunk]
+};
+struct NoSaveBufs {};
+
 template <int DK>
 __device__ __forceinline__ void state_refresh_operand(StateRegs<DK>& st) {
 #pragma unroll
@@ -728,12 +738,19 @@ __device__ __forceinline__ half8 ld_kt(const _Float16* Kb, int r, int ks, int la
 //   E  K^T D E over tokens 32 .. 63; the fp16 copies of the new state
 // LDS reads are issued one phase ahead and in bursts of at most about 15
 // behind the oldest one still needed (the LDS wait counter's range).
-template <int DK, int buf>
-__device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int lane) {
+template <int DK, int buf, bool kSave = false>
+__device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st, int lane,
+                                            SaveBufs<DK>* sv = nullptr) {
     using Cfg = MainCfg<DK>;
     constexpr int KS = Cfg::KSTEP;
     constexpr int NST = Cfg::NST;
     const int lr = lane & 15, lq = lane >> 4;
+    if constexpr (kSave) {
+        // S_p before the update (tile r, lane group lq holds 4 consecutive rows)
+#pragma unroll
+        for (int r = 0; r < NST; ++r)
+            *reinterpret_cast<float4v*>(&sv->S[buf][lr][state_row<DK>(r, lq, 0)]) = st.S[r];
+    }
     const _Float16* Kb = sm.K[buf];
     const _Float16* Tb = sm.Tp[buf];
     const float* gate = sm.gate[buf];
@@ -825,6 +842,11 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
 #pragma unroll
     for (int I = 2; I < NB; ++I) e[I] = mma(ta[I][1], Rb1, e[I]);
     fence();
+    if constexpr (kSave) {
+#pragma unroll
+        for (int I = 0; I < NB; ++I) *reinterpret_cast<float4v*>(&sv->E[buf][lr][I * 16 + 4 * lq]) = e[I];
+        fence();
+    }
     // D: K^T D E over tokens 0 .. 31; the second K step of K^T in flight
     const half8 Eb0 = cat(dscale(dc[0], e[0]), dscale(dc[1], e[1]));
 #pragma unroll
@@ -833,7 +855,7 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
 #pragma unroll
     for (int r = 0; r < NST; ++r) {
         st.S[r] = mma(kt[0][r], Eb0, st.S[r]);
-        if (r == NST / 2) {
+        if (r == NST / 2 && !kSave) {
             fence();
 #pragma unroll
             for (int I = 0; I < NB; ++I)
@@ -848,12 +870,12 @@ __device__ __forceinline__ void state_chunk(MainSmem<DK>& sm, StateRegs<DK>& st,
     for (int r = 0; r < NST; ++r) st.S[r] = mma(kt[1][r], Eb1, st.S[r]);
     fence();
     state_refresh_operand(st);
-    state_publish<DK>(st, sm.ST[buf ^ 1], lane);
+    if constexpr (!kSave) state_publish<DK>(st, sm.ST[buf ^ 1], lane);
 }
 
-template <int DK>
+template <int DK, bool kSave = false>
 __device__ __forceinline__ void state_role(MainSmem<DK>& sm, const Walk& w, const float* S0, float* S_out,
-                                           long sbase, int DV, int lane) {
+                                           long sbase, int DV, int lane, SaveBufs<DK>* sv = nullptr) {
     using Cfg = MainCfg<DK>;
     const int lr = lane & 15, lq = lane >> 4;
     StateRegs<DK> st;
@@ -867,13 +889,13 @@ __device__ __forceinline__ void state_role(MainSmem<DK>& sm, const Walk& w, cons
     const int n = w.nchunks;
     int p = 0;
     for (; p + 1 < n; p += 2) {
-        state_chunk<DK, 0>(sm, st, lane);
+        state_chunk<DK, 0, kSave>(sm, st, lane, sv);
         period_end();
-        state_chunk<DK, 1>(sm, st, lane);
+        state_chunk<DK, 1, kSave>(sm, st, lane, sv);
         period_end();
     }
     if (p < n) {
-        state_chunk<DK, 0>(sm, st, lane);
+        state_chunk<DK, 0, kSave>(sm, st, lane, sv);
         period_end();
         ++p;
     }
@@ -1064,14 +1086,49 @@ __device__ __forceinline__ void output_role(MainSmem<DK>& sm, const Walk& w, int
     report_nonfinite(w.status, !__builtin_isfinite(o.ysum), 1u);
 }
 
+// Copy role of the state-saving walk: wave I writes rows I DK / 4 .. of S_p
+// and tokens 16 I .. 16 I + 15 of E_p (fp32, row-major [row][column] as the
+// backward pass reads them) in period p + 1, from the buffers the state wave
+// filled in period p.
 template <int DK>
+__device__ __forceinline__ void copy_role(const SaveBufs<DK>* sv, const Walk& w, float* ws_S, float* ws_E,
+                                          long bhn0, int DV, int col0, int I, int lane) {
+    constexpr int RW = DK / 4;                 // state rows per copy wave
+    const int c4 = lane & 3, lrow = lane >> 2;
+    period_end();
+    const int n = w.nchunks;
+    for (int p = 0; p <= n; ++p) {
+        if (p >= 1) {
+            const int c = p - 1, buf = c & 1;
+            const long bhn = bhn0 + c;
+#pragma unroll
+            for (int hh = 0; hh < RW / 16; ++hh) {
+                const int row = I * RW + 16 * hh + lrow;
+                float4v x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = sv->S[buf][4 * c4 + e][row];
+                *reinterpret_cast<float4v*>(&ws_S[(bhn * DK + row) * DV + col0 + 4 * c4]) = x;
+            }
+            const int tok = I * 16 + lrow;
+            float4v x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = sv->E[buf][4 * c4 + e][tok];
+            *reinterpret_cast<float4v*>(&ws_E[(bhn * C + tok) * DV + col0 + 4 * c4]) = x;
+        }
+        period_end();
+    }
+}
+
+template <int DK, bool kSave = false>
 __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, const _Float16* __restrict__ ws,
                                                    const float* __restrict__ S0, float* __restrict__ S_out,
                                                    float* __restrict__ y, int B, int T, int H, int DV, int nsl,
-                                                   float scale, unsigned* status) {
+                                                   float scale, unsigned* status, float* __restrict__ ws_S,
+                                                   float* __restrict__ ws_E) {
     using Cfg = MainCfg<DK>;
     __shared__ MainSmem<DK> sm;
+    __shared__ typename std::conditional<kSave, SaveBufs<DK>, NoSaveBufs>::type sv;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     // block -> (head, slice): the slices of a head share block ids modulo kXcds
     const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
@@ -1087,7 +1144,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     w.q = q + tok0 * w.rowq;
     w.k = k + tok0 * w.rowq;
     w.v = v + tok0 * w.rowv;
-    w.y = y + tok0 * w.rowv;
+    w.y = y ? y + tok0 * w.rowv : nullptr;
     w.hq = static_cast<unsigned>(h * DK);
     w.hv = static_cast<unsigned>(h * DV + col0);
     w.T = T;
@@ -1105,16 +1162,23 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
 
     // Each role runs its own loop with the same barrier sequence: one barrier
     // after the prologue and one after every period (nchunks + 1 periods).
+    // (state-saving walk: the state wave and the loaders as usual, the four
+    // output waves copy S_p and E_p out instead of forming y)
     if (wv == Cfg::W_STATE) {
-        state_role<DK>(sm, w, S0, S_out, static_cast<long>(bh) * DK * DV + col0, DV, lane);
-    } else if (wv == 1) {
-        output_role<DK, 3>(sm, w, lane);
-    } else if (wv == 5) {
-        output_role<DK, 0>(sm, w, lane);
-    } else if (wv == 2) {
-        output_role<DK, 2>(sm, w, lane);
-    } else if (wv == 6) {
-        output_role<DK, 1>(sm, w, lane);
+        if constexpr (kSave)
+            state_role<DK, true>(sm, w, S0, S_out, static_cast<long>(bh) * DK * DV + col0, DV, lane, &sv);
+        else
+            state_role<DK>(sm, w, S0, S_out, static_cast<long>(bh) * DK * DV + col0, DV, lane);
+    } else if (wv == 1 || wv == 2 || wv == 5 || wv == 6) {
+        const int blk = wv == 1 ? 3 : (wv == 5 ? 0 : (wv == 2 ? 2 : 1));
+        if constexpr (kSave) {
+            copy_role<DK>(&sv, w, ws_S, ws_E, static_cast<long>(bh) * w.nchunks, DV, col0, blk, lane);
+        } else {
+            if (blk == 3) output_role<DK, 3>(sm, w, lane);
+            else if (blk == 0) output_role<DK, 0>(sm, w, lane);
+            else if (blk == 2) output_role<DK, 2>(sm, w, lane);
+            else output_role<DK, 1>(sm, w, lane);
+        }
     } else if (wv == Cfg::W_MISC) {
         MiscLoader<DK> ld;
         ld.init(lane, w);
@@ -1138,7 +1202,7 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
 }
 
 template <int DK>
-static hipError_t launch_t(const PrefillArgs& a) {
+static hipError_t launch_t(const PrefillArgs& a, float* save_S = nullptr, float* save_E = nullptr) {
     using Cfg = MainCfg<DK>;
     const int nchunks = (a.T + C - 1) / C;
     unsigned* status = static_cast<unsigned*>(a.workspace);
@@ -1158,10 +1222,19 @@ static hipError_t launch_t(const PrefillArgs& a) {
     }
     const int nsl = a.dv / Cfg::SV;
     const int groups = (a.B * a.H + kXcds - 1) / kXcds;
+    if constexpr (DK >= 64) {
+        if (save_S) {
+            hipLaunchKernelGGL((main_kernel<DK, true>), dim3(groups * kXcds * nsl), dim3(Cfg::NT), 0, a.stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), ws, a.initial_state, a.final_state, nullptr,
+                               a.B, a.T, a.H, a.dv, nsl, a.scale, status, save_S, save_E);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((main_kernel<DK>), dim3(groups * kXcds * nsl), dim3(Cfg::NT), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), ws, a.initial_state, a.final_state, a.y,
-                       a.B, a.T, a.H, a.dv, nsl, a.scale, status);
+                       a.B, a.T, a.H, a.dv, nsl, a.scale, status, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1170,6 +1243,18 @@ static hipError_t launch_t(const PrefillArgs& a) {
 size_t prefill_bf16_workspace_bytes(int B, int T, int H) {
     const long nchunks = (T + chunked::C - 1) / chunked::C;
     return chunked::kStatusBytes + static_cast<size_t>(B) * H * nchunks * chunked::WS_CHUNK * sizeof(_Float16);
+}
+
+// The chunk-start states and E of every chunk (fp32, [b h chunk][d_k][d_v]
+// and [b h chunk][token][d_v]) from the same walk, for the backward pass;
+// y is not formed.  d_k = d_v >= 64.
+hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E) {
+    if (a.dk != a.dv) return hipErrorInvalidValue;
+    switch (a.dk) {
+        case 64: return chunked::launch_t<64>(a, S, E);
+        case 128: return chunked::launch_t<128>(a, S, E);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a) {
