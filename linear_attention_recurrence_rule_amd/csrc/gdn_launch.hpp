@@ -149,6 +149,28 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a);
 // fp32) of the bf16 chunked walk, without y; d_k = d_v in {64, 128}; the
 // workspace as for launch_prefill_bf16.
 hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E);
+
+// The backward's reverse walk for bf16 inputs (d_k = d_v = d in {64, 128}):
+// dS' per chunk, dR per chunk, dv and d_initial_state, from the backward
+// workspace's g, T and P (fp32, [B H nchunks] x 64, x 64 x 64).
+struct RevWalkArgs {
+    const void* q;
+    const void* k;
+    const float* beta;
+    const float* dy;
+    const float* dST;            // may be null
+    const float* g;
+    const float* Tm;
+    const float* P;
+    float* dS;
+    float* dR;
+    float* dv;
+    float* dS0;                  // may be null
+    int B, T, H, d;
+    float scale;
+    hipStream_t stream;
+};
+hipError_t launch_bwd_reverse_walk(const RevWalkArgs& a);
 size_t prefill_bf16_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);

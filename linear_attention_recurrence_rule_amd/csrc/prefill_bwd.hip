@@ -1213,9 +1213,34 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
         hipLaunchKernelGGL((bwd::bwd_states_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.k, a.v, a.beta,
                            a.initial_state, g, Tm, S, E, a.T, a.H, nch, BH);
     }
-    hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.q, a.k, a.beta,
-                       a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, BH,
-                       a.scale);
+    if constexpr (kBf16 && D >= 64) {
+        // the reverse walk with the dS chain in one wave's registers
+        RevWalkArgs ra{};
+        ra.q = a.q;
+        ra.k = a.k;
+        ra.beta = a.beta;
+        ra.dy = a.dy;
+        ra.dST = a.d_final_state;
+        ra.g = g;
+        ra.Tm = Tm;
+        ra.P = P;
+        ra.dS = dS;
+        ra.dR = dR;
+        ra.dv = a.dv;
+        ra.dS0 = a.d_initial_state;
+        ra.B = a.B;
+        ra.T = a.T;
+        ra.H = a.H;
+        ra.d = D;
+        ra.scale = a.scale;
+        ra.stream = a.stream;
+        const hipError_t e = launch_bwd_reverse_walk(ra);
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((bwd::bwd_dstates_kernel<D, D, kBf16>), gs, dim3(512), 0, a.stream, a.q, a.k, a.beta,
+                           a.dy, a.d_final_state, g, Tm, P, dS, dR, a.dv, a.d_initial_state, a.T, a.H, nch, BH,
+                           a.scale);
+    }
     hipLaunchKernelGGL((bwd::bwd_grads_kernel<D, kBf16>), gc, dim3(512), 0, a.stream, a.q, a.k, a.v, a.alpha,
                        a.beta, a.dy, g, P, M, S, dS, E, dR, a.dq, a.dk, a.dalpha, a.dbeta, a.T, a.H, nch, a.scale);
     return hipGetLastError();

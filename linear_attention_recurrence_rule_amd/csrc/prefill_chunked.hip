@@ -1201,6 +1201,527 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     }
 }
 
+// ===========================================================================
+// Reverse walk of the backward pass (bf16 inputs, d_k = d_v = DK in {64,
+// 128}): the adjoint of the chunk chain above.  Per (head, 16-column value
+// slice) the chunks c = n - 1 .. 0 are walked with the state gradient dS
+// (d_k x 16, fp32) held in the accumulator registers of one wave, in the
+// forward state wave's row order.  With g the chunk's cumulative log decay,
+// gamma = exp(g), lam = exp(g_last - g), T = (I + A)^-1 and the masked gated
+// Gram P = Gamma o (Q K^T) (the backward's chunk-parallel pass stores g, T
+// and P), chunk c turns dS' (the gradient of the state after the chunk) into
+//     dE = scale P^T dY + diag(lam) K dS'
+//     dR = T^T dE                              (dV = diag(beta) dR)
+//     dS = gamma_last dS' + Q^T (scale diag(gamma) dY) - K^T (diag(beta gamma) dR)
+// (the chunkwise form of the delta rule differentiated, slinene page, Module
+// A).  Roles, wave w on SIMD w % 4:
+//   0     the dS chain: K dS', dE, dR and the update, as the forward's state
+//         wave runs K S, R, E and its update
+//   1, 2  helpers: scale P^T dY and Q^T (scale gamma dY) of the next chunk
+//         (neither depends on dS), left in LDS as accumulator tiles
+//   3     copy: dS' (the gradient workspace), dR and dV of the previous chunk
+//   4, 5  loaders of the next chunk's k, and T with the gates
+//   6, 7  loaders of q, and P, the dY slice and scale gamma, two chunks ahead
+// Two barriers open the walk (the loaders' first stores, then the helpers'
+// first chunk); then one ends each of the n + 1 periods.  Period p processes
+// chunk n - 1 - p.
+// ===========================================================================
+template <int DK>
+struct alignas(16) RevSmem {
+    static constexpr int NST = DK / 16;
+    _Float16 K[2][C * DK];        // k of the state wave's chunk, rows swizzled
+    _Float16 Tm[2][C * C];        // T, [t][i], rows swizzled
+    float gate[2][3 * C];         // lam, -beta gamma, and gamma_last at [2 C]
+    _Float16 Q[2][C * DK];        // q of the helpers' chunk
+    _Float16 P[2][C * C];         // P, [t][i], rows swizzled
+    _Float16 dY[2][C * 16];       // dY slice, [t][column]
+    float hg[2][C];               // scale gamma
+    float4v PdY[2][NB][64];       // scale P^T dY, accumulator tiles, lane-major
+    float4v QB[2][NST][64];       // Q^T (scale gamma dY), the state's tiles, lane-major
+    float4v SS[2][NST][64];       // dS' of the chunk, for the copy wave
+    float4v SR[2][NB][64];        // dR of the chunk
+};
+
+struct RevWalk {
+    const uint16_t* q;        // this sequence's rows
+    const uint16_t* k;
+    const float* beta;        // this sequence and head: beta[t * H]
+    const float* dy;          // this sequence's rows
+    const float* g;           // this head's chunks in the backward workspace
+    const float* Tm;
+    const float* P;
+    long rowq, rowv;
+    unsigned hq, hv;          // element offsets of the head (q, k) and the slice (dy)
+    int H, T, nchunks;
+    float scale;
+};
+
+// A operand of (X^T) for row block I of X's columns and token step ks, from
+// a row-major swizzled [token][LD] fp16 tile X: lane (m + 16 g) gets
+// X[32 ks + 16 (s / 4) + 4 g + s % 4][16 I + m] in slot s (the split-K token
+// order of the accumulator tiles stacked along K).
+template <int LD>
+__device__ __forceinline__ half8 ld_tn(const _Float16* X, int I, int ks, int lane) {
+    const int g = lane >> 4, x = lane & 15;
+    const int o = swz<LD>(4 * g + (x >> 2), 16 * I + 4 * (x & 3));
+    return cat(ld_tr4(X + ks * 32 * LD + o), ld_tr4(X + (ks * 32 + 16) * LD + o));
+}
+
+__device__ __forceinline__ rsrc_t rev_rsrc(const void* base, long elem_off, long bytes, bool live) {
+    return make_rsrc(static_cast<const char*>(base) + (live ? elem_off : 0), live ? bytes : 0);
+}
+
+// bf16 rows (k or q) -> fp16 swizzled tile; pieces i = j * 64 + lane.
+template <int DK, bool kQ>
+struct RevRows {
+    static constexpr int QC = DK / 8, N = C * QC / 64;
+    int voff[N], loff[N];
+    uint4 a[2][N];
+    __device__ void init(int ls, const RevWalk& w) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i = j * 64 + ls, t = i / QC, cq = i % QC;
+            voff[j] = static_cast<int>((static_cast<unsigned>(t) * static_cast<unsigned>(w.rowq) + w.hq + cq * 8u) * 2u);
+            loff[j] = swz<DK>(t, cq * 8);
+        }
+    }
+    template <int set>
+    __device__ void load(const RevWalk& w, int chunk) {
+        const bool live = chunk >= 0 && chunk < w.nchunks;
+        const long t0 = static_cast<long>(chunk) * C;
+        const rsrc_t r = rev_rsrc(kQ ? w.q : w.k, t0 * w.rowq * 2, (w.T - t0) * w.rowq * 2, live);
+#pragma unroll
+        for (int j = 0; j < N; ++j) a[set][j] = bload16(r, voff[j]);
+    }
+    template <int set, int buf>
+    __device__ void store(RevSmem<DK>& sm) const {
+        _Float16* dst = kQ ? sm.Q[buf] : sm.K[buf];
+#pragma unroll
+        for (int j = 0; j < N; ++j) st16(&dst[loff[j]], bf16x8_to_h8(a[set][j]));
+    }
+};
+
+// fp32 64 x 64 workspace tile (T or P) -> fp16 swizzled tile, 16 pieces per lane.
+template <int DK, bool kP>
+struct RevTile {
+    int loff[16];
+    int lane;
+    uint4 a[2][16];
+    __device__ void init(int ls) {
+        lane = ls;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = j * 64 + ls;
+            loff[j] = swz<C>(i >> 4, 4 * (i & 15));
+        }
+    }
+    template <int set>
+    __device__ void load(const RevWalk& w, int chunk) {
+        const bool live = chunk >= 0 && chunk < w.nchunks;
+        const rsrc_t r = rev_rsrc(kP ? w.P : w.Tm, static_cast<long>(chunk) * C * C * 4, C * C * 4, live);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[set][j] = bload16(r, (j * 64 + lane) * 16);
+    }
+    template <int set, int buf>
+    __device__ void store(RevSmem<DK>& sm) const {
+        _Float16* dst = kP ? sm.P[buf] : sm.Tm[buf];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            *reinterpret_cast<half4*>(&dst[loff[j]]) = to_h4(__builtin_bit_cast(float4v, a[set][j]));
+    }
+};
+
+// Per-token gate values of a chunk (lane = token): g_t, g_last and beta_t.
+struct RevGates {
+    float g[2], gl[2], b[2];
+    template <int set>
+    __device__ void load(const RevWalk& w, int chunk, int lane, bool need_beta) {
+        const bool live = chunk >= 0 && chunk < w.nchunks;
+        const long t0 = static_cast<long>(chunk) * C;
+        const rsrc_t rg = rev_rsrc(w.g, t0 * 4, C * 4, live);
+        g[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
+        gl[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (C - 1) * 4, 0, 0));
+        if (need_beta) {
+            const rsrc_t rb = rev_rsrc(w.beta, t0 * w.H * 4, (w.T - t0) * w.H * 4, live);
+            b[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * w.H * 4, 0, 0));
+        }
+    }
+};
+
+// The dY slice (fp32 rows) -> fp16 [t][16], 4 pieces per lane.
+struct RevDy {
+    int voff[4], loff[4];
+    uint4 a[2][4];
+    __device__ void init(int ls, const RevWalk& w) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = j * 64 + ls, t = i >> 2, c4 = i & 3;
+            voff[j] = static_cast<int>((static_cast<unsigned>(t) * static_cast<unsigned>(w.rowv) + w.hv + 4u * c4) * 4u);
+            loff[j] = t * 16 + 4 * c4;
+        }
+    }
+    template <int set>
+    __device__ void load(const RevWalk& w, int chunk) {
+        const bool live = chunk >= 0 && chunk < w.nchunks;
+        const long t0 = static_cast<long>(chunk) * C;
+        const rsrc_t r = rev_rsrc(w.dy, t0 * w.rowv * 4, (w.T - t0) * w.rowv * 4, live);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[set][j] = bload16(r, voff[j]);
+    }
+    template <int set, int buf, int DK>
+    __device__ void store(RevSmem<DK>& sm) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<half4*>(&sm.dY[buf][loff[j]]) = to_h4(__builtin_bit_cast(float4v, a[set][j]));
+    }
+};
+
+// Loader schedules.  State data (k, T, gates): the opening stores chunk
+// n - 1 and has the next two in flight; period p stores the chunk of period
+// p + 1 and loads the one of period p + 3.  Helper data (q, P, dY, scale
+// gamma): the opening stores the chunks of periods 0 and 1; period p stores
+// the chunk of period p + 2 and loads the one of period p + 4.  Loads past
+// either end read zeros.
+template <class L>
+__device__ __forceinline__ void rev_state_schedule(L& ld, int n) {
+    ld.template load<0>(n - 1);
+    ld.template load<1>(n - 2);
+    ld.template store<0, 0>();
+    ld.template load<0>(n - 3);
+    period_end();
+    period_end();
+    int p = 0;
+    for (; p + 1 <= n; p += 2) {
+        ld.template store<1, 1>();
+        ld.template load<1>(n - 4 - p);
+        period_end();
+        ld.template store<0, 0>();
+        ld.template load<0>(n - 5 - p);
+        period_end();
+    }
+    if (p <= n) {
+        ld.template store<1, 1>();
+        ld.template load<1>(n - 4 - p);
+        period_end();
+    }
+}
+template <class L>
+__device__ __forceinline__ void rev_help_schedule(L& ld, int n) {
+    ld.template load<0>(n - 1);
+    ld.template load<1>(n - 2);
+    ld.template store<0, 0>();
+    ld.template store<1, 1>();
+    ld.template load<0>(n - 3);
+    ld.template load<1>(n - 4);
+    period_end();
+    period_end();
+    int p = 0;
+    for (; p + 1 <= n; p += 2) {
+        ld.template store<0, 0>();
+        ld.template load<0>(n - 5 - p);
+        period_end();
+        ld.template store<1, 1>();
+        ld.template load<1>(n - 6 - p);
+        period_end();
+    }
+    if (p <= n) {
+        ld.template store<0, 0>();
+        ld.template load<0>(n - 5 - p);
+        period_end();
+    }
+}
+
+// Wave 4: k.  Wave 5: T and the state wave's gates.  Wave 6: q.  Wave 7: P,
+// the dY slice and scale gamma.
+template <int DK>
+struct RevLoadK {
+    RevRows<DK, false> rows;
+    RevSmem<DK>* sm;
+    const RevWalk* w;
+    template <int set> __device__ void load(int chunk) { rows.template load<set>(*w, chunk); }
+    template <int set, int buf> __device__ void store() { rows.template store<set, buf>(*sm); }
+};
+template <int DK>
+struct RevLoadT {
+    RevTile<DK, false> tile;
+    RevGates gt;
+    RevSmem<DK>* sm;
+    const RevWalk* w;
+    int lane;
+    template <int set> __device__ void load(int chunk) {
+        tile.template load<set>(*w, chunk);
+        gt.template load<set>(*w, chunk, lane, true);
+    }
+    template <int set, int buf> __device__ void store() {
+        tile.template store<set, buf>(*sm);
+        const float g = gt.g[set], gl = gt.gl[set];
+        sm->gate[buf][lane] = __expf(gl - g);
+        sm->gate[buf][C + lane] = -gt.b[set] * __expf(g);
+        if (lane == 0) sm->gate[buf][2 * C] = __expf(gl);
+    }
+};
+template <int DK>
+struct RevLoadQ {
+    RevRows<DK, true> rows;
+    RevSmem<DK>* sm;
+    const RevWalk* w;
+    template <int set> __device__ void load(int chunk) { rows.template load<set>(*w, chunk); }
+    template <int set, int buf> __device__ void store() { rows.template store<set, buf>(*sm); }
+};
+template <int DK>
+struct RevLoadP {
+    RevTile<DK, true> tile;
+    RevDy dyl;
+    RevGates gt;
+    RevSmem<DK>* sm;
+    const RevWalk* w;
+    int lane;
+    template <int set> __device__ void load(int chunk) {
+        tile.template load<set>(*w, chunk);
+        dyl.template load<set>(*w, chunk);
+        gt.template load<set>(*w, chunk, lane, false);
+    }
+    template <int set, int buf> __device__ void store() {
+        tile.template store<set, buf>(*sm);
+        dyl.template store<set, buf>(*sm);
+        sm->hg[buf][lane] = w->scale * __expf(gt.g[set]);
+    }
+};
+
+// One chunk of the dS chain (the chunk's data in buffer `buf`).
+template <int DK, int buf>
+__device__ __forceinline__ void rev_chunk(RevSmem<DK>& sm, StateRegs<DK>& st, int lane) {
+    constexpr int KS = DK / 32, NST = DK / 16;
+    const int lr = lane & 15, lq = lane >> 4;
+    const _Float16* Kb = sm.K[buf];
+    const float* gate = sm.gate[buf];
+    // dS' out, for the copy wave
+#pragma unroll
+    for (int r = 0; r < NST; ++r) sm.SS[buf][r][lane] = st.S[r];
+    // K dS' for the four token blocks
+    float4v kd[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) kd[I] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+            kd[I] = mma(ld8<DK>(Kb + I * 16 * DK, lr, 8 * ks_chunk<DK>(kk, lq)), st.Sb[kk], kd[I]);
+    // the update's accumulator input: gamma_last dS' + Q^T (scale gamma dY)
+    const float gl = gate[2 * C];
+#pragma unroll
+    for (int r = 0; r < NST; ++r) st.S[r] = gl * st.S[r] + sm.QB[buf][r][lane];
+    // dE = scale P^T dY + lam o K dS'
+    half4 eh[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+        const float4v lam = *reinterpret_cast<const float4v*>(&gate[I * 16 + 4 * lq]);
+        const float4v pd = sm.PdY[buf][I][lane];
+        eh[I] = to_h4(pd[0] + lam[0] * kd[I][0], pd[1] + lam[1] * kd[I][1], pd[2] + lam[2] * kd[I][2],
+                      pd[3] + lam[3] * kd[I][3]);
+    }
+    const half8 Eb0 = cat(eh[0], eh[1]), Eb1 = cat(eh[2], eh[3]);
+    // dR = T^T dE; T^T is upper triangular, so row blocks 2 and 3 see only
+    // tokens 32 .. 63
+    float4v dr[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+        dr[I] = mma(ld_tn<C>(sm.Tm[buf], I, 1, lane), Eb1, float4v{0.f, 0.f, 0.f, 0.f});
+        if (I < 2) dr[I] = mma(ld_tn<C>(sm.Tm[buf], I, 0, lane), Eb0, dr[I]);
+    }
+#pragma unroll
+    for (int I = 0; I < NB; ++I) sm.SR[buf][I][lane] = dr[I];
+    // -beta gamma o dR, the B operand of the update
+    half4 bh[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+        const float4v nb = *reinterpret_cast<const float4v*>(&gate[C + I * 16 + 4 * lq]);
+        bh[I] = to_h4(nb * dr[I]);
+    }
+    const half8 Bb0 = cat(bh[0], bh[1]), Bb1 = cat(bh[2], bh[3]);
+#pragma unroll
+    for (int r = 0; r < NST; ++r) st.S[r] = mma(ld_kt<DK>(Kb, r, 0, lane), Bb0, st.S[r]);
+#pragma unroll
+    for (int r = 0; r < NST; ++r) st.S[r] = mma(ld_kt<DK>(Kb, r, 1, lane), Bb1, st.S[r]);
+    state_refresh_operand(st);
+}
+
+// Helper h (0, 1) on the chunk in buffer hb: Q^T (scale gamma dY) for half
+// of the state's tiles, and (helper 0) scale P^T dY.
+template <int DK, int kHelper>
+__device__ __forceinline__ void rev_helper(RevSmem<DK>& sm, int hb, int lane, float scale) {
+    constexpr int NST = DK / 16, R0 = kHelper * NST / 2;
+    const int lr = lane & 15, lq = lane >> 4;
+    half4 dyh[NB], b1[NB];
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+        dyh[J] = ld_tr4(&sm.dY[hb][(J * 16 + 4 * lq + (lr >> 2)) * 16 + 4 * (lr & 3)]);
+        const float4v hg = *reinterpret_cast<const float4v*>(&sm.hg[hb][J * 16 + 4 * lq]);
+        b1[J] = to_h4(hg[0] * static_cast<float>(dyh[J][0]), hg[1] * static_cast<float>(dyh[J][1]),
+                      hg[2] * static_cast<float>(dyh[J][2]), hg[3] * static_cast<float>(dyh[J][3]));
+    }
+    const half8 B0 = cat(b1[0], b1[1]), B1 = cat(b1[2], b1[3]);
+#pragma unroll
+    for (int r = R0; r < R0 + NST / 2; ++r) {
+        float4v acc = mma(ld_kt<DK>(sm.Q[hb], r, 0, lane), B0, float4v{0.f, 0.f, 0.f, 0.f});
+        acc = mma(ld_kt<DK>(sm.Q[hb], r, 1, lane), B1, acc);
+        sm.QB[hb][r][lane] = acc;
+    }
+    if constexpr (kHelper == 0) {
+        const half8 Y0 = cat(dyh[0], dyh[1]), Y1 = cat(dyh[2], dyh[3]);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            float4v acc = mma(ld_tn<C>(sm.P[hb], I, 1, lane), Y1, float4v{0.f, 0.f, 0.f, 0.f});
+            if (I < 2) acc = mma(ld_tn<C>(sm.P[hb], I, 0, lane), Y0, acc);
+            sm.PdY[hb][I][lane] = scale * acc;
+        }
+    }
+}
+
+template <int DK>
+__global__ __launch_bounds__(512) void rev_walk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                       const float* __restrict__ beta, const float* __restrict__ dy,
+                                                       const float* __restrict__ dST, const float* __restrict__ ws_g,
+                                                       const float* __restrict__ ws_T, const float* __restrict__ ws_P,
+                                                       float* __restrict__ ws_dS, float* __restrict__ ws_dR,
+                                                       float* __restrict__ dv_out, float* __restrict__ dS0, int B,
+                                                       int T, int H, int nsl, float scale) {
+    constexpr int DV = DK, NST = DK / 16;
+    __shared__ RevSmem<DK> sm;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+    const int bh = (jx / nsl) * kXcds + xcd;
+    const int slice = jx % nsl;
+    if (bh >= B * H) return;
+    const int b = bh / H, h = bh % H;
+    const int col0 = slice * 16;
+    const long tok0 = static_cast<long>(b) * T;
+    RevWalk w;
+    w.rowq = static_cast<long>(H) * DK;
+    w.rowv = static_cast<long>(H) * DV;
+    w.q = q + tok0 * w.rowq;
+    w.k = k + tok0 * w.rowq;
+    w.beta = beta + tok0 * H + h;
+    w.dy = dy + tok0 * w.rowv;
+    w.T = T;
+    w.H = H;
+    w.nchunks = (T + C - 1) / C;
+    const int n = w.nchunks;
+    w.g = ws_g + static_cast<long>(bh) * n * C;
+    w.Tm = ws_T + static_cast<long>(bh) * n * C * C;
+    w.P = ws_P + static_cast<long>(bh) * n * C * C;
+    w.hq = static_cast<unsigned>(h * DK);
+    w.hv = static_cast<unsigned>(h * DV + col0);
+    w.scale = scale;
+
+    if (wv == 0) {
+        StateRegs<DK> st;
+#pragma unroll
+        for (int r = 0; r < NST; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                st.S[r][j] = dST ? dST[(static_cast<long>(bh) * DK + state_row<DK>(r, lq, j)) * DV + col0 + lr] : 0.f;
+        state_refresh_operand(st);
+        period_end();
+        period_end();
+        int p = 0;
+        for (; p + 1 < n; p += 2) {
+            rev_chunk<DK, 0>(sm, st, lane);
+            period_end();
+            rev_chunk<DK, 1>(sm, st, lane);
+            period_end();
+        }
+        if (p < n) {
+            rev_chunk<DK, 0>(sm, st, lane);
+            period_end();
+        }
+        period_end();   // the copy wave's last period
+        if (dS0) {
+#pragma unroll
+            for (int r = 0; r < NST; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dS0[(static_cast<long>(bh) * DK + state_row<DK>(r, lq, j)) * DV + col0 + lr] = st.S[r][j];
+        }
+    } else if (wv == 1 || wv == 2) {
+        period_end();
+        if (n > 0) {
+            if (wv == 1) rev_helper<DK, 0>(sm, 0, lane, scale);
+            else rev_helper<DK, 1>(sm, 0, lane, scale);
+        }
+        period_end();
+        for (int p = 0; p <= n; ++p) {
+            if (p + 1 < n) {
+                if (wv == 1) rev_helper<DK, 0>(sm, (p + 1) & 1, lane, scale);
+                else rev_helper<DK, 1>(sm, (p + 1) & 1, lane, scale);
+            }
+            period_end();
+        }
+    } else if (wv == 3) {
+        float bcur = 0.f;
+        period_end();
+        period_end();
+        for (int p = 0; p <= n; ++p) {
+            if (p >= 1) {
+                const int c = n - p, cb = (p - 1) & 1;
+                const long bhn = static_cast<long>(bh) * n + c;
+#pragma unroll
+                for (int r = 0; r < NST; ++r) {
+                    const float4v x = sm.SS[cb][r][lane];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        ws_dS[(bhn * DK + state_row<DK>(r, lq, j)) * DV + col0 + lr] = x[j];
+                }
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const float4v x = sm.SR[cb][I][lane];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = I * 16 + 4 * lq + j;
+                        ws_dR[(bhn * C + t) * DV + col0 + lr] = x[j];
+                        const float bt = __shfl(bcur, t);
+                        if (static_cast<long>(c) * C + t < T)
+                            dv_out[((tok0 + static_cast<long>(c) * C + t) * H + h) * DV + col0 + lr] = bt * x[j];
+                    }
+                }
+            }
+            // beta of the chunk copied next period
+            const int cn = n - 1 - p;
+            bcur = 0.f;
+            if (cn >= 0 && static_cast<long>(cn) * C + lane < T) bcur = w.beta[(static_cast<long>(cn) * C + lane) * H];
+            period_end();
+        }
+    } else if (wv == 4) {
+        RevLoadK<DK> ld;
+        ld.rows.init(lane, w);
+        ld.sm = &sm;
+        ld.w = &w;
+        rev_state_schedule(ld, n);
+    } else if (wv == 5) {
+        RevLoadT<DK> ld;
+        ld.tile.init(lane);
+        ld.sm = &sm;
+        ld.w = &w;
+        ld.lane = lane;
+        rev_state_schedule(ld, n);
+    } else if (wv == 6) {
+        RevLoadQ<DK> ld;
+        ld.rows.init(lane, w);
+        ld.sm = &sm;
+        ld.w = &w;
+        rev_help_schedule(ld, n);
+    } else {
+        RevLoadP<DK> ld;
+        ld.tile.init(lane);
+        ld.dyl.init(lane, w);
+        ld.sm = &sm;
+        ld.w = &w;
+        ld.lane = lane;
+        rev_help_schedule(ld, n);
+    }
+}
+
 template <int DK>
 static hipError_t launch_t(const PrefillArgs& a, float* save_S = nullptr, float* save_E = nullptr) {
     using Cfg = MainCfg<DK>;
@@ -1255,6 +1776,29 @@ hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E) 
         case 128: return chunked::launch_t<128>(a, S, E);
         default: return hipErrorInvalidValue;
     }
+}
+
+// The backward's reverse walk (see rev_walk_kernel); d in {64, 128}.
+hipError_t launch_bwd_reverse_walk(const RevWalkArgs& a) {
+    if (a.T <= 0) return hipSuccess;
+    const int nsl = a.d / 16;
+    const int groups = (a.B * a.H + chunked::kXcds - 1) / chunked::kXcds;
+    const dim3 grid(groups * chunked::kXcds * nsl);
+    switch (a.d) {
+        case 64:
+            hipLaunchKernelGGL((chunked::rev_walk_kernel<64>), grid, dim3(512), 0, a.stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.beta, a.dy,
+                               a.dST, a.g, a.Tm, a.P, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
+            break;
+        case 128:
+            hipLaunchKernelGGL((chunked::rev_walk_kernel<128>), grid, dim3(512), 0, a.stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.beta, a.dy,
+                               a.dST, a.g, a.Tm, a.P, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a) {
