@@ -145,14 +145,17 @@ struct QsaSelectArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
-// Chunk-start states S_c ([B H nchunks][d][d] fp32) and E_c ([B H nchunks][64][d]
-// fp32) of the bf16 chunked walk, without y; d_k = d_v in {64, 128}; the
-// workspace as for launch_prefill_bf16.
+// Chunk-start states S_c ([B H nchunks][d][d]) and E_c ([B H nchunks][64][d]),
+// as fp16 at the start of the given fp32-sized buffers, from the bf16 chunked
+// walk without y; d_k = d_v in {64, 128}; the workspace as for
+// launch_prefill_bf16.
 hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E);
 
 // The backward's reverse walk for bf16 inputs (d_k = d_v = d in {64, 128}):
-// dS' per chunk, dR per chunk, dv and d_initial_state, from the backward
-// workspace's g, T and P (fp32, [B H nchunks] x 64, x 64 x 64).
+// dS' per chunk and dR per chunk (as fp16, laid out as their fp32 slots,
+// at the slots' start), dv and d_initial_state (fp32), from the backward
+// workspace's g (fp32, [B H nchunks] x 64) and T slots ([B H nchunks] x 16 KB,
+// holding fp16 T then fp16 P, 64 x 64 each).
 struct RevWalkArgs {
     const void* q;
     const void* k;
@@ -161,7 +164,6 @@ struct RevWalkArgs {
     const float* dST;            // may be null
     const float* g;
     const float* Tm;
-    const float* P;
     float* dS;
     float* dR;
     float* dv;

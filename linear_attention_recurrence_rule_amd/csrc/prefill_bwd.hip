@@ -423,6 +423,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
             const float pv = row >= col ? gam * qk[u][j] : 0.f;
             gM[row * C + col] = m;
             gP[row * C + col] = pv;
+            // bf16 inputs, d >= 64: the reverse walk reads fp16 P from the
+            // second half of the chunk's T slot
+            if constexpr (kBf16 && DK >= 64) reinterpret_cast<_Float16*>(ws_T + bhn * C * C)[C * C + row * C + col] = pv;
             sQA[row * LDA + col] = sb[row] * m;
         }
     }
@@ -479,14 +482,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
         }
         __syncthreads();
     }
-    // T out, zero above the diagonal blocks
+    // T out, zero above the diagonal blocks (fp16 in the first half of the
+    // slot for bf16 inputs with d >= 64, where only the reverse walk reads it)
     float* gT = ws_T + bhn * C * C;
 #pragma unroll
     for (int it = 0; it < C * C / 4 / 256; ++it) {
         const int idx = tid + 256 * it, row = idx / (C / 4), c4 = 4 * (idx % (C / 4));
         float4v v = *reinterpret_cast<const float4v*>(&sT[row * LDT + c4]);
         if (c4 / 16 > row / 16) v = float4v{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<float4v*>(&gT[row * C + c4]) = v;
+        if constexpr (kBf16 && DK >= 64)
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(gT) + row * C + c4) = to_h4(v);
+        else
+            *reinterpret_cast<float4v*>(&gT[row * C + c4]) = v;
     }
 }
 
@@ -856,21 +863,32 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         const int hr = tid >> 3, hc = tid & 7;            // row item: row hr, columns 4 hc ..
         const int tgh = c * C + hr, tch = tgh < T ? tgh : T - 1;
         const long rowh = (static_cast<long>(b) * T + tch) * H + h;
+        // S, dS, E and dR come as fp16 (the walks for bf16 inputs store them
+        // rounded, at the start of their fp32-sized slots)
+        const _Float16* S16 = reinterpret_cast<const _Float16*>(ws_S);
+        const _Float16* dS16 = reinterpret_cast<const _Float16*>(ws_dS);
+        const _Float16* E16 = reinterpret_cast<const _Float16*>(ws_E);
+        const _Float16* dR16 = reinterpret_cast<const _Float16*>(ws_dR);
         struct SlabH {
-            float4v dy, dr, e, s[NSI], ds[NSI];
+            float4v dy;
+            half4 dr, e, s[NSI], ds[NSI];
             Raw4<true> v;
         };
         SlabH f[kDepthH];
         auto fetch = [&](SlabH& x, int v0) {
             x.dy = *reinterpret_cast<const float4v*>(&dy[rowh * D + v0 + 4 * hc]);
             x.v = raw_load<true>(v, rowh * D + v0 + 4 * hc);
-            x.dr = *reinterpret_cast<const float4v*>(&ws_dR[(bhn * C + hr) * D + v0 + 4 * hc]);
-            x.e = *reinterpret_cast<const float4v*>(&ws_E[(bhn * C + hr) * D + v0 + 4 * hc]);
+            x.dr = *reinterpret_cast<const half4*>(&dR16[(bhn * C + hr) * D + v0 + 4 * hc]);
+            x.e = *reinterpret_cast<const half4*>(&E16[(bhn * C + hr) * D + v0 + 4 * hc]);
 #pragma unroll
             for (int i = 0; i < NSI; ++i) {
-                x.s[i] = *reinterpret_cast<const float4v*>(&ws_S[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
-                x.ds[i] = *reinterpret_cast<const float4v*>(&ws_dS[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
+                x.s[i] = *reinterpret_cast<const half4*>(&S16[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
+                x.ds[i] = *reinterpret_cast<const half4*>(&dS16[(bhn * D + hr + 64 * i) * D + v0 + 4 * hc]);
             }
+        };
+        auto f32 = [](half4 hv) {
+            return float4v{static_cast<float>(hv[0]), static_cast<float>(hv[1]), static_cast<float>(hv[2]),
+                           static_cast<float>(hv[3])};
         };
 #pragma unroll
         for (int s = 0; s < kDepthH; ++s) fetch(f[s], s * SH);
@@ -881,15 +899,16 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 float4v xdy = x.dy, xv = raw_cvt<true>(x.v);
                 if (tgh >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
                 *reinterpret_cast<half4*>(&hY[hr * LDH + 4 * hc]) = to_h4(xdy);
-                *reinterpret_cast<half4*>(&hR[hr * LDH + 4 * hc]) = to_h4(x.dr);
-                *reinterpret_cast<half4*>(&hE[hr * LDH + 4 * hc]) = to_h4(x.e);
-                drv += x.dr.x * xv.x + x.dr.y * xv.y + x.dr.z * xv.z + x.dr.w * xv.w;
+                *reinterpret_cast<half4*>(&hR[hr * LDH + 4 * hc]) = x.dr;
+                *reinterpret_cast<half4*>(&hE[hr * LDH + 4 * hc]) = x.e;
+                const float4v dr = f32(x.dr);
+                drv += dr.x * xv.x + dr.y * xv.y + dr.z * xv.z + dr.w * xv.w;
 #pragma unroll
                 for (int i = 0; i < NSI; ++i) {
-                    *reinterpret_cast<half4*>(&hS[(hr + 64 * i) * LDH + 4 * hc]) = to_h4(x.s[i]);
-                    *reinterpret_cast<half4*>(&hD[(hr + 64 * i) * LDH + 4 * hc]) = to_h4(x.ds[i]);
-                    sds += x.s[i].x * x.ds[i].x + x.s[i].y * x.ds[i].y + x.s[i].z * x.ds[i].z +
-                           x.s[i].w * x.ds[i].w;
+                    *reinterpret_cast<half4*>(&hS[(hr + 64 * i) * LDH + 4 * hc]) = x.s[i];
+                    *reinterpret_cast<half4*>(&hD[(hr + 64 * i) * LDH + 4 * hc]) = x.ds[i];
+                    const float4v sv = f32(x.s[i]), dsv = f32(x.ds[i]);
+                    sds += sv.x * dsv.x + sv.y * dsv.y + sv.z * dsv.z + sv.w * dsv.w;
                 }
             }
             if (s == 0) {
@@ -1223,7 +1242,6 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a) {
         ra.dST = a.d_final_state;
         ra.g = g;
         ra.Tm = Tm;
-        ra.P = P;
         ra.dS = dS;
         ra.dR = dR;
         ra.dv = a.dv;

@@ -1087,11 +1087,11 @@ __device__ __forceinline__ void output_role(MainSmem<DK>& sm, const Walk& w, int
 }
 
 // Copy role of the state-saving walk: wave I writes rows I DK / 4 .. of S_p
-// and tokens 16 I .. 16 I + 15 of E_p (fp32, row-major [row][column] as the
-// backward pass reads them) in period p + 1, from the buffers the state wave
-// filled in period p.
+// and tokens 16 I .. 16 I + 15 of E_p (rounded to fp16, row-major
+// [row][column] as the backward pass reads them) in period p + 1, from the
+// buffers the state wave filled in period p.
 template <int DK>
-__device__ __forceinline__ void copy_role(const SaveBufs<DK>* sv, const Walk& w, float* ws_S, float* ws_E,
+__device__ __forceinline__ void copy_role(const SaveBufs<DK>* sv, const Walk& w, _Float16* ws_S, _Float16* ws_E,
                                           long bhn0, int DV, int col0, int I, int lane) {
     constexpr int RW = DK / 4;                 // state rows per copy wave
     const int c4 = lane & 3, lrow = lane >> 2;
@@ -1107,13 +1107,13 @@ __device__ __forceinline__ void copy_role(const SaveBufs<DK>* sv, const Walk& w,
                 float4v x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = sv->S[buf][4 * c4 + e][row];
-                *reinterpret_cast<float4v*>(&ws_S[(bhn * DK + row) * DV + col0 + 4 * c4]) = x;
+                *reinterpret_cast<half4*>(&ws_S[(bhn * DK + row) * DV + col0 + 4 * c4]) = to_h4(x);
             }
             const int tok = I * 16 + lrow;
             float4v x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = sv->E[buf][4 * c4 + e][tok];
-            *reinterpret_cast<float4v*>(&ws_E[(bhn * C + tok) * DV + col0 + 4 * c4]) = x;
+            *reinterpret_cast<half4*>(&ws_E[(bhn * C + tok) * DV + col0 + 4 * c4]) = to_h4(x);
         }
         period_end();
     }
@@ -1172,7 +1172,8 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
     } else if (wv == 1 || wv == 2 || wv == 5 || wv == 6) {
         const int blk = wv == 1 ? 3 : (wv == 5 ? 0 : (wv == 2 ? 2 : 1));
         if constexpr (kSave) {
-            copy_role<DK>(&sv, w, ws_S, ws_E, static_cast<long>(bh) * w.nchunks, DV, col0, blk, lane);
+            copy_role<DK>(&sv, w, reinterpret_cast<_Float16*>(ws_S), reinterpret_cast<_Float16*>(ws_E),
+                          static_cast<long>(bh) * w.nchunks, DV, col0, blk, lane);
         } else {
             if (blk == 3) output_role<DK, 3>(sm, w, lane);
             else if (blk == 0) output_role<DK, 0>(sm, w, lane);
@@ -1208,8 +1209,9 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
 // (d_k x 16, fp32) held in the accumulator registers of one wave, in the
 // forward state wave's row order.  With g the chunk's cumulative log decay,
 // gamma = exp(g), lam = exp(g_last - g), T = (I + A)^-1 and the masked gated
-// Gram P = Gamma o (Q K^T) (the backward's chunk-parallel pass stores g, T
-// and P), chunk c turns dS' (the gradient of the state after the chunk) into
+// Gram P = Gamma o (Q K^T) (the backward's chunk-parallel pass stores g, and
+// T and P as fp16 in each chunk's T slot), chunk c turns dS' (the gradient of
+// the state after the chunk) into
 //     dE = scale P^T dY + diag(lam) K dS'
 //     dR = T^T dE                              (dV = diag(beta) dR)
 //     dS = gamma_last dS' + Q^T (scale diag(gamma) dY) - K^T (diag(beta gamma) dR)
@@ -1220,8 +1222,10 @@ __global__ __launch_bounds__(512) void main_kernel(const uint16_t* __restrict__ 
 //   1, 2  helpers: scale P^T dY and Q^T (scale gamma dY) of the next chunk
 //         (neither depends on dS), left in LDS as accumulator tiles
 //   3     copy: dS' (the gradient workspace), dR and dV of the previous chunk
-//   4, 5  loaders of the next chunk's k, and T with the gates
-//   6, 7  loaders of q, and P, the dY slice and scale gamma, two chunks ahead
+//   7, 5  loaders of the next chunk's k, and T with the gates
+//   6, 4  loaders of q, and P, the dY slice and scale gamma, two chunks ahead
+//         (the k conversion, the heaviest loader work, stays off the state
+//         wave's SIMD)
 // Two barriers open the walk (the loaders' first stores, then the helpers'
 // first chunk); then one ends each of the n + 1 periods.  Period p processes
 // chunk n - 1 - p.
@@ -1238,8 +1242,8 @@ struct alignas(16) RevSmem {
     float hg[2][C];               // scale gamma
     float4v PdY[2][NB][64];       // scale P^T dY, accumulator tiles, lane-major
     float4v QB[2][NST][64];       // Q^T (scale gamma dY), the state's tiles, lane-major
-    float4v SS[2][NST][64];       // dS' of the chunk, for the copy wave
-    float4v SR[2][NB][64];        // dR of the chunk
+    float SS[2][16][DK + 4];      // dS' of the chunk, [column][d_k row], for the copy wave
+    float SR[2][16][C + 4];       // dR of the chunk, [column][token]
 };
 
 struct RevWalk {
@@ -1248,8 +1252,7 @@ struct RevWalk {
     const float* beta;        // this sequence and head: beta[t * H]
     const float* dy;          // this sequence's rows
     const float* g;           // this head's chunks in the backward workspace
-    const float* Tm;
-    const float* P;
+    const float* Tm;          // T slots: fp16 T, then fp16 P
     long rowq, rowv;
     unsigned hq, hv;          // element offsets of the head (q, k) and the slice (dy)
     int H, T, nchunks;
@@ -1301,33 +1304,33 @@ struct RevRows {
     }
 };
 
-// fp32 64 x 64 workspace tile (T or P) -> fp16 swizzled tile, 16 pieces per lane.
+// fp16 64 x 64 workspace tile (T, or P in the second half of the chunk's T
+// slot) -> swizzled LDS tile, 8 pieces per lane.
 template <int DK, bool kP>
 struct RevTile {
-    int loff[16];
+    int loff[8];
     int lane;
-    uint4 a[2][16];
+    uint4 a[2][8];
     __device__ void init(int ls) {
         lane = ls;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 8; ++j) {
             const int i = j * 64 + ls;
-            loff[j] = swz<C>(i >> 4, 4 * (i & 15));
+            loff[j] = swz<C>(i >> 3, 8 * (i & 7));
         }
     }
     template <int set>
     __device__ void load(const RevWalk& w, int chunk) {
         const bool live = chunk >= 0 && chunk < w.nchunks;
-        const rsrc_t r = rev_rsrc(kP ? w.P : w.Tm, static_cast<long>(chunk) * C * C * 4, C * C * 4, live);
+        const rsrc_t r = rev_rsrc(w.Tm, static_cast<long>(chunk) * C * C * 4 + (kP ? C * C * 2 : 0), C * C * 2, live);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) a[set][j] = bload16(r, (j * 64 + lane) * 16);
+        for (int j = 0; j < 8; ++j) a[set][j] = bload16(r, (j * 64 + lane) * 16);
     }
     template <int set, int buf>
     __device__ void store(RevSmem<DK>& sm) const {
         _Float16* dst = kP ? sm.P[buf] : sm.Tm[buf];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            *reinterpret_cast<half4*>(&dst[loff[j]]) = to_h4(__builtin_bit_cast(float4v, a[set][j]));
+        for (int j = 0; j < 8; ++j) st16(&dst[loff[j]], a[set][j]);
     }
 };
 
@@ -1431,7 +1434,7 @@ __device__ __forceinline__ void rev_help_schedule(L& ld, int n) {
     }
 }
 
-// Wave 4: k.  Wave 5: T and the state wave's gates.  Wave 6: q.  Wave 7: P,
+// Wave 7: k.  Wave 5: T and the state wave's gates.  Wave 6: q.  Wave 4: P,
 // the dY slice and scale gamma.
 template <int DK>
 struct RevLoadK {
@@ -1495,9 +1498,9 @@ __device__ __forceinline__ void rev_chunk(RevSmem<DK>& sm, StateRegs<DK>& st, in
     const int lr = lane & 15, lq = lane >> 4;
     const _Float16* Kb = sm.K[buf];
     const float* gate = sm.gate[buf];
-    // dS' out, for the copy wave
+    // dS' out, for the copy wave (tile r, lane group lq: 4 consecutive rows)
 #pragma unroll
-    for (int r = 0; r < NST; ++r) sm.SS[buf][r][lane] = st.S[r];
+    for (int r = 0; r < NST; ++r) *reinterpret_cast<float4v*>(&sm.SS[buf][lr][state_row<DK>(r, lq, 0)]) = st.S[r];
     // K dS' for the four token blocks
     float4v kd[NB];
 #pragma unroll
@@ -1530,7 +1533,7 @@ __device__ __forceinline__ void rev_chunk(RevSmem<DK>& sm, StateRegs<DK>& st, in
         if (I < 2) dr[I] = mma(ld_tn<C>(sm.Tm[buf], I, 0, lane), Eb0, dr[I]);
     }
 #pragma unroll
-    for (int I = 0; I < NB; ++I) sm.SR[buf][I][lane] = dr[I];
+    for (int I = 0; I < NB; ++I) *reinterpret_cast<float4v*>(&sm.SR[buf][lr][I * 16 + 4 * lq]) = dr[I];
     // -beta gamma o dR, the B operand of the update
     half4 bh[NB];
 #pragma unroll
@@ -1582,7 +1585,7 @@ template <int DK>
 __global__ __launch_bounds__(512) void rev_walk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                        const float* __restrict__ beta, const float* __restrict__ dy,
                                                        const float* __restrict__ dST, const float* __restrict__ ws_g,
-                                                       const float* __restrict__ ws_T, const float* __restrict__ ws_P,
+                                                       const float* __restrict__ ws_T,
                                                        float* __restrict__ ws_dS, float* __restrict__ ws_dR,
                                                        float* __restrict__ dv_out, float* __restrict__ dS0, int B,
                                                        int T, int H, int nsl, float scale) {
@@ -1610,7 +1613,6 @@ __global__ __launch_bounds__(512) void rev_walk_kernel(const uint16_t* __restric
     const int n = w.nchunks;
     w.g = ws_g + static_cast<long>(bh) * n * C;
     w.Tm = ws_T + static_cast<long>(bh) * n * C * C;
-    w.P = ws_P + static_cast<long>(bh) * n * C * C;
     w.hq = static_cast<unsigned>(h * DK);
     w.hv = static_cast<unsigned>(h * DV + col0);
     w.scale = scale;
@@ -1659,40 +1661,57 @@ __global__ __launch_bounds__(512) void rev_walk_kernel(const uint16_t* __restric
             period_end();
         }
     } else if (wv == 3) {
-        float bcur = 0.f;
-        period_end();
-        period_end();
-        for (int p = 0; p <= n; ++p) {
+        // dS' and dR go out rounded to fp16 (the gradient pass takes them as
+        // fp16 operands)
+        _Float16* dS16 = reinterpret_cast<_Float16*>(ws_dS);
+        _Float16* dR16 = reinterpret_cast<_Float16*>(ws_dR);
+        // period p loads beta of the chunk copied in period p + 1 into one
+        // register and copies with the other (the loop runs in pairs, so no
+        // register move waits for the load)
+        auto copy_period = [&](int p, float& bload, const float& buse) {
+            // issued before this period's stores: memory operations retire in
+            // order, so a load issued after them would wait for them
+            const int cn = n - 1 - p;
+            const rsrc_t rb = rev_rsrc(w.beta, static_cast<long>(cn) * C * H * 4,
+                                       (T - static_cast<long>(cn) * C) * H * 4, cn >= 0);
+            bload = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
             if (p >= 1) {
-                const int c = n - p, cb = (p - 1) & 1;
+                // 16-byte row pieces: lane (4 row + c4) writes columns 4 c4 .. 4 c4 + 3
+                const int c = n - p, cb = (p - 1) & 1, c4 = lane & 3, lrow = lane >> 2;
                 const long bhn = static_cast<long>(bh) * n + c;
 #pragma unroll
-                for (int r = 0; r < NST; ++r) {
-                    const float4v x = sm.SS[cb][r][lane];
+                for (int hh = 0; hh < DK / 16; ++hh) {
+                    const int row = 16 * hh + lrow;
+                    float4v x;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        ws_dS[(bhn * DK + state_row<DK>(r, lq, j)) * DV + col0 + lr] = x[j];
+                    for (int e = 0; e < 4; ++e) x[e] = sm.SS[cb][4 * c4 + e][row];
+                    *reinterpret_cast<half4*>(&dS16[(bhn * DK + row) * DV + col0 + 4 * c4]) = to_h4(x);
                 }
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    const float4v x = sm.SR[cb][I][lane];
+                for (int hh = 0; hh < NB; ++hh) {
+                    const int t = 16 * hh + lrow;
+                    float4v x;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = I * 16 + 4 * lq + j;
-                        ws_dR[(bhn * C + t) * DV + col0 + lr] = x[j];
-                        const float bt = __shfl(bcur, t);
-                        if (static_cast<long>(c) * C + t < T)
-                            dv_out[((tok0 + static_cast<long>(c) * C + t) * H + h) * DV + col0 + lr] = bt * x[j];
-                    }
+                    for (int e = 0; e < 4; ++e) x[e] = sm.SR[cb][4 * c4 + e][t];
+                    *reinterpret_cast<half4*>(&dR16[(bhn * C + t) * DV + col0 + 4 * c4]) = to_h4(x);
+                    const float bt = __shfl(buse, t);
+                    if (static_cast<long>(c) * C + t < T)
+                        *reinterpret_cast<float4v*>(&dv_out[((tok0 + static_cast<long>(c) * C + t) * H + h) * DV + col0 +
+                                                            4 * c4]) = bt * x;
                 }
             }
-            // beta of the chunk copied next period
-            const int cn = n - 1 - p;
-            bcur = 0.f;
-            if (cn >= 0 && static_cast<long>(cn) * C + lane < T) bcur = w.beta[(static_cast<long>(cn) * C + lane) * H];
             period_end();
+        };
+        float b0 = 0.f, b1 = 0.f;
+        period_end();
+        period_end();
+        int p = 0;
+        for (; p + 1 <= n; p += 2) {
+            copy_period(p, b0, b1);
+            copy_period(p + 1, b1, b0);
         }
-    } else if (wv == 4) {
+        if (p <= n) copy_period(p, b0, b1);
+    } else if (wv == 7) {
         RevLoadK<DK> ld;
         ld.rows.init(lane, w);
         ld.sm = &sm;
@@ -1711,7 +1730,7 @@ __global__ __launch_bounds__(512) void rev_walk_kernel(const uint16_t* __restric
         ld.sm = &sm;
         ld.w = &w;
         rev_help_schedule(ld, n);
-    } else {
+    } else {   // wave 4
         RevLoadP<DK> ld;
         ld.tile.init(lane);
         ld.dyl.init(lane, w);
@@ -1766,9 +1785,9 @@ size_t prefill_bf16_workspace_bytes(int B, int T, int H) {
     return chunked::kStatusBytes + static_cast<size_t>(B) * H * nchunks * chunked::WS_CHUNK * sizeof(_Float16);
 }
 
-// The chunk-start states and E of every chunk (fp32, [b h chunk][d_k][d_v]
-// and [b h chunk][token][d_v]) from the same walk, for the backward pass;
-// y is not formed.  d_k = d_v >= 64.
+// The chunk-start states and E of every chunk ([b h chunk][d_k][d_v] and
+// [b h chunk][token][d_v], rounded to fp16) from the same walk, for the
+// backward pass; y is not formed.  d_k = d_v >= 64.
 hipError_t launch_prefill_bf16_states(const PrefillArgs& a, float* S, float* E) {
     if (a.dk != a.dv) return hipErrorInvalidValue;
     switch (a.dk) {
@@ -1788,12 +1807,12 @@ hipError_t launch_bwd_reverse_walk(const RevWalkArgs& a) {
         case 64:
             hipLaunchKernelGGL((chunked::rev_walk_kernel<64>), grid, dim3(512), 0, a.stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.beta, a.dy,
-                               a.dST, a.g, a.Tm, a.P, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
+                               a.dST, a.g, a.Tm, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
             break;
         case 128:
             hipLaunchKernelGGL((chunked::rev_walk_kernel<128>), grid, dim3(512), 0, a.stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.beta, a.dy,
-                               a.dST, a.g, a.Tm, a.P, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
+                               a.dST, a.g, a.Tm, a.dS, a.dR, a.dv, a.dS0, a.B, a.T, a.H, nsl, a.scale);
             break;
         default:
             return hipErrorInvalidValue;
