@@ -462,7 +462,9 @@ def main():
         b_ms = e0.elapsed_time(e1) / n_b
         bb, bf = bwd_bytes(B, T, H, dk, dv), bwd_flops(B, T, H, dk)
         result["backward"] = {"workload": f"backward of the long prefill, B={B} T={T} H={H} d={dk}, bf16 inputs, "
-                                          "fp32 gradients", "kernels": "bwd_prep, bwd_states, bwd_dstates, bwd_grads",
+                                          "fp32 gradients",
+                              "kernels": "bwd_prep; prep_kernel + main_kernel in its state-saving mode (chunk-start "
+                                         "states); rev_walk_kernel (state gradients); bwd_grads",
                               "avg_call_ms": b_ms, "tokens_per_s": B * T / (b_ms * 1e-3),
                               "algorithmic_bytes": bb, "GBps": bb / (b_ms * 1e-3) / 1e9,
                               "hbm_frac": bb / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,

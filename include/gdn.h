@@ -260,7 +260,9 @@ gdn_status gdn_decode_mtp_commit_verify(const void* q, const void* k, const void
  *                  gdn_prefill_bwd_workspace_bytes(...) bytes, 16-byte aligned
  *                  (per 64-token chunk and head: the chunk's T, P and M
  *                  matrices, its start state and end-state gradient, and two
- *                  64 x d_v products, all float32)
+ *                  64 x d_v products, each in a float32-sized slot; for bf16
+ *                  inputs with d >= 64 the states, products, T and a copy of P
+ *                  are kept as fp16 in the first half of their slots)
  *   d_k == d_v in {16, 32, 64, 128}.  With T == 0 only d_initial_state is
  *   written (a copy of d_final_state, or zeros); no workspace is needed.
  */
