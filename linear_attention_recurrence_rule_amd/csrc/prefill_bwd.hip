@@ -301,6 +301,25 @@ struct RowTile {
             }
         }
     }
+    // The transpose as fp16, [d][token] with leading dimension ld.  Rows
+    // past T (clamped copies of the last row, so finite) are zeroed by a
+    // factor rather than a select, which the compiler may turn into a branch
+    // with the prefetched load sunk into it.
+    __device__ __forceinline__ void store_t(_Float16* s, int ld, int c, int T) const {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int i = threadIdx.x + NT * m;
+            // (no run-time check where the items divide evenly: a branch here
+            // would also take the prefetched load into it)
+            if (kItems % NT == 0 || i < kItems) {
+                const int t = i / (D / 4), c4 = i - t * (D / 4);
+                const float live = c * C + t < T ? 1.f : 0.f;
+                const float4v x = raw_cvt<kBf16>(r[m]) * live;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[(4 * c4 + e) * ld + t] = static_cast<_Float16>(x[e]);
+            }
+        }
+    }
 };
 
 // A C x C float32 chunk matrix of the workspace, register-staged the same way.
@@ -813,8 +832,14 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     constexpr int kPMFloats = 2 * C * LDX;
     constexpr int kRegion = kSlabFloats > kPMFloats ? kSlabFloats : kPMFloats;
     __shared__ __align__(16) float sR[kRegion];
-    __shared__ __align__(16) float sQ[C * LDK];
-    __shared__ __align__(16) float sK[C * LDK];
+    // q and k: fp32 row-major for the fp32-operand path; for bf16 inputs
+    // with d >= 64, their fp16 transposes [d][token] (leading dimension LDT)
+    constexpr bool kH = kBf16 && D >= 64;
+    constexpr int LDT = C + 8;
+    __shared__ __align__(16) float sQ[kH ? 4 : C * LDK];
+    __shared__ __align__(16) float sK[kH ? 4 : C * LDK];
+    __shared__ __align__(16) _Float16 hQt[kH ? D * LDT : 8];
+    __shared__ __align__(16) _Float16 hKt[kH ? D * LDT : 8];
     __shared__ __align__(16) float sX4[C * LDX];    // X4, then dP o Gamma
     __shared__ __align__(16) float sX5[C * LDX];    // X5, then Dm
     __shared__ float sg[C], sb[C], sa[C];
@@ -835,7 +860,15 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     for (int u = 0; u < 2; ++u) x4[u] = x5[u] = float4v{0.f, 0.f, 0.f, 0.f};
     float drv = 0.f, sds = 0.f;
 
-    // phase-2 operands are loaded into registers first
+    // per-token values and phase-2 operands are loaded into registers first
+    float pre_a = 1.f, pre_b = 0.f, pre_g = 0.f;
+    if (tid < C) {
+        const int tg = c * C + tid;
+        const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
+        pre_a = alpha[gi];
+        pre_b = beta[gi];
+        pre_g = ws_g[bhn * C + tid];
+    }
     RowTile<D, 512, kBf16> tq, tk;
     MatTile<512> tp, tm;
     tq.load(q, b, c, T, H, h);
@@ -896,8 +929,10 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
         for (int s = 0; s < NSH; ++s) {
             SlabH& x = f[s % kDepthH];
             {
-                float4v xdy = x.dy, xv = raw_cvt<true>(x.v);
-                if (tgh >= T) xdy = xv = float4v{0.f, 0.f, 0.f, 0.f};
+                // rows past T (clamped copies of the last row) zeroed by a
+                // factor: a select may become a branch with the load sunk into it
+                const float live = tgh < T ? 1.f : 0.f;
+                const float4v xdy = x.dy * live, xv = raw_cvt<true>(x.v) * live;
                 *reinterpret_cast<half4*>(&hY[hr * LDH + 4 * hc]) = to_h4(xdy);
                 *reinterpret_cast<half4*>(&hR[hr * LDH + 4 * hc]) = x.dr;
                 *reinterpret_cast<half4*>(&hE[hr * LDH + 4 * hc]) = x.e;
@@ -912,8 +947,8 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 }
             }
             if (s == 0) {
-                tq.store(sQ, LDK, c, T);
-                tk.store(sK, LDK, c, T);
+                tq.store_t(hQt, LDT, c, T);
+                tk.store_t(hKt, LDT, c, T);
             }
             __syncthreads();
             if (s + kDepthH < NSH) fetch(x, (s + kDepthH) * SH);
@@ -1025,11 +1060,9 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
     tm.store(sM, LDX);
     if (tid < C) {
         const int tg = c * C + tid;
-        const long gi = (static_cast<long>(b) * T + (tg < T ? tg : T - 1)) * H + h;
-        const float a = alpha[gi], be = beta[gi];
-        sg[tid] = ws_g[bhn * C + tid];
-        sb[tid] = tg < T ? be : 0.f;
-        sa[tid] = tg < T ? a : 1.f;
+        sg[tid] = pre_g;
+        sb[tid] = tg < T ? pre_b : 0.f;
+        sa[tid] = tg < T ? pre_a : 1.f;
         sQX1[tid] = sKX2[tid] = sKX3[tid] = 0.f;
     }
     if (tid == 0) sSdS = 0.f;
@@ -1060,9 +1093,17 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j;
-                const float a1 = dpp_sum16(sQ[row * LDK + col] * x1[u][j]);
-                const float a2 = dpp_sum16(sK[row * LDK + col] * x2[u][j]);
-                const float a3 = dpp_sum16(sK[row * LDK + col] * x3[u][j]);
+                float qv, kv;
+                if constexpr (kH) {
+                    qv = static_cast<float>(hQt[col * LDT + row]);
+                    kv = static_cast<float>(hKt[col * LDT + row]);
+                } else {
+                    qv = sQ[row * LDK + col];
+                    kv = sK[row * LDK + col];
+                }
+                const float a1 = dpp_sum16(qv * x1[u][j]);
+                const float a2 = dpp_sum16(kv * x2[u][j]);
+                const float a3 = dpp_sum16(kv * x3[u][j]);
                 if ((l & 15) == 0) {
                     atomicAdd(&sQX1[row], a1);
                     atomicAdd(&sKX2[row], a2);
@@ -1138,6 +1179,24 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
             dalpha[gi] = __logf(a) >= kLogFloor ? x / a : 0.f;
         }
     }
+    // bf16 inputs, d >= 64: G = dP o Gamma, its transpose and Dm + Dm^T as
+    // fp16 tiles (in the slab region: P and M are no longer read), so that
+    // every operand of the dq and dk contractions is one 16-byte LDS read
+    _Float16* hG = reinterpret_cast<_Float16*>(sR);
+    _Float16* hGt = hG + C * LDT;
+    _Float16* hDs = hGt + C * LDT;
+    if constexpr (kH) {
+        static_assert(3 * C * LDT * 2 <= kRegion * 4, "fp16 G tiles fit the slab region");
+        __syncthreads();                                   // every read of P and M is done
+        for (int idx = tid; idx < C * C; idx += 512) {
+            const int t = idx / C, i = idx - t * C;
+            const float gv = sX4[t * LDX + i];
+            hG[t * LDT + i] = static_cast<_Float16>(gv);
+            hGt[i * LDT + t] = static_cast<_Float16>(gv);
+            hDs[t * LDT + i] = static_cast<_Float16>(sX5[t * LDX + i] + sX5[i * LDX + t]);
+        }
+        __syncthreads();
+    }
     // dq and dk tiles
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
@@ -1152,9 +1211,19 @@ __global__ __launch_bounds__(512) void bwd_grads_kernel(
                 aq[j] = scale * gam * x1[u][j];
                 ak[j] = lam * x3[u][j] - sb[row] * gam * x2[u][j];
             }
-            aq = mma_x<kBf16, false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
-            ak = mma_sym_x<kBf16, C>(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, ak);
-            ak = mma_x<kBf16, true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
+            if constexpr (kH) {
+#pragma unroll
+                for (int ks = 0; ks < C / 32; ++ks) {
+                    const half8 bK = frag_h(&hKt[16 * tj * LDT + 32 * ks], LDT);
+                    aq = mma_hh(frag_h(&hG[16 * ti * LDT + 32 * ks], LDT), bK, aq);
+                    ak = mma_hh(frag_h(&hDs[16 * ti * LDT + 32 * ks], LDT), bK, ak);
+                    ak = mma_hh(frag_h(&hGt[16 * ti * LDT + 32 * ks], LDT), frag_h(&hQt[16 * tj * LDT + 32 * ks], LDT), ak);
+                }
+            } else {
+                aq = mma_x<kBf16, false, true, C>(&sX4[16 * ti * LDX], LDX, &sK[16 * tj], LDK, 0, aq);   // dP o Gamma: lower
+                ak = mma_sym_x<kBf16, C>(sX5, LDX, 16 * ti, &sK[16 * tj], LDK, 0, ak);
+                ak = mma_x<kBf16, true, true, C>(&sX4[16 * ti], LDX, &sQ[16 * tj], LDK, 0, ak);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * ti + 4 * (l >> 4) + j, tg = c * C + row;
