@@ -3,10 +3,11 @@
 // mixer output, per (token, head) row of d_v values:
 //     out = sigmoid(z) * y / sqrt(mean(y^2) + eps) * (1 + w)
 // A pure stream (read y and z, write out once), bound by HBM bandwidth.
-// Each row is handled by d_v/8 lanes holding 8 values each (two 16-byte y
-// loads, one 16-byte z load and one 16-byte store for bf16); the row's sum of
-// squares is reduced with DPP lane moves inside the lane group, so no LDS is
-// used.  A thread covers kNormPasses rows and loads all of them before
+// Each row is handled by d_v/8 lanes holding 8 values each: lane `sub` takes
+// columns 4 sub .. 4 sub + 3 of each half of the row, so that every load and
+// store instruction covers whole contiguous lines of y, z and out.  The row's
+// sum of squares is reduced with DPP lane moves inside the lane group, so no
+// LDS is used.  A thread covers kNormPasses rows and loads all of them before
 // reducing any.
 #include <type_traits>
 
@@ -49,14 +50,16 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
 #pragma unroll
     for (int p = 0; p < kNormPasses; ++p) {
         const long row = row0 + p * kRowsPerPass;
-        const long base = (row < rows ? row : rows - 1) * DV + sub * 8;   // clamped; not stored
+        // columns 4 sub .. 4 sub + 3 (values 0..3) and DV / 2 + 4 sub .. (values 4..7)
+        const long base = (row < rows ? row : rows - 1) * DV + sub * 4;   // clamped; not stored
         const float4 y0 = *reinterpret_cast<const float4*>(y + base);
-        const float4 y1 = *reinterpret_cast<const float4*>(y + base + 4);
+        const float4 y1 = *reinterpret_cast<const float4*>(y + base + DV / 2);
         yv[p][0] = y0.x; yv[p][1] = y0.y; yv[p][2] = y0.z; yv[p][3] = y0.w;
         yv[p][4] = y1.x; yv[p][5] = y1.y; yv[p][6] = y1.z; yv[p][7] = y1.w;
         if constexpr (kBf16) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(z) + base);
-            const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint2 r0 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(z) + base);
+            const uint2 r1 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(z) + base + DV / 2);
+            const uint32_t wds[4] = {r0.x, r0.y, r1.x, r1.y};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 zv[p][2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xffffu));
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
             }
         } else {
             const float4 z0 = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base);
-            const float4 z1 = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base + 4);
+            const float4 z1 = *reinterpret_cast<const float4*>(static_cast<const float*>(z) + base + DV / 2);
             zv[p][0] = z0.x; zv[p][1] = z0.y; zv[p][2] = z0.z; zv[p][3] = z0.w;
             zv[p][4] = z1.x; zv[p][5] = z1.y; zv[p][6] = z1.z; zv[p][7] = z1.w;
         }
@@ -73,8 +76,8 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = 0.f;
     if (weight) {
-        const float4 w0 = reinterpret_cast<const float4*>(weight)[2 * sub];
-        const float4 w1 = reinterpret_cast<const float4*>(weight)[2 * sub + 1];
+        const float4 w0 = reinterpret_cast<const float4*>(weight)[sub];
+        const float4 w1 = reinterpret_cast<const float4*>(weight + DV / 2)[sub];
         w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
         w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
     }
@@ -94,18 +97,19 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const float* __restr
             const float gate = __builtin_amdgcn_rcpf(1.0f + __expf(-zv[p][i]));
             o[i] = gate * (yv[p][i] * inv) * (1.0f + w[i]);
         }
-        const long base = row * DV + sub * 8;
+        const long base = row * DV + sub * 4;
         // streaming stores: the output is not read again here
         if constexpr (kBf16) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            __builtin_nontemporal_store(u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                                              pack_bf16x2(o[6], o[7])},
-                                        reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + base));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
+                                        reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base));
+            __builtin_nontemporal_store(u32x2{pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])},
+                                        reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base + DV / 2));
         } else {
             __builtin_nontemporal_store(float4v{o[0], o[1], o[2], o[3]},
                                         reinterpret_cast<float4v*>(static_cast<float*>(out) + base));
             __builtin_nontemporal_store(float4v{o[4], o[5], o[6], o[7]},
-                                        reinterpret_cast<float4v*>(static_cast<float*>(out) + base + 4));
+                                        reinterpret_cast<float4v*>(static_cast<float*>(out) + base + DV / 2));
         }
     }
 }
