@@ -38,10 +38,19 @@ struct Lane {
     typedef float Vec __attribute__((ext_vector_type(N)));
 };
 
+// A lane's 16 bytes as loaded, and converted to floats.  Prefetched rows stay
+// raw until the step that uses them, so that the conversion does not wait
+// for a load just issued.
 template <bool kBf16>
-__device__ __forceinline__ typename Lane<kBf16>::Vec loadv(const void* p, long i) {
+using Raw = typename std::conditional<kBf16, uint4, float4v>::type;
+template <bool kBf16>
+__device__ __forceinline__ Raw<kBf16> loadr(const void* p, long i) {
+    if constexpr (kBf16) return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    else return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
+}
+template <bool kBf16>
+__device__ __forceinline__ typename Lane<kBf16>::Vec cvt(const Raw<kBf16>& r) {
     if constexpr (kBf16) {
-        const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
         typename Lane<kBf16>::Vec v;
 #pragma unroll
@@ -51,8 +60,12 @@ __device__ __forceinline__ typename Lane<kBf16>::Vec loadv(const void* p, long i
         }
         return v;
     } else {
-        return *reinterpret_cast<const float4v*>(static_cast<const float*>(p) + i);
+        return r;
     }
+}
+template <bool kBf16>
+__device__ __forceinline__ typename Lane<kBf16>::Vec loadv(const void* p, long i) {
+    return cvt<kBf16>(loadr<kBf16>(p, i));
 }
 
 template <bool kBf16>
@@ -123,18 +136,40 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 #pragma unroll
         for (int j = 0; j < W; ++j) wt[j][c] = w[(static_cast<long>(h) * D + NC * sub + c) * W + j];
 
-    // the W-1 rows before t0: from the sequence, the caller's history, or zero
-    Vec win[W > 1 ? W - 1 : 1];
+    // kStep tokens per step, independent of each other given the inputs, so
+    // their reductions overlap; the next step's rows are loaded meanwhile.
+    // Offsets inside the run are 32-bit (a run spans kRun rows).
+    const int last = t1 - 1 - t0;
+    const int rs = static_cast<int>(row_stride);
+    const long run_base = base + t0 * row_stride;
+    using R = Raw<kBf16>;
+    auto load_rows = [&](R (&r)[kStep], int r0) {
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) {
-        const int t = t0 - (W - 1) + j;
-        if (t >= 0) {
-            win[j] = loadv<kBf16>(x, base + t * row_stride);
-        } else if (hist) {
-            const long hb = ((static_cast<long>(b) * (W - 1) + (W - 1 + t)) * H + h) * D + NC * sub;
-            win[j] = loadv<kBf16>(hist, hb);
-        } else {
-            win[j] = Vec{};
+        for (int u = 0; u < kStep; ++u) r[u] = loadr<kBf16>(x, run_base + min(r0 + u, last) * rs);
+    };
+    // the run's first rows go out first, ahead of the window rows
+    R ra[kStep], rb[kStep];
+    load_rows(ra, 0);
+
+    // the W-1 rows before t0: from the sequence, the caller's history, or
+    // zero.  Both loads are issued with clamped indices and the choice made
+    // afterwards, so that the loads overlap instead of each waiting in a branch.
+    Vec win[W > 1 ? W - 1 : 1];
+    {
+        Raw<kBf16> rx[W > 1 ? W - 1 : 1], rh[W > 1 ? W - 1 : 1];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const int t = t0 - (W - 1) + j;
+            rx[j] = loadr<kBf16>(x, base + (t >= 0 ? t : 0) * row_stride);
+            if (hist) {
+                const int slot = t < 0 ? W - 1 + t : 0;
+                rh[j] = loadr<kBf16>(hist, ((static_cast<long>(b) * (W - 1) + slot) * H + h) * D + NC * sub);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const int t = t0 - (W - 1) + j;
+            win[j] = t >= 0 ? cvt<kBf16>(rx[j]) : (hist ? cvt<kBf16>(rh[j]) : Vec{});
         }
     }
 
@@ -152,18 +187,13 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
         }
     }
 
-    // kStep tokens per step, independent of each other given the inputs, so
-    // their reductions overlap; the next step's rows are loaded meanwhile.
-    // Offsets inside the run are 32-bit (a run spans kRun rows).
-    const int last = t1 - 1 - t0;
-    const int rs = static_cast<int>(row_stride);
-    const long run_base = base + t0 * row_stride;
-    auto load_rows = [&](Vec (&r)[kStep], int r0) {
+    // every step loads the next one's rows (clamped to the run's last row, so
+    // the loads are unconditional and the wait counts exact)
+    auto step = [&](const R (&cur_raw)[kStep], R (&nxt)[kStep], int r0) {
+        load_rows(nxt, r0 + kStep);
+        Vec cur[kStep];
 #pragma unroll
-        for (int u = 0; u < kStep; ++u) r[u] = loadv<kBf16>(x, run_base + min(r0 + u, last) * rs);
-    };
-    auto step = [&](Vec (&cur)[kStep], Vec (&nxt)[kStep], int r0) {
-        if (r0 + kStep <= last) load_rows(nxt, r0 + kStep);
+        for (int u = 0; u < kStep; ++u) cur[u] = cvt<kBf16>(cur_raw[u]);
         Vec s[kStep];
 #pragma unroll
         for (int u = 0; u < kStep; ++u) {
@@ -201,12 +231,13 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
             win[j] = src >= 0 ? cur[src >= 0 ? src : 0] : win[j + kStep < W - 1 ? j + kStep : 0];
         }
     };
-    // steps in pairs over two register sets, so that no copies are needed
-    Vec ra[kStep], rb[kStep];
-    load_rows(ra, 0);
-    for (int r0 = 0; r0 <= last; r0 += 2 * kStep) {
-        step(ra, rb, r0);
-        if (r0 + kStep <= last) step(rb, ra, r0 + kStep);
+    // the run's steps unrolled over two register sets, so that no copies are
+    // needed (steps past a short run's last row compute on clamped rows and
+    // store nothing)
+#pragma unroll
+    for (int k = 0; k < kRun / kStep; ++k) {
+        if (k % 2 == 0) step(ra, rb, k * kStep);
+        else step(rb, ra, k * kStep);
     }
     if constexpr (kGates) {
         const float ea = __expf(A[h]), ba = b_alpha[h];
