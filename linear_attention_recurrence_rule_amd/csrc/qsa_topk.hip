@@ -37,6 +37,8 @@
 #include "gdn_launch.hpp"
 #include "qsa_wave.hpp"
 
+#include <type_traits>
+
 namespace gdn {
 namespace qsa {
 
@@ -46,7 +48,9 @@ constexpr int kTB = 64;              // key blocks per tile
 constexpr int kHB = 256;             // histogram bins per query
 
 // sum over the four heads of ReLU(score); ReLU as a signed-integer max with 0
-// on the bit pattern (negative floats, -0 included, are negative integers)
+// on the bit pattern (negative floats, -0 included, are negative integers).
+// Each term is +0 or a positive float, so the sum has its sign bit clear and
+// its bit pattern orders like its value.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 __device__ __forceinline__ float relu_sum(const float4v& a) {
     return relu(a[0]) + relu(a[1]) + relu(a[2]) + relu(a[3]);
@@ -255,10 +259,10 @@ __device__ __forceinline__ int sampled_tile(int j) { return 8 * j + ((5 * j) & 7
 //     shared; the uncapped lengths are kept, which catches an overflow.
 // ---------------------------------------------------------------------------
 template <int D, bool kBf16, bool kEmit>
-__global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__ q, const void* __restrict__ kbar,
-                                                        const float* __restrict__ kmax, uint2* __restrict__ info,
-                                                        int* __restrict__ cnt, uint2* __restrict__ list, int n,
-                                                        int r, int nb, int KB, int cap) {
+__global__ __launch_bounds__(256, kBf16 ? 2 : 1)   // bf16: two workgroups per CU
+void qsa_pass4_kernel(const void* __restrict__ q, const void* __restrict__ kbar, const float* __restrict__ kmax,
+                      uint2* __restrict__ info, int* __restrict__ cnt, uint2* __restrict__ list, int n, int r,
+                      int nb, int KB, int cap) {
     constexpr int ES = kBf16 ? 2 : 4;
     constexpr int LD = D + (kBf16 ? 8 : 4);
     constexpr int kVec = 16 / ES;                    // elements per 16-byte load
@@ -295,12 +299,11 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
     auto tile_of = [&](int j) { return sampled ? sampled_tile(j) : j; };
 
     int lo[MT];
-    unsigned tlo[MT], thi[MT];
+    unsigned tlo[MT];                                // emit pass: 0xFFFFFFFF (above every sum) keeps nothing
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         lo[mt] = 0;
-        tlo[mt] = 0u;
-        thi[mt] = 0xFFFFFFFFu;
+        tlo[mt] = 0xFFFFFFFFu;
     }
     if constexpr (!kEmit) {
         // bound: sum_h |q^h| max_j |kbar_j|; lanes r = 4 u + h of group mt hold (query u, head h)
@@ -317,14 +320,18 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
         for (int j = l; j < 4 * MT * kHB; j += 64) sH[4 * MT * wave + j / kHB][j % kHB] = 0u;
     } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (act[mt]) {
-                const uint2 t = info[static_cast<long>(b) * n + qi[mt]];
-                tlo[mt] = t.x;
-                thi[mt] = t.y;
-            }
-        }
+        for (int mt = 0; mt < MT; ++mt)
+            if (act[mt]) tlo[mt] = info[static_cast<long>(b) * n + qi[mt]].x;
     }
+    // emit pass: this lane's sub-list of each of its queries (the blocks of residue l % 16)
+    uint2* lrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        lrow[mt] = list + ((static_cast<long>(b) * n + (qi[mt] < n ? qi[mt] : 0)) * 16 + (l & 15)) * cap;
+    // the wave's first query sees the fewest blocks: a tile below its count is
+    // visible to all the wave's queries
+    const int q_lo = i0 + 4 * MT * wave;
+    const int vis_lo = q_lo < n ? (q_lo + 1) / r : 0;
     unsigned zc[MT];                                 // histogram pass: zeros seen by this lane
     int nl[MT];                                      // emit pass: this lane's sub-list lengths
 #pragma unroll
@@ -349,33 +356,44 @@ __global__ __launch_bounds__(256) void qsa_pass4_kernel(const void* __restrict__
             *reinterpret_cast<float4v*>(sK[buf] + (rr * LD + c * kVec) * ES) = p[u];
         }
     };
+    // emit pass: the blocks of one tile with u >= tlo go to the lane sub-lists;
+    // a full tile (one every query of the wave sees whole) needs no per-block bound
+    auto emit = [&](const float4v (&acc)[MT][4], int b0, auto full) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int blk = b0 + 16 * nt + (l & 15);
+                const unsigned u = __float_as_uint(relu_sum(acc[mt][nt]));
+                const bool keep = u >= tlo[mt] && (decltype(full)::value || blk < vis[mt]);
+                if (keep && nl[mt] < cap)
+                    lrow[mt][static_cast<unsigned>(nl[mt])] = make_uint2(u, static_cast<unsigned>(blk));
+                nl[mt] += static_cast<int>(keep);
+            }
+        }
+    };
     // step j: scores of key tile tile_of(j) from LDS buffer j & 1
     auto step = [&](int j, int buf) {
         const int bt = tile_of(j);                   // may pass nbt in the last sampled group
         const int b0 = bt * kTB;
         float4v acc[MT][4];
         tile_scores<D, kBf16, LD, MT>(f, sK[buf], l, acc);
+        if constexpr (!kEmit) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int blk = b0 + 16 * nt + (l & 15);
-                const unsigned u = __float_as_uint(relu_sum(acc[mt][nt])) & 0x7FFFFFFFu;
-                const bool valid = act[mt] && blk < vis[mt];
-                if constexpr (!kEmit) {
-                    if (valid) {
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int blk = b0 + 16 * nt + (l & 15);
+                    const unsigned u = __float_as_uint(relu_sum(acc[mt][nt]));
+                    if (act[mt] && blk < vis[mt]) {
                         if (u == 0u) ++zc[mt];
                         else atomicAdd(&sH[4 * MT * wave + 4 * mt + g][ubin(u, lo[mt])], 1u);
                     }
-                } else {
-                    // lane sub-list (query, l % 16): blocks of that residue mod 16
-                    const bool keep = valid && u >= tlo[mt];
-                    if (keep && nl[mt] < cap)
-                        list[((static_cast<long>(b) * n + qi[mt]) * 16 + (l & 15)) * cap + nl[mt]] =
-                            make_uint2(u, static_cast<unsigned>(blk));
-                    nl[mt] += keep ? 1 : 0;
                 }
             }
+        } else {
+            if (b0 + kTB <= vis_lo) emit(acc, b0, std::true_type{});
+            else emit(acc, b0, std::false_type{});
         }
     };
     fetch(pre[0], tile_of(0));
