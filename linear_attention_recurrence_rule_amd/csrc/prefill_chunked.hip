@@ -297,10 +297,13 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
         {
             const int bd = lq, c = lr;
             const float* Ab = sm.Ad + bd * ABLK;
+            // x[t] = 0 for t < c and x[c] = 1 exactly (every earlier x is 0);
+            // the selection below keeps the loop-invariant identity column out of
+            // registers (as 16 constants it had pushed the kernel into a spill)
             float x[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float s0 = (t == c) ? 1.f : 0.f, s1 = 0.f;
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
                 for (int i4 = 0; i4 < (t + 3) / 4; ++i4) {
                     const float4v a4 = *reinterpret_cast<const float4v*>(&Ab[t * LDA + 4 * i4]);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
                         }
                     }
                 }
-                x[t] = s0 + s1;
+                x[t] = (t == c) ? 1.f : s0 + s1;
             }
             const float bc = sm.beta[l];
             half8 lo, hi;
