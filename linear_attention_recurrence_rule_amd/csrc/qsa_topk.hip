@@ -458,8 +458,9 @@ void qsa_pass4_kernel(const void* __restrict__ q, const void* __restrict__ kbar,
 // query's 16 sub-lists hold every block with u >= tlo; those with u >= thi
 // are taken outright, the rest are candidates.  The candidates are gathered
 // (LDS) and held in registers (slot t of lane l: candidate 64 t + l); the
-// need = K_B - (outright count) largest bit patterns are found by bisection,
-// and among the ties at the cut the later blocks (bisection on the index).
+// need-th largest bit pattern, need = K_B - (outright count), is found by
+// radix selection, 10 bits a round, and among the ties at the cut the later
+// blocks are taken (bisection on the index).
 // The taken blocks are marked in an LDS bitmap, 16384 blocks at a time, and
 // written out in ascending order.  A band that missed (need outside
 // [1, candidates]) or an overflowing sub-list queues the query.
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(256, 4) void qsa_merge_kernel(const uint2* __restri
         for (int j = lane; j < KB; j += 64) out[j] = j < m ? j : -1;
         return;
     }
-    __shared__ unsigned sKey[4][kCapB];
+    __shared__ __align__(16) unsigned sKey[4][kCapB];
     __shared__ int sBlk[4][kCapB];
     __shared__ unsigned long long sMap[4][kMapWords];
     const unsigned thi = info[row].y;
@@ -582,14 +583,37 @@ __global__ __launch_bounds__(256, 4) void qsa_merge_kernel(const uint2* __restri
             if (t < ns) c += static_cast<unsigned>(__popcll(__ballot(bi[t] >= 0 && pred(key[t], bi[t]))));
         return c;
     };
-    // the need-th largest key: count(key >= lo) >= need > count(key >= hi)
-    unsigned lo = kmn, hi = kmx + 1u;
-    while (hi - lo > 1u) {
-        const unsigned mid = lo + (hi - lo) / 2u;
-        if (count_if([&](unsigned k, int) { return k >= mid; }) >= static_cast<unsigned>(need)) lo = mid;
-        else hi = mid;
+    // the need-th largest key T, count(key > T) < need <= count(key >= T), by
+    // radix selection on key - base: a 1024-bin histogram of the keys still in
+    // [base, base + rng] (in this wave's sKey row, free now that the
+    // candidates are in registers), then the bin that holds the rank-th
+    // largest becomes the range; a range of at most 1024 values is decided
+    // exactly.  Three rounds cover the usual band of about 2^21 patterns.
+    static_assert(kCapB == 1024, "the histogram takes one sKey row");
+    unsigned* hist = sKey[w];
+    unsigned base = kmn, rng = kmx - kmn;
+    unsigned rank = static_cast<unsigned>(need);     // from the top, inside the range
+    for (;;) {
+        const int bits = rng ? 32 - __clz(static_cast<int>(rng)) : 0;
+        const int shift = bits > 10 ? bits - 10 : 0;
+        wave_sync();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) reinterpret_cast<uint4*>(hist)[lane * 4 + j] = make_uint4(0u, 0u, 0u, 0u);
+        wave_sync();
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t) {
+            const unsigned d = key[t] - base;        // keys below base wrap past rng
+            if (t < ns && bi[t] >= 0 && d <= rng) atomicAdd(&hist[d >> shift], 1u);
+        }
+        wave_sync();
+        unsigned above;
+        const unsigned bin = wave_threshold(hist, kCapB / 64, rank, &above);
+        rank -= above;
+        base += bin << shift;
+        if (shift == 0) break;
+        rng = min(rng - (bin << shift), (1u << shift) - 1u);
     }
-    const unsigned T = lo;
+    const unsigned T = base;
     const unsigned take_eq = static_cast<unsigned>(need) - count_if([&](unsigned k, int) { return k > T; });
     // among the keys equal to T, the take_eq latest blocks: largest X with count(idx >= X) >= take_eq
     // (X = 0 when every one of them is taken, the usual case)
