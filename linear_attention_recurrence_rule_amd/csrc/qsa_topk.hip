@@ -23,8 +23,8 @@
 //                     tlo are listed (bit pattern, block) in per-lane
 //                     sub-lists of the query.
 //   qsa_merge_kernel  one wave per query: the K_B - (outright count) best
-//                     candidates are found by bisection on the bit patterns
-//                     (ties to the later block), and the union with the
+//                     candidates are found by radix selection on the bit
+//                     patterns (ties to the later block), and the union with the
 //                     outright blocks goes out ascending through an LDS
 //                     bitmap.  A band that missed (too few or too many taken
 //                     outright) or an overflowing list queues the query.
