@@ -11,7 +11,7 @@
 // sqrt(sum(x^2) + eps) over the head dimension.
 //
 // One pass per stream (q, k, v), each a pure stream over its input and output
-// (HBM-bound).  A row group of lanes owns one (sequence, head) and a run of
+// (HBM-bound); with d_k = d_v the three passes run as one launch.  A row group of lanes owns one (sequence, head) and a run of
 // kRun consecutive tokens; each lane owns 16 bytes of a row (8 bf16 or 4
 // fp32 channels), keeps its filter
 // taps and the last W-1 input rows in registers and slides along the run
@@ -104,21 +104,21 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+// One block of a stream pass: row groups blk * RPB .. of the stream.
 template <int D, int W, bool kNorm, bool kGates, bool kBf16>
-__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x, const float* __restrict__ w,
-                                                     const void* __restrict__ hist, void* __restrict__ out,
-                                                     const float* __restrict__ a_logit,
-                                                     const float* __restrict__ b_logit,
-                                                     const float* __restrict__ A, const float* __restrict__ b_alpha,
-                                                     float* __restrict__ alpha, float* __restrict__ beta, int B,
-                                                     int T, int H, float eps) {
+__device__ __forceinline__ void stream_block(const void* __restrict__ x, const float* __restrict__ w,
+                                             const void* __restrict__ hist, void* __restrict__ out,
+                                             const float* __restrict__ a_logit, const float* __restrict__ b_logit,
+                                             const float* __restrict__ A, const float* __restrict__ b_alpha,
+                                             float* __restrict__ alpha, float* __restrict__ beta, int B, int T, int H,
+                                             float eps, long blk) {
     using Vec = typename Lane<kBf16>::Vec;
     constexpr int NC = Lane<kBf16>::N;      // channels per lane
     constexpr int LPR = D / NC;             // lanes per row
     constexpr int RPB = 256 / LPR;          // row groups per block
     const int tid = threadIdx.x;
     const int sub = tid % LPR;
-    const long task = static_cast<long>(blockIdx.x) * RPB + tid / LPR;
+    const long task = blk * RPB + tid / LPR;
     const int nruns = (T + kRun - 1) / kRun;
     const int h = static_cast<int>(task % H);
     const long rest = task / H;
@@ -254,10 +254,52 @@ __global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x,
 }
 
 template <int D, int W, bool kNorm, bool kGates, bool kBf16>
-static hipError_t launch_stream(const void* x, const float* w, const void* hist, void* out, const FrontendArgs& a) {
-    constexpr int RPB = 256 / (D / Lane<kBf16>::N);
+__global__ __launch_bounds__(256) void stream_kernel(const void* __restrict__ x, const float* __restrict__ w,
+                                                     const void* __restrict__ hist, void* __restrict__ out,
+                                                     const float* __restrict__ a_logit,
+                                                     const float* __restrict__ b_logit,
+                                                     const float* __restrict__ A, const float* __restrict__ b_alpha,
+                                                     float* __restrict__ alpha, float* __restrict__ beta, int B,
+                                                     int T, int H, float eps) {
+    stream_block<D, W, kNorm, kGates, kBf16>(x, w, hist, out, a_logit, b_logit, A, b_alpha, alpha, beta, B, T, H,
+                                             eps, blockIdx.x);
+}
+
+// All three passes in one launch when d_k = d_v: blocks [0, nb) are q's,
+// [nb, 2 nb) k's and [2 nb, 3 nb) v's, so the passes share one grid and
+// one tail instead of three.
+template <int D, int W, bool kBf16>
+__global__ __launch_bounds__(256) void qkv_kernel(const FrontendArgs a, long nb) {
+    const long bx = blockIdx.x;
+    if (bx < 2 * nb) {                               // block-uniform
+        const bool isq = bx < nb;
+        stream_block<D, W, true, false, kBf16>(isq ? a.q_proj : a.k_proj, isq ? a.conv_q : a.conv_k,
+                                               isq ? a.q_hist : a.k_hist, isq ? a.q : a.k, nullptr, nullptr,
+                                               nullptr, nullptr, nullptr, nullptr, a.B, a.T, a.H, a.eps,
+                                               isq ? bx : bx - nb);
+    } else {
+        stream_block<D, W, false, true, kBf16>(a.v_proj, a.conv_v, a.v_hist, a.v, a.a_logit, a.b_logit, a.A,
+                                               a.b_alpha, a.alpha, a.beta, a.B, a.T, a.H, a.eps, bx - 2 * nb);
+    }
+}
+
+template <int D>
+static long blocks_of(const FrontendArgs& a, int nc) {
     const long tasks = static_cast<long>(a.B) * a.H * ((a.T + kRun - 1) / kRun);
-    const long blocks = (tasks + RPB - 1) / RPB;
+    const int rpb = 256 / (D / nc);
+    return (tasks + rpb - 1) / rpb;
+}
+
+template <int D, int W, bool kBf16>
+static hipError_t launch_qkv(const FrontendArgs& a) {
+    const long nb = blocks_of<D>(a, Lane<kBf16>::N);
+    hipLaunchKernelGGL((qkv_kernel<D, W, kBf16>), dim3(static_cast<unsigned>(3 * nb)), dim3(256), 0, a.stream, a, nb);
+    return hipGetLastError();
+}
+
+template <int D, int W, bool kNorm, bool kGates, bool kBf16>
+static hipError_t launch_stream(const void* x, const float* w, const void* hist, void* out, const FrontendArgs& a) {
+    const long blocks = blocks_of<D>(a, Lane<kBf16>::N);
     hipLaunchKernelGGL((stream_kernel<D, W, kNorm, kGates, kBf16>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        0, a.stream, x, w, hist, out, a.a_logit, a.b_logit, a.A, a.b_alpha, a.alpha, a.beta, a.B, a.T,
                        a.H, a.eps);
@@ -277,6 +319,15 @@ static hipError_t launch_d(int d, const void* x, const float* w, const void* his
 
 template <int W, bool kBf16>
 static hipError_t launch_all(const FrontendArgs& a) {
+    if (a.dk == a.dv) {
+        switch (a.dk) {
+            case 16: return launch_qkv<16, W, kBf16>(a);
+            case 32: return launch_qkv<32, W, kBf16>(a);
+            case 64: return launch_qkv<64, W, kBf16>(a);
+            case 128: return launch_qkv<128, W, kBf16>(a);
+            default: return hipErrorInvalidValue;
+        }
+    }
     hipError_t e = launch_d<W, true, false, kBf16>(a.dk, a.q_proj, a.conv_q, a.q_hist, a.q, a);
     if (e != hipSuccess) return e;
     e = launch_d<W, true, false, kBf16>(a.dk, a.k_proj, a.conv_k, a.k_hist, a.k, a);

@@ -53,7 +53,7 @@ def _compare(got, ref, dtype, label=""):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32), (16, 128), (32, 16)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 32), (16, 128), (32, 16)])
 @pytest.mark.parametrize("width", [1, 2, 4])
 def test_frontend_matches_oracle(dtype, dk, dv, width):
     say(f"frontend dtype={dtype} dk={dk} dv={dv} W={width}")
