@@ -581,7 +581,7 @@ def main():
         fe_ms = e0.elapsed_time(e1) / n_fe
         fe_bytes = B * T * H * ((2 * dk + dv) * 2 * 2 + 4 * 4)
         result["frontend"] = {"workload": f"front end, B={B} T={T} H={H} d={dk}, conv width {W}, bf16",
-                              "kernel": "frontend stream_kernel x3", "avg_call_ms": fe_ms,
+                              "kernel": "frontend qkv_kernel (q, k and v passes in one launch)", "avg_call_ms": fe_ms,
                               "algorithmic_bytes_per_call": fe_bytes,
                               "achieved": fe_bytes / (fe_ms * 1e-3) / 1e9, "unit": "GB/s",
                               "frac": fe_bytes / (fe_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
