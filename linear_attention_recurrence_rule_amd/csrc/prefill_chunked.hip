@@ -112,7 +112,7 @@ __device__ __forceinline__ half8 ld_split_lo(const _Float16* base, int row, int 
 // diagonal blocks and the output.
 // ===========================================================================
 constexpr int kPrepWaves = 4;        // waves (chunks in flight) per workgroup
-constexpr int kPrepResidentWGs = 768; // three workgroups per CU
+constexpr int kPrepGridWGs = 6144;    // workgroups per launch (eight rounds of three per CU) before a wave takes several chunks
 
 template <int DK>
 struct PrepCfg {
@@ -194,9 +194,11 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
 // (x, y) takes head bh = kPrepWaves x + w and its chunks y cpw + j, j < cpw.
 // Neighbouring workgroups run the same chunks of neighbouring heads, so the k
 // rows in flight at one time are whole token rows of the (token, head, d_k)
-// tensor rather than scattered 256-byte pieces.  cpw is chosen so that the
-// grid is about one round of resident workgroups: each wave then pays the
-// latency of its first k load once and hides the others behind its work.
+// tensor rather than scattered 256-byte pieces.  cpw is 1 unless the grid
+// would exceed kPrepGridWGs workgroups: the resident waves of one round then
+// hide the k-load latency of the next (measured 79.5 us at 32 heads x 512
+// chunks, against 89.6 us with six chunks per wave and one round); a wave
+// with several chunks loads the next one while it works on the current.
 // Rows past the end of the sequence load the last row (their beta is 0, so A
 // has zero rows there and they never matter).
 template <int DK>
@@ -1751,11 +1753,11 @@ static hipError_t launch_t(const PrefillArgs& a, float* save_S = nullptr, float*
     unsigned* status = static_cast<unsigned*>(a.workspace);
     _Float16* ws = status ? reinterpret_cast<_Float16*>(static_cast<char*>(a.workspace) + kStatusBytes) : nullptr;
     if (nchunks > 0) {
-        // chunks per wave: about one round of resident workgroups, at most 16
+        // chunks per wave: one, unless the grid would pass kPrepGridWGs; at most 16
         const int BH = a.B * a.H;
         const long gx = (BH + kPrepWaves - 1) / kPrepWaves;
         const int cpw = static_cast<int>(
-            std::min<long>(16, std::max<long>(1, (gx * nchunks + kPrepResidentWGs - 1) / kPrepResidentWGs)));
+            std::min<long>(16, std::max<long>(1, (gx * nchunks + kPrepGridWGs - 1) / kPrepGridWGs)));
         const int gy = (nchunks + cpw - 1) / cpw;
         hipLaunchKernelGGL((prep_kernel<DK>), dim3(static_cast<unsigned>(gx), gy), dim3(256), 0, a.stream,
                            static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, status, a.T, a.H, BH, nchunks,
