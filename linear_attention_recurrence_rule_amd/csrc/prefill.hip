@@ -22,8 +22,9 @@
 // Precision.  bf16 inputs are converted exactly to fp16 (q and k are unit
 // vectors); the Gram products, T, R, E, P and the state copy are fp16 MFMA
 // operands with float32 accumulation; the state, gates and outputs are
-// float32.  The float32 input path runs the same schedule on float32 MFMA
-// with a 32-token chunk (the float32 tiles of a 64-token chunk do not fit LDS).
+// float32.  The float32 input path runs the same schedule on float32 MFMA,
+// with 64-token chunks for d_k <= 32 and 32-token chunks for d_k = 64 and
+// 128, where the float32 tiles of a 64-token chunk do not fit the LDS.
 //
 // Workgroup: 4 waves.  Per chunk (barriers between stages):
 //   0. chunk c's q, k, v, alpha, beta (prefetched into registers during chunk
@@ -432,7 +433,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
 template <int DK, int SV, bool kBf16>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
-    using Cfg = PrefillCfg<DK, SV, kBf16 ? 64 : 32, kBf16>;
+    // C = 64 wherever the float32 tiles fit the 160 KB of LDS (d_k <= 32);
+    // at d_k = 64 and 128 they do not, and the walk takes 32-token chunks
+    using Cfg = PrefillCfg<DK, SV, (kBf16 || DK <= 32) ? 64 : 32, kBf16>;
     const int nsl = a.dv / SV;
     const int groups = (a.B * a.H + kXcds - 1) / kXcds;
     const long blocks = static_cast<long>(groups) * kXcds * nsl;
