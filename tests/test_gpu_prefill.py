@@ -40,6 +40,16 @@ def test_multi_chunk_ragged(dtype, dk, dv):
     run_case(d, dtype, scale=0.5)
 
 
+@pytest.mark.parametrize("B,H,dk,dv", [(3, 44, 32, 32), (2, 40, 16, 64)])
+def test_fp32_wide_slices_many_heads(B, H, dk, dv):
+    """float32 inputs with more than 256 16-column slices, which the fp32 walk
+    covers with 32-column slices (64-token chunks at these d_k), over two
+    chunks and a ragged tail."""
+    say(f"prefill fp32 B={B} H={H} dk={dk} dv={dv}")
+    d = prefill_inputs(B, 64 * 2 + 21, H, dk, dv, "f32", -1.0, 0.5, seed=B * H + dk, state_std=0.05)
+    run_case(d, "f32", scale=0.75)
+
+
 @pytest.mark.parametrize("T", [1, 15, 16, 31, 63, 64, 65, 128, 129])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_lengths_around_chunk_edges(T, dtype):
