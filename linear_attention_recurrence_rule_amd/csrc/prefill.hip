@@ -15,16 +15,15 @@
 // Parallel decomposition.  The recurrence is separable over value columns,
 // so one workgroup owns a slice of SV columns of one (batch, head) state and
 // walks its chunks in order, keeping the float32 state slice in registers for
-// the whole sequence (plus an fp16 copy in LDS as an MFMA operand).  The
+// the whole sequence (plus a copy in LDS as an MFMA operand).  The
 // slices of one head recompute the state-independent Gram products; they are
 // placed on one XCD so that the q/k chunk loads they share hit that XCD's L2.
 //
-// Precision.  bf16 inputs are converted exactly to fp16 (q and k are unit
-// vectors); the Gram products, T, R, E, P and the state copy are fp16 MFMA
-// operands with float32 accumulation; the state, gates and outputs are
-// float32.  The float32 input path runs the same schedule on float32 MFMA,
-// with 64-token chunks for d_k <= 32 and 32-token chunks for d_k = 64 and
-// 128, where the float32 tiles of a 64-token chunk do not fit the LDS.
+// This kernel serves float32 inputs (bf16 inputs take the kernels of
+// prefill_chunked.hip).  Every product runs on float32 MFMA with float32
+// operands and accumulation, with 64-token chunks for d_k <= 32 and 32-token
+// chunks for d_k = 64 and 128, where the float32 tiles of a 64-token chunk do
+// not fit the LDS.
 //
 // Workgroup: 4 waves.  Per chunk (barriers between stages):
 //   0. chunk c's q, k, v, alpha, beta (prefetched into registers during chunk
@@ -47,11 +46,10 @@ namespace gdn {
 constexpr float kLogDecayFloor = -30.0f;
 constexpr int kXcds = 8;
 
-template <int DK_, int SV_, int C_, bool kBf16_>
+template <int DK_, int SV_, int C_>
 struct PrefillCfg {
     static constexpr int DK = DK_, SV = SV_, C = C_;
-    static constexpr bool kBf16 = kBf16_;
-    using Op = std::conditional_t<kBf16, _Float16, float>;
+    using Op = float;
     static constexpr int NW = 4, NT = 256;
     static constexpr int PAD = 16 / sizeof(Op);
     static constexpr int LDQ = DK + PAD;  // rows over d_k (Q, K, S^T)
@@ -64,7 +62,7 @@ struct PrefillCfg {
     static constexpr int NS_TILES = (DK / 16) * NSV;
     static constexpr int NST = (NS_TILES + NW - 1) / NW;   // state tiles per wave
     static constexpr int NYB = (NB + NW - 1) / NW;         // output row blocks per wave
-    static constexpr int EPL = kBf16 ? 8 : 4;              // input elements per 16-byte load
+    static constexpr int EPL = 4;                          // input elements per 16-byte load
     static constexpr int QK_LOADS = (C * DK / EPL + NT - 1) / NT;
     static constexpr int V_LOADS = (C * SV / EPL + NT - 1) / NT;
 };
@@ -89,31 +87,14 @@ struct PrefillSmem {
     float g[Cfg::C], gam[Cfg::C], beta[Cfg::C], dec[Cfg::C];
 };
 
-template <class Op>
-__device__ __forceinline__ void store4(Op* p, float a, float b, float c, float d) {
-    if constexpr (std::is_same_v<Op, _Float16>) {
-        half4 h = {static_cast<_Float16>(a), static_cast<_Float16>(b), static_cast<_Float16>(c),
-                   static_cast<_Float16>(d)};
-        *reinterpret_cast<half4*>(p) = h;
-    } else {
-        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-    }
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-// Expand one 16-byte global load into EPL floats.
-template <bool kBf16>
+// One 16-byte global load as EPL = 4 floats.
 __device__ __forceinline__ void unpack16(const uint4& r, float* out) {
-    if constexpr (kBf16) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-        out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
-        out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
-    }
+    out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
 }
 
 template <class Cfg>
@@ -231,13 +212,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             rg.q[i] = rg.k[i] = make_uint4(0, 0, 0, 0);
             if (idx < C * DK / EPL && t0 + row < T) {
                 const long off = ((tok0 + t0 + row) * H + h) * DK + cv * EPL;
-                if constexpr (Cfg::kBf16) {
-                    rg.q[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
-                    rg.k[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + off);
-                } else {
-                    rg.q[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off);
-                    rg.k[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(k) + off);
-                }
+                rg.q[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off);
+                rg.k[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(k) + off);
             }
         }
 #pragma unroll
@@ -247,10 +223,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             rg.v[i] = make_uint4(0, 0, 0, 0);
             if (idx < C * SV / EPL && t0 + row < T) {
                 const long off = ((tok0 + t0 + row) * H + h) * static_cast<long>(DV) + col0 + cv * EPL;
-                if constexpr (Cfg::kBf16)
-                    rg.v[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(v) + off);
-                else
-                    rg.v[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(v) + off);
+                rg.v[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(v) + off);
             }
         }
         rg.alpha = 1.f;
@@ -269,8 +242,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             if (idx < C * DK / EPL) {
                 const int row = idx / (DK / EPL), c0 = (idx % (DK / EPL)) * EPL;
                 float fq[EPL], fk[EPL];
-                unpack16<Cfg::kBf16>(rg.q[i], fq);
-                unpack16<Cfg::kBf16>(rg.k[i], fk);
+                unpack16(rg.q[i], fq);
+                unpack16(rg.k[i], fk);
 #pragma unroll
                 for (int e = 0; e < EPL; e += 4) {
                     store4(&sm.Q[row * LDQ + c0 + e], fq[e], fq[e + 1], fq[e + 2], fq[e + 3]);
@@ -286,7 +259,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             if (idx < C * SV / EPL) {
                 const int row = idx / (SV / EPL), c0 = (idx % (SV / EPL)) * EPL;
                 float fv[EPL];
-                unpack16<Cfg::kBf16>(rg.v[i], fv);
+                unpack16(rg.v[i], fv);
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) sm.V[row * SV + c0 + e] = fv[e];
             }
@@ -431,11 +404,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
 }
 
-template <int DK, int SV, bool kBf16>
+template <int DK, int SV>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
     // C = 64 wherever the float32 tiles fit the 160 KB of LDS (d_k <= 32);
     // at d_k = 64 and 128 they do not, and the walk takes 32-token chunks
-    using Cfg = PrefillCfg<DK, SV, (kBf16 || DK <= 32) ? 64 : 32, kBf16>;
+    using Cfg = PrefillCfg<DK, SV, DK <= 32 ? 64 : 32>;
     const int nsl = a.dv / SV;
     const int groups = (a.B * a.H + kXcds - 1) / kXcds;
     const long blocks = static_cast<long>(groups) * kXcds * nsl;
@@ -445,24 +418,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-template <int DK, bool kBf16>
+template <int DK>
 static hipError_t launch_prefill_dk(const PrefillArgs& a) {
     // One workgroup per (head, SV-column slice).  Narrow slices spread a few
     // heads over the 256 CUs; once there are enough heads, wider slices cut
     // the Gram work that every slice of a head repeats.
     constexpr int kCUs = 256;
     const long bh = static_cast<long>(a.B) * a.H;
-    if (a.dv >= 32 && bh * (a.dv / 16) > kCUs) return launch_prefill_t<DK, 32, kBf16>(a);
-    return launch_prefill_t<DK, 16, kBf16>(a);
+    if (a.dv >= 32 && bh * (a.dv / 16) > kCUs) return launch_prefill_t<DK, 32>(a);
+    return launch_prefill_t<DK, 16>(a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.bf16) return launch_prefill_bf16(a);
     switch (a.dk) {
-        case 16: return launch_prefill_dk<16, false>(a);
-        case 32: return launch_prefill_dk<32, false>(a);
-        case 64: return launch_prefill_dk<64, false>(a);
-        case 128: return launch_prefill_dk<128, false>(a);
+        case 16: return launch_prefill_dk<16>(a);
+        case 32: return launch_prefill_dk<32>(a);
+        case 64: return launch_prefill_dk<64>(a);
+        case 128: return launch_prefill_dk<128>(a);
         default: return hipErrorInvalidValue;
     }
 }
