@@ -18,7 +18,7 @@
 //                     result per query is a band [tlo, thi) of bit patterns
 //                     meant to hold the K_B-th largest score: the exact
 //                     threshold bin when every tile was read, else the bins
-//                     of the sample ranks p K_B -+ (3 sqrt(p K_B) + 2).
+//                     of the sample ranks p K_B -+ (3.5 sqrt(p K_B) + 2).
 //   qsa_pass4_kernel  (emit pass) every visible tile again: blocks at or above
 //                     tlo are listed (bit pattern, block) in per-lane
 //                     sub-lists of the query.
@@ -250,7 +250,7 @@ __device__ __forceinline__ int sampled_tile(int j) { return 8 * j + ((5 * j) & 7
 //   kEmit = false: histogram pass.  For each query with m > K_B it keeps the
 //     band [tlo, thi) of score bit patterns that should hold its K_B-th
 //     largest score: exact bin edges when every tile was read, otherwise the
-//     bins of the sample ranks p K_B -+ (3 sqrt(p K_B) + 2), p the sampled
+//     bins of the sample ranks p K_B -+ (3.5 sqrt(p K_B) + 2), p the sampled
 //     fraction of the query's blocks.
 //   kEmit = true: emit pass over every visible tile.  Every block with
 //     u >= tlo is listed as (bit pattern, block); the merge tells the
@@ -434,7 +434,11 @@ void qsa_pass4_kernel(const void* __restrict__ q, const void* __restrict__ kbar,
                 unsigned khi = static_cast<unsigned>(KB), klo = static_cast<unsigned>(KB);
                 if (sampled) {
                     const float k = static_cast<float>(KB) * static_cast<float>(total) / static_cast<float>(m);
-                    const float dlt = 3.f * sqrtf(k) + 2.f;
+                    // 3.5 standard deviations of the sampled rank: at 64K tokens
+                    // no row then misses the band (at 3, a few did, and the
+                    // exact pass that takes them cost ~120 us); at 4 and more
+                    // some rows pass the 1024-candidate cap of the merge
+                    const float dlt = 3.5f * sqrtf(k) + 2.f;
                     khi = k - dlt >= 1.f ? static_cast<unsigned>(k - dlt) : 0u;
                     klo = static_cast<unsigned>(ceilf(k + dlt));
                 }
