@@ -190,11 +190,12 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
 // step of T' R is one 16-byte piece; then the float32 gates g2[C], gamma[C],
 // d[C], w[C].
 //
-// Grid (ceil(B*H / kPrepWaves), ceil(chunks / cpw)): wave w of workgroup
-// (x, y) takes head bh = kPrepWaves x + w and its chunks y cpw + j, j < cpw.
-// Neighbouring workgroups run the same chunks of neighbouring heads, so the k
-// rows in flight at one time are whole token rows of the (token, head, d_k)
-// tensor rather than scattered 256-byte pieces.  cpw is 1 unless the grid
+// Grid gx x gy = (ceil(B*H / kPrepWaves), ceil(chunks / cpw)), launched as
+// one dimension: wave w of workgroup (x, y) takes head bh = kPrepWaves x + w
+// and its chunks y cpw + j, j < cpw.  Each XCD runs every head group of one
+// chunk group before the next, so the k rows in flight on it are whole token
+// rows of the (token, head, d_k) tensor and the alpha / beta lines of a chunk
+// are fetched once.  cpw is 1 unless the grid
 // would exceed kPrepGridWGs workgroups: the resident waves of one round then
 // hide the k-load latency of the next (measured 79.5 us at 32 heads x 512
 // chunks, against 89.6 us with six chunks per wave and one round); a wave
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
                                                    const float* __restrict__ alpha,
                                                    const float* __restrict__ beta,
                                                    _Float16* __restrict__ ws, unsigned* __restrict__ status,
-                                                   int T, int H, int BH, int nchunks, int cpw) {
+                                                   int T, int H, int BH, int nchunks, int cpw, int gx, int gy) {
     using Cfg = PrepCfg<DK>;
     using Frag = typename PrepFrag<DK>::type;
     constexpr int KS = Cfg::KSTEP, LDA = Cfg::LDA, ABLK = Cfg::ABLK;
@@ -215,12 +216,18 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(const uint16_t* __restrict
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int lr = l & 15, lq = l >> 4;
     PrepWaveSmem& sm = smem[w];
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0u;   // this call's status
-    const int bh = static_cast<int>(blockIdx.x) * kPrepWaves + w;
-    if (bh >= BH) return;   // no workgroup barriers below
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;   // this call's status
+    // workgroup (bx, by) of the gx x gy grid: consecutive workgroup ids go to
+    // the XCDs in turn, and each XCD takes every head group of one chunk group
+    // before the next, so the alpha and beta lines of a chunk (one 128-byte
+    // line holds 32 heads of a token) are fetched into one L2 only
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds, jx = static_cast<int>(blockIdx.x) / kXcds;
+    const int bx = jx % gx, by = (jx / gx) * kXcds + xcd;
+    const int bh = bx * kPrepWaves + w;
+    if (by >= gy || bh >= BH) return;   // no workgroup barriers below
     const int b = bh / H, h = bh % H;
     const long tok0 = static_cast<long>(b) * T;
-    auto chunk_of = [&](int j) { return static_cast<int>(blockIdx.y) * cpw + j; };
+    auto chunk_of = [&](int j) { return by * cpw + j; };
 
     // lane (r + 16 g) of fragment [I][kk]: k row 16 I + r, columns kk * 32 + FW g .. + FW
     Frag kf[NB][KS];
@@ -1759,9 +1766,10 @@ static hipError_t launch_t(const PrefillArgs& a, float* save_S = nullptr, float*
         const int cpw = static_cast<int>(
             std::min<long>(16, std::max<long>(1, (gx * nchunks + kPrepGridWGs - 1) / kPrepGridWGs)));
         const int gy = (nchunks + cpw - 1) / cpw;
-        hipLaunchKernelGGL((prep_kernel<DK>), dim3(static_cast<unsigned>(gx), gy), dim3(256), 0, a.stream,
+        const long nblk = gx * ((gy + kXcds - 1) / kXcds) * kXcds;
+        hipLaunchKernelGGL((prep_kernel<DK>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, a.stream,
                            static_cast<const uint16_t*>(a.k), a.alpha, a.beta, ws, status, a.T, a.H, BH, nchunks,
-                           cpw);
+                           cpw, static_cast<int>(gx), gy);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
