@@ -270,7 +270,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is per "
-              "(sequence, head) and needs no collectives; see DESIGN.md for how it would shard.",
+              "(sequence, head): sequences or heads split across GPUs with no communication inside the "
+              "mixer, so one GPU's share runs exactly the kernels measured here.",
               file=sys.stderr)
         sys.exit(2)
 

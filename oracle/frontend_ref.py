@@ -16,7 +16,7 @@ of this step):
     beta_t  = sigmoid(b_logit_t)
     alpha_t = exp(-exp(A_h) * softplus(a_logit_t + b_alpha_h))
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * ShortConv is a causal depthwise convolution over time, one filter of
     width W per channel and head, no bias:
         conv_t[c] = sum_{j=0}^{W-1} w[h, c, j] * x_{t-(W-1)+j}[c],

@@ -16,7 +16,7 @@ Sources (pages on "On the Design of Qwen3.8-Next Architecture"):
   * paper.rainbus.top digest, method step (1): the same recurrence written as
     alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * no 1/sqrt(d_k) on the query (the pages show none); ``scale`` defaults to 1;
   * RMSNorm is taken per (token, head) over d_v with an epsilon the caller
     gives (1e-6 by default, the pages state none), weight (1 + w) with w of

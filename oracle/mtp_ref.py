@@ -29,7 +29,7 @@ Two operations, each written out token by token:
      already hold the misses of that block), so no prefix state has to be kept
      in memory to roll back.
 
-Readings (listed in the design doc): the pages name the drafting scheme but print
+Readings: the pages name the drafting scheme but print
 no kernel; the draft block uses the same q, k, v, alpha, beta per token as a
 prefill, laid out [N, K, H, ...] (sequence, draft position, head), and j runs
 from 0 (reject all) to K (accept all).  Parity pins live in

@@ -18,7 +18,7 @@ heads and one shared key head.  Per sequence of n tokens, with block size r:
     tail tokens r floor((i + 1) / r) .. i of the current incomplete block.
 The same selection is described on the rainbus digest (method step (2)).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * the partial rotary embedding acts on the first ``rope_dims`` (64) of the
     head's 128 dimensions, in rotate-half pairs (j, j + rope_dims / 2) with
     angle pos * base^(-2 j / rope_dims), base 10000;
